@@ -1,0 +1,127 @@
+"""Seeded synthetic workloads for block-sparse masked attention.
+
+This module only draws inputs. It holds none of the attention arithmetic:
+no mask predicate, no score modification, no softmax. The oracle (a CPU
+reference used by the tests) and the HIP path both consume what it returns,
+and neither of them is imported here.
+
+The five workloads follow the shapes the pages use:
+
+* ``c1``: small fp32 case, sliding window W=64 over 256 tokens, block 64.
+* ``c2``: the create_block_mask example of the tensorplay API page
+  (B=1, H=1, 8192 tokens, head dim 64, causal), in bf16.
+* ``c3``: a 1k-token sliding window over an 8k context, as in the
+  sliding-window section of the FlexAttention-on-Apple-Silicon how-to
+  ("Mask 2"), batched as B=4, H=16, head dim 128.
+* ``c4``: four packed documents (the how-to's "Mask 3" and its at-a-glance
+  table), scaled to 32768 tokens, with the tanh soft-cap of its "Bonus"
+  section at cap 50.
+* ``c5``: causal attention with an ALiBi distance bias over 16384 tokens.
+
+Values are N(0, 1) from ``numpy.random.default_rng(seed)``, drawn as float32
+in (B, H, S, D) order: the document lengths first (``c4`` only), then Q, K
+and V. bf16 workloads are rounded to bf16 with round-to-nearest-even, and
+both sides use those rounded values.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["Workload", "CONFIGS", "get", "doc_lengths", "doc_ids",
+           "draw_qkv", "make_inputs"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str              # "bf16" or "fp32"
+    B: int
+    H: int
+    H_kv: int
+    q_len: int
+    kv_len: int
+    D: int
+    mask: str               # "none" | "causal" | "sliding_window" | "document"
+    block_m: int
+    block_n: int
+    seed: int
+    window: Optional[int] = None
+    n_docs: Optional[int] = None
+    min_doc_len: Optional[int] = None
+    score: str = "none"     # "none" | "softcap" | "alibi"
+    softcap: Optional[float] = None
+
+    @property
+    def scale(self) -> float:
+        # 1/sqrt(D), the SDPA default the pages' API mirrors.
+        return 1.0 / float(np.sqrt(self.D))
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+CONFIGS = {
+    "c1": Workload("c1", "fp32", 1, 2, 2, 256, 256, 64, "sliding_window",
+                   64, 64, seed=0, window=64),
+    "c2": Workload("c2", "bf16", 1, 1, 1, 8192, 8192, 64, "causal",
+                   128, 128, seed=1),
+    "c3": Workload("c3", "bf16", 4, 16, 16, 8192, 8192, 128,
+                   "sliding_window", 128, 128, seed=2, window=1024),
+    "c4": Workload("c4", "bf16", 1, 32, 32, 32768, 32768, 128, "document",
+                   128, 128, seed=3, n_docs=4, min_doc_len=2048,
+                   score="softcap", softcap=50.0),
+    "c5": Workload("c5", "bf16", 2, 32, 32, 16384, 16384, 128, "causal",
+                   128, 128, seed=4, score="alibi"),
+}
+
+
+def get(name: str) -> Workload:
+    return CONFIGS[name]
+
+
+def doc_lengths(rng: np.random.Generator, total: int, n_docs: int,
+                min_len: int) -> np.ndarray:
+    """Stick-breaking draw of ``n_docs`` lengths, each >= ``min_len``,
+    summing to ``total``: the slack beyond the minimum is cut at
+    ``n_docs - 1`` sorted uniform integer points."""
+    extra = total - n_docs * min_len
+    if extra < 0:
+        raise ValueError("documents do not fit")
+    cuts = np.sort(rng.integers(0, extra + 1, size=n_docs - 1))
+    parts = np.diff(np.concatenate([[0], cuts, [extra]]))
+    return (min_len + parts).astype(np.int64)
+
+
+def doc_ids(lengths) -> np.ndarray:
+    """int32 document id per token, consecutive runs in order."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    return np.repeat(np.arange(len(lengths), dtype=np.int32), lengths)
+
+
+def draw_qkv(rng: np.random.Generator, w: Workload):
+    """float32 Q [B,H,q_len,D], K and V [B,H_kv,kv_len,D], N(0,1)."""
+    q = rng.standard_normal((w.B, w.H, w.q_len, w.D), dtype=np.float32)
+    k = rng.standard_normal((w.B, w.H_kv, w.kv_len, w.D), dtype=np.float32)
+    v = rng.standard_normal((w.B, w.H_kv, w.kv_len, w.D), dtype=np.float32)
+    return q, k, v
+
+
+def make_inputs(w: Workload):
+    """Return ``(q, k, v, doc_id)`` as CPU torch tensors in the workload's
+    dtype (bf16 values are RNE-rounded from the float32 draw) and
+    ``doc_id`` as an int32 numpy array or ``None``."""
+    import torch
+
+    rng = np.random.default_rng(w.seed)
+    doc = None
+    if w.mask == "document":
+        if w.q_len != w.kv_len:
+            raise ValueError("document workloads use q_len == kv_len")
+        doc = doc_ids(doc_lengths(rng, w.kv_len, w.n_docs, w.min_doc_len))
+    q, k, v = draw_qkv(rng, w)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    qt, kt, vt = (torch.from_numpy(x).to(tdt) for x in (q, k, v))
+    return qt, kt, vt, doc
