@@ -1,0 +1,14 @@
+"""block_sparse_masked_fa_amd: FlexAttention-style block-sparse masked
+attention forward for MI355X (gfx950).
+
+The work runs in ``libflexattn.so`` (hand-written HIP kernels behind a C ABI,
+``include/flexattn.h``); this package is its Python binding. Importing it
+does not load the library; the first call does, and fails loudly if the
+library has not been built (``python -m block_sparse_masked_fa_amd.build``).
+"""
+from .api import (  # noqa: F401
+    BlockMask, FlexAttnError, MaskMod, ScoreMod, alibi, causal,
+    create_block_mask, document, fa_block_mask_dims, fa_create_block_mask,
+    fa_flex_attention_fwd, flex_attention, no_mask, sliding_window, softcap,
+)
+from ._capi import LIB_PATH, lib  # noqa: F401

@@ -1,0 +1,310 @@
+"""Python binding of libflexattn.so.
+
+Thin marshalling over the C ABI (``include/flexattn.h``): torch provides the
+device buffers and the current HIP stream, every computation runs in the HIP
+kernels. Two layers:
+
+* the raw entry points with the C names (``fa_block_mask_dims``,
+  ``fa_create_block_mask``, ``fa_flex_attention_fwd``), taking ctypes structs
+  and integer device addresses;
+* a FlexAttention-style convenience layer: ``create_block_mask(...)`` returns
+  a :class:`BlockMask` holding its index tensors, and
+  ``flex_attention(q, k, v, block_mask, score_mod)`` returns ``(O, LSE)``.
+  The shapes follow scaled_dot_product_attention: (B, H, S, D).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Optional, Tuple, Union
+
+import torch
+
+from . import _capi as C
+
+__all__ = [
+    "MaskMod", "ScoreMod", "causal", "sliding_window", "document",
+    "no_mask", "softcap", "alibi", "BlockMask", "create_block_mask",
+    "flex_attention", "fa_block_mask_dims", "fa_create_block_mask",
+    "fa_flex_attention_fwd", "FlexAttnError",
+]
+
+FlexAttnError = C.FlexAttnError
+
+
+# ------------------------------------------------------------------ mods
+@dataclasses.dataclass(frozen=True)
+class MaskMod:
+    """A built-in mask_mod. ``doc_id`` is an int32 tensor on the device."""
+    kind: int
+    window: int = 0
+    doc_id: Optional[torch.Tensor] = None
+
+    def to_c(self) -> C.fa_mask_mod:
+        doc = self.doc_id
+        return C.fa_mask_mod(
+            kind=self.kind, window=int(self.window),
+            doc_id=doc.data_ptr() if doc is not None else None,
+            doc_len=doc.numel() if doc is not None else 0)
+
+
+def causal() -> MaskMod:
+    return MaskMod(C.FA_MASK_CAUSAL)
+
+
+def sliding_window(window: int) -> MaskMod:
+    return MaskMod(C.FA_MASK_SLIDING_WINDOW, window=int(window))
+
+
+def document(doc_id: torch.Tensor) -> MaskMod:
+    if doc_id.dtype != torch.int32 or doc_id.dim() != 1:
+        raise ValueError("doc_id must be a 1-D int32 tensor")
+    return MaskMod(C.FA_MASK_DOCUMENT, doc_id=doc_id.contiguous())
+
+
+def no_mask() -> MaskMod:
+    return MaskMod(C.FA_MASK_NONE)
+
+
+@dataclasses.dataclass(frozen=True)
+class ScoreMod:
+    kind: int
+    cap: float = 0.0
+
+    def to_c(self) -> C.fa_score_mod:
+        return C.fa_score_mod(kind=self.kind, softcap=float(self.cap))
+
+
+def softcap(cap: float) -> ScoreMod:
+    return ScoreMod(C.FA_SCORE_SOFTCAP, float(cap))
+
+
+def alibi() -> ScoreMod:
+    return ScoreMod(C.FA_SCORE_ALIBI)
+
+
+def _mask_from(spec, window=None, doc_id=None) -> MaskMod:
+    if isinstance(spec, MaskMod):
+        return spec
+    if spec is None or spec == "none":
+        return no_mask()
+    if spec == "causal":
+        return causal()
+    if spec == "sliding_window":
+        return sliding_window(window)
+    if spec == "document":
+        return document(doc_id)
+    raise ValueError(f"unknown mask_mod {spec!r}")
+
+
+def _score_from(spec) -> ScoreMod:
+    if isinstance(spec, ScoreMod):
+        return spec
+    if spec is None or spec == "none":
+        return ScoreMod(C.FA_SCORE_NONE)
+    if spec == "alibi":
+        return alibi()
+    if isinstance(spec, tuple) and len(spec) == 2 and spec[0] == "softcap":
+        return softcap(spec[1])
+    raise ValueError(f"unknown score_mod {spec!r}")
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+# -------------------------------------------------------------- raw calls
+def fa_block_mask_dims(q_len: int, kv_len: int, block_m: int,
+                       block_n: int) -> Tuple[int, int]:
+    nq, nk = ctypes.c_int32(), ctypes.c_int32()
+    C.check(C.lib().fa_block_mask_dims(q_len, kv_len, block_m, block_n,
+                                       ctypes.byref(nq), ctypes.byref(nk)),
+            "fa_block_mask_dims")
+    return nq.value, nk.value
+
+
+def fa_create_block_mask(mask: C.fa_mask_mod, B: int, H: int, q_len: int,
+                         kv_len: int, block_m: int, block_n: int,
+                         separate_full_blocks: int, bm: C.fa_block_mask,
+                         stream: Optional[int]) -> int:
+    return C.lib().fa_create_block_mask(
+        ctypes.byref(mask), B, H, q_len, kv_len, block_m, block_n,
+        separate_full_blocks, ctypes.byref(bm), stream)
+
+
+def fa_flex_attention_fwd(dtype: int, B: int, H: int, H_kv: int, q_len: int,
+                          kv_len: int, D: int, q: int, q_stride, k: int,
+                          k_stride, v: int, v_stride, scale: float,
+                          bm: C.fa_block_mask, score: Optional[C.fa_score_mod],
+                          o: int, lse: Optional[int],
+                          stream: Optional[int]) -> int:
+    return C.lib().fa_flex_attention_fwd(
+        dtype, B, H, H_kv, q_len, kv_len, D,
+        q, C.Stride3(*q_stride), k, C.Stride3(*k_stride),
+        v, C.Stride3(*v_stride), scale, ctypes.byref(bm),
+        ctypes.byref(score) if score is not None else None, o, lse, stream)
+
+
+# ------------------------------------------------------------- BlockMask
+class BlockMask:
+    """Block mask: index tensors (int32, on the device) plus the mask_mod
+    they were built from. Built once, reused by any number of
+    flex_attention calls (the mask stays valid while its tensors live)."""
+
+    def __init__(self, mask: MaskMod, B: int, H: int, q_len: int,
+                 kv_len: int, block_m: int, block_n: int,
+                 kv_num_blocks: torch.Tensor, kv_indices: torch.Tensor,
+                 full_kv_num_blocks: Optional[torch.Tensor],
+                 full_kv_indices: Optional[torch.Tensor]):
+        self.mask = mask
+        self.B, self.H = B, H
+        self.q_len, self.kv_len = q_len, kv_len
+        self.block_m, self.block_n = block_m, block_n
+        self.kv_num_blocks = kv_num_blocks
+        self.kv_indices = kv_indices
+        self.full_kv_num_blocks = full_kv_num_blocks
+        self.full_kv_indices = full_kv_indices
+        self.num_q_blocks = kv_num_blocks.shape[-1]
+        self.num_kv_blocks = kv_indices.shape[-1]
+
+    @property
+    def separate_full_blocks(self) -> bool:
+        return self.full_kv_num_blocks is not None
+
+    def to_c(self) -> C.fa_block_mask:
+        f = self.full_kv_num_blocks
+        fi = self.full_kv_indices
+        return C.fa_block_mask(
+            mask=self.mask.to_c(), B=self.B, H=self.H, q_len=self.q_len,
+            kv_len=self.kv_len, block_m=self.block_m, block_n=self.block_n,
+            num_q_blocks=self.num_q_blocks, num_kv_blocks=self.num_kv_blocks,
+            separate_full_blocks=int(self.separate_full_blocks),
+            kv_num_blocks=self.kv_num_blocks.data_ptr(),
+            kv_indices=self.kv_indices.data_ptr(),
+            full_kv_num_blocks=f.data_ptr() if f is not None else None,
+            full_kv_indices=fi.data_ptr() if fi is not None else None)
+
+    @classmethod
+    def from_kv_blocks(cls, kv_num_blocks: torch.Tensor,
+                       kv_indices: torch.Tensor,
+                       full_kv_num_blocks: Optional[torch.Tensor] = None,
+                       full_kv_indices: Optional[torch.Tensor] = None, *,
+                       mask_mod=None, q_len: int, kv_len: int,
+                       BLOCK_SIZE: Union[int, Tuple[int, int]] = 128,
+                       window=None, doc_id=None) -> "BlockMask":
+        """Wrap caller-provided index tensors (tensorplay
+        create_block_mask page: precomputed metadata is supplied through
+        BlockMask.from_kv_blocks). The mask_mod is still applied to the
+        listed partial blocks."""
+        bm_, bn_ = ((BLOCK_SIZE, BLOCK_SIZE) if isinstance(BLOCK_SIZE, int)
+                    else BLOCK_SIZE)
+        for t in (kv_num_blocks, kv_indices, full_kv_num_blocks,
+                  full_kv_indices):
+            if t is not None and (t.dtype != torch.int32 or not t.is_cuda
+                                  or not t.is_contiguous()):
+                raise ValueError("index tensors must be contiguous int32 "
+                                 "device tensors")
+        if (full_kv_num_blocks is None) != (full_kv_indices is None):
+            raise ValueError("give both full block tensors or neither")
+        B, H = kv_num_blocks.shape[0], kv_num_blocks.shape[1]
+        return cls(_mask_from(mask_mod, window, doc_id), B, H, q_len, kv_len,
+                   bm_, bn_, kv_num_blocks, kv_indices, full_kv_num_blocks,
+                   full_kv_indices)
+
+    def __repr__(self):
+        return (f"BlockMask(B={self.B}, H={self.H}, q_len={self.q_len}, "
+                f"kv_len={self.kv_len}, block=({self.block_m}, "
+                f"{self.block_n}), separate_full_blocks="
+                f"{self.separate_full_blocks})")
+
+
+def create_block_mask(mask_mod, B: Optional[int], H: Optional[int],
+                      Q_LEN: int, KV_LEN: int, device="cuda",
+                      BLOCK_SIZE: Union[int, Tuple[int, int]] = 128,
+                      separate_full_blocks: bool = True, *, window=None,
+                      doc_id=None) -> BlockMask:
+    """Build a block mask on the device (one call of fa_create_block_mask).
+
+    ``mask_mod``: a :class:`MaskMod` or one of "causal", "sliding_window"
+    (with ``window``), "document" (with ``doc_id``), "none". ``B``/``H``
+    None broadcast the mask over every batch entry / head."""
+    mask = _mask_from(mask_mod, window, doc_id)
+    device = torch.device(device)
+    if device.type != "cuda":
+        raise ValueError("the block mask is built on a HIP device")
+    bm_, bn_ = ((BLOCK_SIZE, BLOCK_SIZE) if isinstance(BLOCK_SIZE, int)
+                else BLOCK_SIZE)
+    Bm = 1 if B is None else int(B)
+    Hm = 1 if H is None else int(H)
+    nqb, nkvb = fa_block_mask_dims(Q_LEN, KV_LEN, bm_, bn_)
+    opts = dict(dtype=torch.int32, device=device)
+    num = torch.empty((Bm, Hm, nqb), **opts)
+    idx = torch.empty((Bm, Hm, nqb, nkvb), **opts)
+    fnum = torch.empty((Bm, Hm, nqb), **opts) if separate_full_blocks else None
+    fidx = (torch.empty((Bm, Hm, nqb, nkvb), **opts)
+            if separate_full_blocks else None)
+    if mask.doc_id is not None and mask.doc_id.device != device:
+        raise ValueError("doc_id must live on the mask's device")
+    cbm = C.fa_block_mask(
+        kv_num_blocks=num.data_ptr(), kv_indices=idx.data_ptr(),
+        full_kv_num_blocks=fnum.data_ptr() if fnum is not None else None,
+        full_kv_indices=fidx.data_ptr() if fidx is not None else None)
+    with torch.cuda.device(device):
+        C.check(fa_create_block_mask(mask.to_c(), Bm, Hm, Q_LEN, KV_LEN, bm_,
+                                     bn_, int(separate_full_blocks), cbm,
+                                     _stream_handle(device)),
+                "fa_create_block_mask")
+    return BlockMask(mask, Bm, Hm, Q_LEN, KV_LEN, bm_, bn_, num, idx, fnum,
+                     fidx)
+
+
+_DTYPES = {torch.bfloat16: C.FA_BF16, torch.float32: C.FA_FP32}
+
+
+def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                   block_mask: BlockMask, score_mod=None,
+                   scale: Optional[float] = None, return_lse: bool = True,
+                   out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None):
+    """Fused block-sparse attention forward (one fa_flex_attention_fwd call).
+
+    q: (B, H, Q_LEN, D); k, v: (B, H_kv, KV_LEN, D), bf16 or fp32, on the
+    same HIP device, last dimension contiguous. ``score_mod``: None,
+    "alibi", ("softcap", cap) or a :class:`ScoreMod`. ``scale`` defaults to
+    1/sqrt(D). Returns ``(O, LSE)`` (``LSE`` fp32 (B, H, Q_LEN), natural
+    log; ``None`` when ``return_lse`` is False)."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D (B, H, S, D)")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share a dtype in {bf16, fp32}")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be HIP device tensors")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, q_len, D = q.shape
+    Bk, H_kv, kv_len, Dk = k.shape
+    if k.shape != v.shape or Bk != B or Dk != D:
+        raise ValueError("k and v must be (B, H_kv, KV_LEN, D)")
+    for t in (q, k, v):
+        if t.numel() and t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    score = _score_from(score_mod)
+    if out is None:
+        out = torch.empty((B, H, q_len, D), dtype=q.dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, H, q_len), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    with torch.cuda.device(q.device):
+        st = fa_flex_attention_fwd(
+            _DTYPES[q.dtype], B, H, H_kv, q_len, kv_len, D,
+            q.data_ptr(), q.stride()[:3], k.data_ptr(), k.stride()[:3],
+            v.data_ptr(), v.stride()[:3], float(scale), block_mask.to_c(),
+            score.to_c(), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None,
+            _stream_handle(q.device))
+    C.check(st, "fa_flex_attention_fwd")
+    return out, lse

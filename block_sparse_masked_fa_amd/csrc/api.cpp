@@ -1,0 +1,99 @@
+// C-ABI entry points of libflexattn.so: check arguments on the host, pick the
+// kernel instance, enqueue it on the caller's stream. No allocation, no
+// synchronisation, no fallback path: anything not built is reported.
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "../../include/flexattn.h"
+#include "internal.hpp"
+#include "validate.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa_status finish(int status, const std::string& msg) {
+  if (status != FA_OK) g_last_error = msg;
+  return static_cast<fa_status>(status);
+}
+
+fa_status hip_status(int err, const char* what) {
+  if (err == 0) return FA_OK;
+  g_last_error = std::string(what) + ": " +
+                 hipGetErrorString(static_cast<hipError_t>(err));
+  return FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_string(int32_t status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER";
+    case FA_ERR_INVALID_VALUE: return "FA_ERR_INVALID_VALUE";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_SHAPE_MISMATCH: return "FA_ERR_SHAPE_MISMATCH";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    default: return "unknown fa_status";
+  }
+}
+
+const char* fa_last_error(void) { return g_last_error.c_str(); }
+
+fa_status fa_block_mask_dims(int32_t q_len, int32_t kv_len, int32_t block_m,
+                             int32_t block_n, int32_t* num_q_blocks,
+                             int32_t* num_kv_blocks) {
+  std::string msg;
+  int st = fa::check_block_mask_dims(q_len, kv_len, block_m, block_n,
+                                     num_q_blocks, num_kv_blocks, &msg);
+  return finish(st, msg);
+}
+
+fa_status fa_create_block_mask(const fa_mask_mod* mask, int32_t B, int32_t H,
+                               int32_t q_len, int32_t kv_len, int32_t block_m,
+                               int32_t block_n, int32_t separate_full_blocks,
+                               fa_block_mask* bm, void* stream) {
+  std::string msg;
+  fa::BlockMaskLaunch p{};
+  int st = fa::check_create_block_mask(mask, B, H, q_len, kv_len, block_m,
+                                       block_n, separate_full_blocks, bm, &p,
+                                       &msg);
+  if (st != FA_OK) return finish(st, msg);
+  if (static_cast<int64_t>(p.Bm) * p.Hm * p.nqb == 0) return FA_OK;
+  return hip_status(fa::launch_block_mask(p, stream), "block-mask kernel launch");
+}
+
+fa_status fa_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H,
+                                int32_t H_kv, int32_t q_len, int32_t kv_len,
+                                int32_t D, const void* q,
+                                const int64_t q_stride[3], const void* k,
+                                const int64_t k_stride[3], const void* v,
+                                const int64_t v_stride[3], float scale,
+                                const fa_block_mask* bm,
+                                const fa_score_mod* score, void* o, float* lse,
+                                void* stream) {
+  std::string msg;
+  fa::FwdLaunch p{};
+  bool nothing = false;
+  int st = fa::check_flex_attention_fwd(dtype, B, H, H_kv, q_len, kv_len, D, q,
+                                        q_stride, k, k_stride, v, v_stride,
+                                        scale, bm, score, o, lse, &p, &nothing,
+                                        &msg);
+  if (st != FA_OK) return finish(st, msg);
+  if (nothing) return FA_OK;
+  int err;
+  if (dtype == FA_FP32)
+    err = fa::launch_fwd_fp32(p, stream);
+  else if (D == 64)
+    err = fa::launch_fwd_bf16_d64(p, stream);
+  else
+    err = fa::launch_fwd_bf16_d128(p, stream);
+  return hip_status(err, "attention kernel launch");
+}
+
+}  // extern "C"

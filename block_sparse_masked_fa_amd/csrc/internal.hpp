@@ -1,0 +1,57 @@
+// Internal host-side launch descriptors shared by the C-ABI layer (api.cpp)
+// and the kernel translation units. Plain data; no HIP types, so the
+// argument checks in validate.cpp build with any C++ compiler.
+#pragma once
+
+#include <stdint.h>
+
+namespace fa {
+
+struct MaskParams {
+  int32_t kind;           // fa_mask_kind
+  int32_t window;         // sliding window W
+  const int32_t* doc_id;  // device, document mask only
+};
+
+struct BlockMaskLaunch {
+  MaskParams mask;
+  int32_t Bm, Hm;
+  int32_t q_len, kv_len;
+  int32_t block_m, block_n;
+  int32_t nqb, nkvb;
+  int32_t separate_full;
+  int32_t* num;
+  int32_t* idx;
+  int32_t* fnum;  // NULL when !separate_full
+  int32_t* fidx;
+};
+
+struct FwdLaunch {
+  int32_t B, H, H_kv;
+  int32_t q_len, kv_len, D;
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t qs[3], ks[3], vs[3];  // element strides (batch, head, sequence)
+  float scale;
+  MaskParams mask;
+  int32_t Bm, Hm;       // block-mask broadcast dims (1 or B / H)
+  int32_t block;        // block_m == block_n
+  int32_t nqb, nkvb;
+  const int32_t* num;
+  const int32_t* idx;
+  const int32_t* fnum;  // may be NULL: no full blocks
+  const int32_t* fidx;
+  int32_t score_kind;
+  float softcap;
+  void* o;
+  float* lse;           // may be NULL
+};
+
+// Kernel launchers: return a hipError_t value (0 = success).
+int launch_block_mask(const BlockMaskLaunch& p, void* stream);
+int launch_fwd_bf16_d64(const FwdLaunch& p, void* stream);
+int launch_fwd_bf16_d128(const FwdLaunch& p, void* stream);
+int launch_fwd_fp32(const FwdLaunch& p, void* stream);
+
+}  // namespace fa

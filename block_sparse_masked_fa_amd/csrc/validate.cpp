@@ -1,0 +1,263 @@
+// Host-only argument checks for the C ABI (no HIP calls, no device access).
+#include "validate.hpp"
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+namespace fa {
+namespace {
+
+int fail(std::string* msg, int status, const std::string& why) {
+  if (msg) *msg = why;
+  return status;
+}
+
+int check_mask_mod(const fa_mask_mod* mask, int32_t q_len, int32_t kv_len,
+                   std::string* msg) {
+  if (!mask) return fail(msg, FA_ERR_NULL_POINTER, "mask is NULL");
+  switch (mask->kind) {
+    case FA_MASK_NONE:
+    case FA_MASK_CAUSAL:
+      return FA_OK;
+    case FA_MASK_SLIDING_WINDOW:
+      if (mask->window < 1)
+        return fail(msg, FA_ERR_INVALID_VALUE,
+                    "sliding window needs window >= 1, got " +
+                        std::to_string(mask->window));
+      return FA_OK;
+    case FA_MASK_DOCUMENT: {
+      if (!mask->doc_id)
+        return fail(msg, FA_ERR_NULL_POINTER, "document mask needs doc_id");
+      int64_t need = q_len > kv_len ? q_len : kv_len;
+      if (mask->doc_len < need)
+        return fail(msg, FA_ERR_SHAPE_MISMATCH,
+                    "doc_len " + std::to_string(mask->doc_len) +
+                        " < max(q_len, kv_len) = " + std::to_string(need));
+      return FA_OK;
+    }
+    default:
+      return fail(msg, FA_ERR_INVALID_VALUE,
+                  "unknown mask kind " + std::to_string(mask->kind));
+  }
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+int check_strides(const char* name, const int64_t s[3], const int64_t dims[3],
+                  int elt, std::string* msg) {
+  if (!s) return fail(msg, FA_ERR_NULL_POINTER, std::string(name) + " stride is NULL");
+  for (int d = 0; d < 3; ++d) {
+    if (dims[d] <= 1) continue;
+    if (s[d] < 0)
+      return fail(msg, FA_ERR_INVALID_VALUE,
+                  std::string(name) + " has a negative stride");
+    if ((s[d] * elt) % 16 != 0)
+      return fail(msg, FA_ERR_UNSUPPORTED,
+                  std::string(name) + " stride " + std::to_string(d) + " = " +
+                      std::to_string(s[d]) +
+                      " elements is not a multiple of 16 bytes");
+  }
+  return FA_OK;
+}
+
+}  // namespace
+
+int check_block_mask_dims(int32_t q_len, int32_t kv_len, int32_t block_m,
+                          int32_t block_n, int32_t* nqb, int32_t* nkvb,
+                          std::string* msg) {
+  if (!nqb || !nkvb)
+    return fail(msg, FA_ERR_NULL_POINTER, "output pointer is NULL");
+  if (q_len < 0 || kv_len < 0)
+    return fail(msg, FA_ERR_INVALID_VALUE, "negative sequence length");
+  if (block_m < 1 || block_n < 1)
+    return fail(msg, FA_ERR_INVALID_VALUE, "block size must be >= 1");
+  if (block_m > kMaxBlock || block_n > kMaxBlock)
+    return fail(msg, FA_ERR_UNSUPPORTED,
+                "block size above " + std::to_string(kMaxBlock));
+  int64_t q = (static_cast<int64_t>(q_len) + block_m - 1) / block_m;
+  int64_t k = (static_cast<int64_t>(kv_len) + block_n - 1) / block_n;
+  if (k > kMaxKvBlocks)
+    return fail(msg, FA_ERR_UNSUPPORTED,
+                "more than " + std::to_string(kMaxKvBlocks) + " key blocks");
+  *nqb = static_cast<int32_t>(q);
+  *nkvb = static_cast<int32_t>(k);
+  return FA_OK;
+}
+
+int check_create_block_mask(const fa_mask_mod* mask, int32_t B, int32_t H,
+                            int32_t q_len, int32_t kv_len, int32_t block_m,
+                            int32_t block_n, int32_t separate_full_blocks,
+                            fa_block_mask* bm, BlockMaskLaunch* out,
+                            std::string* msg) {
+  if (!bm) return fail(msg, FA_ERR_NULL_POINTER, "bm is NULL");
+  int st = check_mask_mod(mask, q_len, kv_len, msg);
+  if (st != FA_OK) return st;
+  if (B < 1 || H < 1)
+    return fail(msg, FA_ERR_INVALID_VALUE, "B and H must be >= 1");
+  int32_t nqb = 0, nkvb = 0;
+  st = check_block_mask_dims(q_len, kv_len, block_m, block_n, &nqb, &nkvb, msg);
+  if (st != FA_OK) return st;
+  const bool sep = separate_full_blocks != 0;
+  const int64_t rows = static_cast<int64_t>(B) * H * nqb;
+  if (rows > INT32_MAX || rows * nkvb > INT32_MAX)
+    return fail(msg, FA_ERR_UNSUPPORTED,
+                "B * H * num_q_blocks * num_kv_blocks too large");
+  if (rows > 0) {
+    if (!bm->kv_num_blocks)
+      return fail(msg, FA_ERR_NULL_POINTER, "kv_num_blocks is NULL");
+    if (nkvb > 0 && !bm->kv_indices)
+      return fail(msg, FA_ERR_NULL_POINTER, "kv_indices is NULL");
+    if (sep && !bm->full_kv_num_blocks)
+      return fail(msg, FA_ERR_NULL_POINTER, "full_kv_num_blocks is NULL");
+    if (sep && nkvb > 0 && !bm->full_kv_indices)
+      return fail(msg, FA_ERR_NULL_POINTER, "full_kv_indices is NULL");
+  }
+  bm->mask = *mask;
+  bm->B = B;
+  bm->H = H;
+  bm->q_len = q_len;
+  bm->kv_len = kv_len;
+  bm->block_m = block_m;
+  bm->block_n = block_n;
+  bm->num_q_blocks = nqb;
+  bm->num_kv_blocks = nkvb;
+  bm->separate_full_blocks = sep ? 1 : 0;
+  if (!sep) {
+    bm->full_kv_num_blocks = nullptr;
+    bm->full_kv_indices = nullptr;
+  }
+  out->mask = MaskParams{mask->kind, mask->window, mask->doc_id};
+  out->Bm = B;
+  out->Hm = H;
+  out->q_len = q_len;
+  out->kv_len = kv_len;
+  out->block_m = block_m;
+  out->block_n = block_n;
+  out->nqb = nqb;
+  out->nkvb = nkvb;
+  out->separate_full = sep ? 1 : 0;
+  out->num = bm->kv_num_blocks;
+  out->idx = bm->kv_indices;
+  out->fnum = bm->full_kv_num_blocks;
+  out->fidx = bm->full_kv_indices;
+  return FA_OK;
+}
+
+int check_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H, int32_t H_kv,
+                             int32_t q_len, int32_t kv_len, int32_t D,
+                             const void* q, const int64_t q_stride[3],
+                             const void* k, const int64_t k_stride[3],
+                             const void* v, const int64_t v_stride[3],
+                             float scale, const fa_block_mask* bm,
+                             const fa_score_mod* score, void* o, float* lse,
+                             FwdLaunch* out, bool* nothing_to_do,
+                             std::string* msg) {
+  *nothing_to_do = false;
+  if (dtype != FA_BF16 && dtype != FA_FP32)
+    return fail(msg, FA_ERR_INVALID_VALUE,
+                "unknown dtype " + std::to_string(dtype));
+  if (B < 0 || H < 0 || q_len < 0 || kv_len < 0)
+    return fail(msg, FA_ERR_INVALID_VALUE, "negative size");
+  if (H_kv < 1 || H % H_kv != 0)
+    return fail(msg, FA_ERR_INVALID_VALUE,
+                "H_kv must be >= 1 and divide H");
+  if (D != 64 && D != 128)
+    return fail(msg, FA_ERR_UNSUPPORTED,
+                "head dimension " + std::to_string(D) + " (built: 64, 128)");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(msg, FA_ERR_INVALID_VALUE, "scale must be finite and > 0");
+  if (!bm) return fail(msg, FA_ERR_NULL_POINTER, "block mask is NULL");
+  int st = check_mask_mod(&bm->mask, q_len, kv_len, msg);
+  if (st != FA_OK) return st;
+  if (bm->q_len != q_len || bm->kv_len != kv_len)
+    return fail(msg, FA_ERR_SHAPE_MISMATCH,
+                "block mask built for lengths (" + std::to_string(bm->q_len) +
+                    ", " + std::to_string(bm->kv_len) + "), call has (" +
+                    std::to_string(q_len) + ", " + std::to_string(kv_len) + ")");
+  if (!(bm->B == 1 || bm->B == B) || !(bm->H == 1 || bm->H == H) ||
+      bm->B < 1 || bm->H < 1)
+    return fail(msg, FA_ERR_SHAPE_MISMATCH,
+                "block mask batch/head dims must be 1 or equal to B/H");
+  int32_t nqb = 0, nkvb = 0;
+  st = check_block_mask_dims(q_len, kv_len, bm->block_m, bm->block_n, &nqb,
+                             &nkvb, msg);
+  if (st != FA_OK) return st;
+  if (nqb != bm->num_q_blocks || nkvb != bm->num_kv_blocks)
+    return fail(msg, FA_ERR_SHAPE_MISMATCH,
+                "block mask block counts disagree with its lengths");
+  if (bm->block_m != bm->block_n || (bm->block_m != 64 && bm->block_m != 128))
+    return fail(msg, FA_ERR_UNSUPPORTED,
+                "attention needs block_m == block_n in {64, 128}");
+  int32_t skind = score ? score->kind : FA_SCORE_NONE;
+  float cap = score ? score->softcap : 0.0f;
+  if (skind != FA_SCORE_NONE && skind != FA_SCORE_SOFTCAP &&
+      skind != FA_SCORE_ALIBI)
+    return fail(msg, FA_ERR_INVALID_VALUE,
+                "unknown score kind " + std::to_string(skind));
+  if (skind == FA_SCORE_SOFTCAP && (!std::isfinite(cap) || !(cap > 0.0f)))
+    return fail(msg, FA_ERR_INVALID_VALUE, "softcap must be finite and > 0");
+  const int64_t rows = static_cast<int64_t>(B) * H * nqb;
+  if (rows > INT32_MAX)
+    return fail(msg, FA_ERR_UNSUPPORTED, "B * H * num_q_blocks too large");
+  if (rows == 0) {
+    *nothing_to_do = true;
+    return FA_OK;
+  }
+  if (!q || !o) return fail(msg, FA_ERR_NULL_POINTER, "q or o is NULL");
+  if (kv_len > 0 && (!k || !v))
+    return fail(msg, FA_ERR_NULL_POINTER, "k or v is NULL");
+  if (!bm->kv_num_blocks)
+    return fail(msg, FA_ERR_NULL_POINTER, "kv_num_blocks is NULL");
+  if (nkvb > 0 && !bm->kv_indices)
+    return fail(msg, FA_ERR_NULL_POINTER, "kv_indices is NULL");
+  if (bm->separate_full_blocks &&
+      (!bm->full_kv_num_blocks || (nkvb > 0 && !bm->full_kv_indices)))
+    return fail(msg, FA_ERR_NULL_POINTER, "full block arrays are NULL");
+  const int elt = dtype == FA_BF16 ? 2 : 4;
+  const int64_t qd[3] = {B, H, q_len};
+  const int64_t kd[3] = {B, H_kv, kv_len};
+  if ((st = check_strides("q", q_stride, qd, elt, msg)) != FA_OK) return st;
+  if (kv_len > 0) {
+    if ((st = check_strides("k", k_stride, kd, elt, msg)) != FA_OK) return st;
+    if ((st = check_strides("v", v_stride, kd, elt, msg)) != FA_OK) return st;
+  }
+  if (!aligned16(q) || !aligned16(o) ||
+      (kv_len > 0 && (!aligned16(k) || !aligned16(v))))
+    return fail(msg, FA_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
+
+  out->B = B;
+  out->H = H;
+  out->H_kv = H_kv;
+  out->q_len = q_len;
+  out->kv_len = kv_len;
+  out->D = D;
+  out->q = q;
+  out->k = k;
+  out->v = v;
+  for (int d = 0; d < 3; ++d) {
+    out->qs[d] = q_stride[d];
+    out->ks[d] = kv_len > 0 ? k_stride[d] : 0;
+    out->vs[d] = kv_len > 0 ? v_stride[d] : 0;
+  }
+  out->scale = scale;
+  out->mask = MaskParams{bm->mask.kind, bm->mask.window, bm->mask.doc_id};
+  out->Bm = bm->B;
+  out->Hm = bm->H;
+  out->block = bm->block_m;
+  out->nqb = nqb;
+  out->nkvb = nkvb;
+  out->num = bm->kv_num_blocks;
+  out->idx = bm->kv_indices;
+  out->fnum = bm->separate_full_blocks ? bm->full_kv_num_blocks : nullptr;
+  out->fidx = bm->separate_full_blocks ? bm->full_kv_indices : nullptr;
+  out->score_kind = skind;
+  out->softcap = cap;
+  out->o = o;
+  out->lse = lse;
+  return FA_OK;
+}
+
+}  // namespace fa

@@ -1,0 +1,41 @@
+// Host-only argument checks for the C ABI. No HIP headers: this file and
+// validate.cpp build with a plain C++ compiler.
+#pragma once
+
+#include <string>
+
+#include "../../include/flexattn.h"
+#include "internal.hpp"
+
+namespace fa {
+
+// Largest block size fa_create_block_mask accepts, and the largest number of
+// key blocks per row (the builder keeps one byte per key block in LDS).
+constexpr int kMaxBlock = 1024;
+constexpr int kMaxKvBlocks = 32768;
+
+int check_block_mask_dims(int32_t q_len, int32_t kv_len, int32_t block_m,
+                          int32_t block_n, int32_t* nqb, int32_t* nkvb,
+                          std::string* msg);
+
+// Fills *out for launch_block_mask and the output fields of *bm on success.
+int check_create_block_mask(const fa_mask_mod* mask, int32_t B, int32_t H,
+                            int32_t q_len, int32_t kv_len, int32_t block_m,
+                            int32_t block_n, int32_t separate_full_blocks,
+                            fa_block_mask* bm, BlockMaskLaunch* out,
+                            std::string* msg);
+
+// Fills *out for the forward launchers on success. *nothing_to_do is set when
+// the problem is empty (B, H or q_len is 0): the call then succeeds without
+// launching anything.
+int check_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H, int32_t H_kv,
+                             int32_t q_len, int32_t kv_len, int32_t D,
+                             const void* q, const int64_t q_stride[3],
+                             const void* k, const int64_t k_stride[3],
+                             const void* v, const int64_t v_stride[3],
+                             float scale, const fa_block_mask* bm,
+                             const fa_score_mod* score, void* o, float* lse,
+                             FwdLaunch* out, bool* nothing_to_do,
+                             std::string* msg);
+
+}  // namespace fa

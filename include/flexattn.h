@@ -1,0 +1,217 @@
+/*
+ * flexattn.h - C ABI of the MI355X (gfx950) block-sparse masked attention
+ * library (libflexattn.so).
+ *
+ * Two operations, both FlexAttention-style:
+ *
+ *   fa_create_block_mask   turns a built-in mask_mod(b, h, q_idx, kv_idx)
+ *                          into per-query-block lists of partial and full
+ *                          key blocks ("How to Use FlexAttention on Apple
+ *                          Silicon", sections "The two hooks" and
+ *                          "Mask 1: causal"; tensorplay create_block_mask
+ *                          page, parameters BLOCK_SIZE and
+ *                          separate_full_blocks).
+ *   fa_flex_attention_fwd  fused attention forward over such a block mask:
+ *                          only live key blocks are read, mask_mod runs on
+ *                          partial blocks only, score_mod runs on every
+ *                          live position, and the softmax is computed online
+ *                          so no score matrix is ever stored (how-to,
+ *                          "The two hooks", "Bonus: a score_mod for
+ *                          soft-capping"; frontiernews, "What Is
+ *                          FlexAttention and Why Does It Matter").
+ *
+ * Conventions shared by every entry point
+ *   - Every pointer argument named "device" is HIP device memory owned by
+ *     the caller. The library never allocates, frees or synchronises; it
+ *     enqueues kernels on the caller's HIP stream (hipStream_t passed as
+ *     void*, NULL = the default stream) and returns.
+ *   - Arguments are checked on the host before anything is enqueued. On any
+ *     error nothing is launched and no output is written. A failed launch
+ *     returns FA_ERR_HIP. Faults inside a kernel surface at the caller's
+ *     next synchronisation, as for any HIP kernel.
+ *   - fa_last_error() gives a human-readable reason for the most recent
+ *     failure on the calling thread.
+ *   - The functions keep no state between calls and may be called from
+ *     several host threads.
+ */
+#ifndef FLEXATTN_H
+#define FLEXATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL                 */
+  FA_ERR_INVALID_VALUE = 2,  /* a value is out of its domain (W < 1, ...)  */
+  FA_ERR_UNSUPPORTED = 3,    /* valid, but not built (dtype, D, block, ...) */
+  FA_ERR_SHAPE_MISMATCH = 4, /* block mask and attention call disagree     */
+  FA_ERR_HIP = 5             /* the HIP runtime refused a launch           */
+} fa_status;
+
+typedef enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
+
+/* Built-in mask_mods. True = the (query, key) pair is allowed.
+ *   NONE            every pair ("either, both, or neither" hook may be
+ *                   given: how-to, "The two hooks")
+ *   CAUSAL          q_idx >= kv_idx (how-to, "Mask 1: causal")
+ *   SLIDING_WINDOW  0 <= q_idx - kv_idx < window; the window counts the
+ *                   diagonal (how-to, "Mask 2"; crackedaicode
+ *                   "Sliding-Window Self-Attention", "State the boundary
+ *                   precisely")
+ *   DOCUMENT        q_idx >= kv_idx and doc_id[q_idx] == doc_id[kv_idx]
+ *                   (how-to, "Mask 3: document-packed")
+ * None of them depends on the batch or head index. */
+typedef enum fa_mask_kind {
+  FA_MASK_NONE = 0,
+  FA_MASK_CAUSAL = 1,
+  FA_MASK_SLIDING_WINDOW = 2,
+  FA_MASK_DOCUMENT = 3
+} fa_mask_kind;
+
+/* Built-in score_mods, applied to the scaled score s = scale * q.k of
+ * every live position (how-to, "The two hooks" and "Bonus"):
+ *   NONE     s
+ *   SOFTCAP  softcap * tanh(s / softcap)
+ *   ALIBI    s - slope_h * (q_idx - kv_idx), slope_h = 2^(-8 (h + 1) / H),
+ *            h = query head, H = number of query heads. */
+typedef enum fa_score_kind {
+  FA_SCORE_NONE = 0,
+  FA_SCORE_SOFTCAP = 1,
+  FA_SCORE_ALIBI = 2
+} fa_score_kind;
+
+typedef struct fa_mask_mod {
+  int32_t kind;          /* fa_mask_kind                                  */
+  int32_t window;        /* SLIDING_WINDOW: W >= 1; ignored otherwise      */
+  const int32_t* doc_id; /* DOCUMENT: device int32 [doc_len], indexed by
+                            both q_idx and kv_idx; must outlive every use of
+                            a block mask built from it. NULL otherwise.    */
+  int64_t doc_len;       /* DOCUMENT: >= max(q_len, kv_len)                */
+} fa_mask_mod;
+
+typedef struct fa_score_mod {
+  int32_t kind;          /* fa_score_kind                                  */
+  float softcap;         /* SOFTCAP: finite and > 0; ignored otherwise     */
+} fa_score_mod;
+
+/* A block mask. The index arrays are caller-allocated device memory of
+ * int32; fa_create_block_mask fills them, fa_flex_attention_fwd reads them.
+ *   kv_num_blocks       [B, H, NQB]         partial blocks per query block
+ *                                           (every live block when
+ *                                           separate_full_blocks == 0)
+ *   kv_indices          [B, H, NQB, NKVB]   row m: the listed key blocks in
+ *                                           ascending order, then all other
+ *                                           key blocks in ascending order
+ *                                           (each row is a permutation)
+ *   full_kv_num_blocks  [B, H, NQB]         fully allowed blocks, on which
+ *   full_kv_indices     [B, H, NQB, NKVB]   mask_mod is skipped; NULL when
+ *                                           separate_full_blocks == 0
+ * NQB = ceil(q_len / block_m), NKVB = ceil(kv_len / block_n). A block cut
+ * by the end of a sequence is never full. B and H are 1 to broadcast one
+ * mask over every batch entry / head (B=None, H=None on the how-to's
+ * "Mask 1: causal"). The mask_mod is stored here: the attention call
+ * applies it to partial blocks. */
+typedef struct fa_block_mask {
+  fa_mask_mod mask;
+  int32_t B, H;
+  int32_t q_len, kv_len;
+  int32_t block_m, block_n;
+  int32_t num_q_blocks, num_kv_blocks;
+  int32_t separate_full_blocks;
+  int32_t* kv_num_blocks;
+  int32_t* kv_indices;
+  int32_t* full_kv_num_blocks;
+  int32_t* full_kv_indices;
+} fa_block_mask;
+
+/* Number of query and key blocks for the given lengths and block sizes.
+ * q_len, kv_len >= 0; 1 <= block_m, block_n <= 1024. Host only. */
+fa_status fa_block_mask_dims(int32_t q_len, int32_t kv_len, int32_t block_m,
+                             int32_t block_n, int32_t* num_q_blocks,
+                             int32_t* num_kv_blocks);
+
+/* create_block_mask (tensorplay create_block_mask page: the block mask is
+ * derived from a mask_mod; separate_full_blocks has the meaning given
+ * there).
+ *
+ * Classifies every (query block, key block) tile exactly, by evaluating
+ * mask_mod on each in-range pair of the tile: no allowed pair = empty,
+ * all block_m * block_n pairs allowed = full, otherwise partial (how-to,
+ * "The two mistakes": only fully masked blocks are skipped). Then writes the
+ * index lists described at fa_block_mask.
+ *
+ *   mask      host pointer; copied into bm->mask.
+ *   B, H      1 = broadcast, else the batch / head count (>= 1).
+ *   q_len, kv_len >= 0; 1 <= block_m, block_n <= 1024; NKVB <= 32768;
+ *             B * H * NQB * NKVB < 2^31.
+ *   bm        host pointer. In: the four device array pointers, sized as
+ *             above (full_* may be NULL iff separate_full_blocks == 0).
+ *             Out: every other field.
+ *   stream    hipStream_t or NULL.
+ * Two kernel launches (classify, then compact); asynchronous. kv_indices
+ * holds intermediate tile states between the two. */
+fa_status fa_create_block_mask(const fa_mask_mod* mask, int32_t B, int32_t H,
+                               int32_t q_len, int32_t kv_len, int32_t block_m,
+                               int32_t block_n, int32_t separate_full_blocks,
+                               fa_block_mask* bm, void* stream);
+
+/* Fused block-sparse attention forward (flex_attention(q, k, v,
+ * block_mask=, score_mod=) on the how-to's "Bonus" section; the shapes
+ * follow scaled_dot_product_attention, how-to FAQ "What tensor shape does
+ * flex_attention expect?").
+ *
+ *   dtype      FA_BF16 (bf16 inputs and O, fp32 accumulation) or FA_FP32.
+ *   B, H       batch and query-head counts (>= 0; 0 is a no-op).
+ *   H_kv       key/value heads, H % H_kv == 0; query head h reads key head
+ *              h / (H / H_kv).
+ *   q_len, kv_len  must equal bm->q_len, bm->kv_len.
+ *   D          head dimension: 64 or 128.
+ *   q          device [B, H, q_len, D] with element strides q_stride =
+ *              {batch, head, sequence}; the D axis is contiguous.
+ *   k, v       device [B, H_kv, kv_len, D], strides k_stride, v_stride.
+ *              Every row start must be 16-byte aligned.
+ *   scale      multiplies q.k before score_mod; finite and > 0
+ *              (1/sqrt(D) is the usual choice).
+ *   bm         host pointer to a block mask for (q_len, kv_len) with
+ *              bm->B in {1, B}, bm->H in {1, H}, and
+ *              block_m == block_n in {64, 128}. Index arrays may come from
+ *              fa_create_block_mask or from the caller; entries outside
+ *              [0, NKVB) are skipped and counts are clamped to [0, NKVB].
+ *   score      host pointer to the score_mod (NULL = none).
+ *   o          device [B, H, q_len, D], contiguous, dtype; 16-byte aligned.
+ *   lse        device fp32 [B, H, q_len], contiguous; may be NULL.
+ *              lse = ln sum_j exp(s_j) over the allowed keys of the row, in
+ *              natural log; a row with no allowed key gets o = 0 and
+ *              lse = -inf.
+ *   stream     hipStream_t or NULL.
+ * One kernel launch; asynchronous. */
+fa_status fa_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H,
+                                int32_t H_kv, int32_t q_len, int32_t kv_len,
+                                int32_t D, const void* q,
+                                const int64_t q_stride[3], const void* k,
+                                const int64_t k_stride[3], const void* v,
+                                const int64_t v_stride[3], float scale,
+                                const fa_block_mask* bm,
+                                const fa_score_mod* score, void* o, float* lse,
+                                void* stream);
+
+/* Static description of a status code. */
+const char* fa_status_string(int32_t status);
+
+/* Reason for the most recent non-FA_OK return on this host thread. */
+const char* fa_last_error(void);
+
+/* FA_ABI_VERSION of the built library. */
+int32_t fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLEXATTN_H */

@@ -1,0 +1,243 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function
+the header declares, its structs have the layout ctypes assumes, and bad
+arguments are refused on the host before anything reaches a GPU.
+
+No test here launches a kernel: every call below fails argument checking,
+which happens before any HIP call.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from block_sparse_masked_fa_amd import _capi as C
+from block_sparse_masked_fa_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flexattn.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(C.LIB_PATH),
+                               reason="libflexattn.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S[^\n(]*?\b(fa_[a-z_0-9]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_and_binding_agree():
+    declared = _declared_functions()
+    assert declared == sorted(C.SIGNATURES), declared
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", C.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_[a-z_0-9]+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, name
+    L = C.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name)
+    assert L.fa_abi_version() == C.ABI_VERSION
+
+
+def test_struct_layout_matches_c(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(f"""
+#include <stdio.h>
+#include <stddef.h>
+#include "{HEADER}"
+int main(void) {{
+  printf("%zu %zu %zu\\n", sizeof(fa_mask_mod), offsetof(fa_mask_mod, doc_id),
+         offsetof(fa_mask_mod, doc_len));
+  printf("%zu %zu\\n", sizeof(fa_score_mod), offsetof(fa_score_mod, softcap));
+  printf("%zu %zu %zu %zu %zu\\n", sizeof(fa_block_mask),
+         offsetof(fa_block_mask, B), offsetof(fa_block_mask, separate_full_blocks),
+         offsetof(fa_block_mask, kv_num_blocks),
+         offsetof(fa_block_mask, full_kv_indices));
+  return 0;
+}}
+""")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-o", str(exe), str(src)],
+                   check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True,
+                           check=True).stdout.split("\n")
+    got = [list(map(int, l.split())) for l in lines if l.strip()]
+    assert got[0] == [ctypes.sizeof(C.fa_mask_mod), C.fa_mask_mod.doc_id.offset,
+                      C.fa_mask_mod.doc_len.offset]
+    assert got[1] == [ctypes.sizeof(C.fa_score_mod),
+                      C.fa_score_mod.softcap.offset]
+    assert got[2] == [ctypes.sizeof(C.fa_block_mask), C.fa_block_mask.B.offset,
+                      C.fa_block_mask.separate_full_blocks.offset,
+                      C.fa_block_mask.kv_num_blocks.offset,
+                      C.fa_block_mask.full_kv_indices.offset]
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    for comp, ext in (("gcc", "c"), ("g++", "cpp")):
+        src = tmp_path / f"inc.{ext}"
+        src.write_text(f'#include "{HEADER}"\nint main(void){{return 0;}}\n')
+        subprocess.run([comp, "-Wall", "-Werror", "-o",
+                        str(tmp_path / f"inc_{ext}"), str(src)], check=True)
+
+
+@needs_lib
+def test_status_strings():
+    L = C.lib()
+    names = [L.fa_status_string(s).decode() for s in range(6)]
+    assert names == ["FA_OK", "FA_ERR_NULL_POINTER", "FA_ERR_INVALID_VALUE",
+                     "FA_ERR_UNSUPPORTED", "FA_ERR_SHAPE_MISMATCH",
+                     "FA_ERR_HIP"]
+    assert L.fa_status_string(99).decode() == "unknown fa_status"
+
+
+@needs_lib
+def test_block_mask_dims():
+    assert api.fa_block_mask_dims(256, 256, 64, 64) == (4, 4)
+    assert api.fa_block_mask_dims(300, 129, 128, 64) == (3, 3)
+    assert api.fa_block_mask_dims(0, 0, 128, 128) == (0, 0)
+    for bad in ((-1, 4, 4, 4), (4, 4, 0, 4), (4, 4, 4, 2000)):
+        with pytest.raises(C.FlexAttnError):
+            api.fa_block_mask_dims(*bad)
+    with pytest.raises(C.FlexAttnError, match="FA_ERR_UNSUPPORTED"):
+        api.fa_block_mask_dims(1 << 30, 1 << 30, 1, 1)
+
+
+FAKE = 1 << 20  # a non-null, 16-byte aligned address that is never touched
+
+
+def _bm(**kw):
+    b = C.fa_block_mask(kv_num_blocks=FAKE, kv_indices=FAKE,
+                        full_kv_num_blocks=FAKE, full_kv_indices=FAKE)
+    for k, v in kw.items():
+        setattr(b, k, v)
+    return b
+
+
+@needs_lib
+@pytest.mark.parametrize("mask,B,H,ql,kl,bm_,bn_,status", [
+    (C.fa_mask_mod(kind=C.FA_MASK_SLIDING_WINDOW, window=0), 1, 1, 64, 64,
+     64, 64, C.FA_ERR_INVALID_VALUE),
+    (C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT), 1, 1, 64, 64, 64, 64,
+     C.FA_ERR_NULL_POINTER),
+    (C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT, doc_id=FAKE, doc_len=63), 1, 1,
+     64, 64, 64, 64, C.FA_ERR_SHAPE_MISMATCH),
+    (C.fa_mask_mod(kind=7), 1, 1, 64, 64, 64, 64, C.FA_ERR_INVALID_VALUE),
+    (C.fa_mask_mod(kind=C.FA_MASK_CAUSAL), 0, 1, 64, 64, 64, 64,
+     C.FA_ERR_INVALID_VALUE),
+    (C.fa_mask_mod(kind=C.FA_MASK_CAUSAL), 1, 1, 64, 64, 0, 64,
+     C.FA_ERR_INVALID_VALUE),
+    (C.fa_mask_mod(kind=C.FA_MASK_CAUSAL), 1, 1, 64, 64, 64, 4096,
+     C.FA_ERR_UNSUPPORTED),
+    (C.fa_mask_mod(kind=C.FA_MASK_CAUSAL), 1, 1, -1, 64, 64, 64,
+     C.FA_ERR_INVALID_VALUE),
+])
+def test_create_block_mask_refuses(mask, B, H, ql, kl, bm_, bn_, status):
+    b = _bm()
+    st = api.fa_create_block_mask(mask, B, H, ql, kl, bm_, bn_, 1, b, None)
+    assert st == status, C.lib().fa_last_error()
+    assert C.lib().fa_last_error().decode()
+
+
+@needs_lib
+def test_create_block_mask_null_arrays():
+    m = C.fa_mask_mod(kind=C.FA_MASK_CAUSAL)
+    for field in ("kv_num_blocks", "kv_indices", "full_kv_num_blocks",
+                  "full_kv_indices"):
+        b = _bm(**{field: None})
+        st = api.fa_create_block_mask(m, 1, 1, 64, 64, 64, 64, 1, b, None)
+        assert st == C.FA_ERR_NULL_POINTER, field
+    st = C.lib().fa_create_block_mask(ctypes.byref(m), 1, 1, 64, 64, 64, 64,
+                                      1, None, None)
+    assert st == C.FA_ERR_NULL_POINTER
+    st = C.lib().fa_create_block_mask(None, 1, 1, 64, 64, 64, 64, 1,
+                                      ctypes.byref(_bm()), None)
+    assert st == C.FA_ERR_NULL_POINTER
+
+
+def _good_bm(q_len=256, kv_len=256, block=128, B=1, H=1):
+    nq = -(-q_len // block)
+    nk = -(-kv_len // block)
+    return _bm(mask=C.fa_mask_mod(kind=C.FA_MASK_CAUSAL), B=B, H=H,
+               q_len=q_len, kv_len=kv_len, block_m=block, block_n=block,
+               num_q_blocks=nq, num_kv_blocks=nk, separate_full_blocks=1)
+
+
+def _fwd(**over):
+    a = dict(dtype=C.FA_BF16, B=2, H=4, H_kv=4, q_len=256, kv_len=256, D=128,
+             q=FAKE, q_stride=(4 * 256 * 128, 256 * 128, 128), k=FAKE,
+             k_stride=(4 * 256 * 128, 256 * 128, 128), v=FAKE,
+             v_stride=(4 * 256 * 128, 256 * 128, 128), scale=0.088,
+             bm=_good_bm(), score=C.fa_score_mod(kind=C.FA_SCORE_NONE),
+             o=FAKE, lse=FAKE, stream=None)
+    a.update(over)
+    return api.fa_flex_attention_fwd(**a)
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=9), C.FA_ERR_INVALID_VALUE),
+    (dict(D=96), C.FA_ERR_UNSUPPORTED),
+    (dict(D=256), C.FA_ERR_UNSUPPORTED),
+    (dict(H_kv=3), C.FA_ERR_INVALID_VALUE),
+    (dict(H_kv=0), C.FA_ERR_INVALID_VALUE),
+    (dict(scale=0.0), C.FA_ERR_INVALID_VALUE),
+    (dict(scale=float("nan")), C.FA_ERR_INVALID_VALUE),
+    (dict(scale=float("inf")), C.FA_ERR_INVALID_VALUE),
+    (dict(q_len=128), C.FA_ERR_SHAPE_MISMATCH),
+    (dict(kv_len=512), C.FA_ERR_SHAPE_MISMATCH),
+    (dict(bm=_good_bm(B=3)), C.FA_ERR_SHAPE_MISMATCH),
+    (dict(bm=_good_bm(H=2)), C.FA_ERR_SHAPE_MISMATCH),
+    (dict(bm=_good_bm(block=32)), C.FA_ERR_UNSUPPORTED),
+    (dict(bm=_bm(**{**{f: getattr(_good_bm(), f) for f, _ in
+                       C.fa_block_mask._fields_}, "num_kv_blocks": 5})),
+     C.FA_ERR_SHAPE_MISMATCH),
+    (dict(score=C.fa_score_mod(kind=C.FA_SCORE_SOFTCAP, softcap=0.0)),
+     C.FA_ERR_INVALID_VALUE),
+    (dict(score=C.fa_score_mod(kind=C.FA_SCORE_SOFTCAP,
+                               softcap=float("inf"))),
+     C.FA_ERR_INVALID_VALUE),
+    (dict(score=C.fa_score_mod(kind=5)), C.FA_ERR_INVALID_VALUE),
+    (dict(q=None), C.FA_ERR_NULL_POINTER),
+    (dict(o=None), C.FA_ERR_NULL_POINTER),
+    (dict(k=None), C.FA_ERR_NULL_POINTER),
+    (dict(bm=None), C.FA_ERR_NULL_POINTER),
+    (dict(q=FAKE + 8), C.FA_ERR_UNSUPPORTED),
+    (dict(v=FAKE + 2), C.FA_ERR_UNSUPPORTED),
+    (dict(q_stride=(4 * 256 * 128, 256 * 128, 100)), C.FA_ERR_UNSUPPORTED),
+    (dict(k_stride=(4 * 256 * 128, -128, 128)), C.FA_ERR_INVALID_VALUE),
+    (dict(B=-1), C.FA_ERR_INVALID_VALUE),
+])
+def test_fwd_refuses(over, status):
+    if "bm" in over and over["bm"] is None:
+        a = dict(over)
+        st = C.lib().fa_flex_attention_fwd(
+            C.FA_BF16, 1, 1, 1, 256, 256, 128, FAKE, C.Stride3(1, 1, 128),
+            FAKE, C.Stride3(1, 1, 128), FAKE, C.Stride3(1, 1, 128), 0.1,
+            None, None, FAKE, FAKE, None)
+        assert st == status
+        return
+    st = _fwd(**over)
+    assert st == status, C.lib().fa_last_error()
+
+
+@needs_lib
+def test_fwd_empty_problem_is_a_noop():
+    # B = 0 or q_len = 0: succeeds without touching any pointer or the GPU
+    assert _fwd(B=0, q=None, k=None, v=None, o=None) == C.FA_OK
+    bm = _good_bm(q_len=0)
+    bm.num_q_blocks = 0
+    assert _fwd(q_len=0, bm=bm, q=None, o=None) == C.FA_OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(C, "_lib", None)
+    monkeypatch.setattr(C, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        C.lib()

@@ -1,0 +1,236 @@
+"""GPU parity of fa_flex_attention_fwd against the fp64 oracle, plus the
+special cases with exact answers.
+
+Small cases are compared on every row; the five workloads at full size are
+compared on a deterministic row sample (every row is computed on the GPU,
+the oracle evaluates the sampled rows one by one)."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_masked_fa_amd as fa
+import workloads as WL
+from oracle import oracle as O
+from tests.helpers import TOL, assert_close, oracle_case, sample_rows, \
+    torch_dtype
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _score_arg(score, cap):
+    if score == "softcap":
+        return ("softcap", cap)
+    return None if score == "none" else score
+
+
+def run_gpu(w: WL.Workload, q, k, v, doc=None, sep=True, score=None,
+            cap=None, bm=None):
+    score = w.score if score is None else score
+    cap = w.softcap if cap is None else cap
+    doc_t = torch.from_numpy(doc).to(DEV) if doc is not None else None
+    if bm is None:
+        bm = fa.create_block_mask(w.mask, None, None, w.q_len, w.kv_len,
+                                  device=DEV, BLOCK_SIZE=w.block_m,
+                                  separate_full_blocks=sep, window=w.window,
+                                  doc_id=doc_t)
+    o, lse = fa.flex_attention(q.to(DEV), k.to(DEV), v.to(DEV), bm,
+                               score_mod=_score_arg(score, cap),
+                               scale=w.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _inputs(w, seed):
+    rng = np.random.default_rng(seed)
+    q, k, v = WL.draw_qkv(rng, w)
+    dt = torch_dtype(w.dtype)
+    return tuple(torch.from_numpy(x).to(dt) for x in (q, k, v))
+
+
+SMALL = []
+for dtype, D, blk in (("bf16", 128, 128), ("bf16", 64, 128),
+                      ("bf16", 128, 64), ("bf16", 64, 64), ("fp32", 64, 64),
+                      ("fp32", 128, 128)):
+    for mask in ("causal", "sliding_window", "document", "none"):
+        for score in ("none", "softcap", "alibi"):
+            SMALL.append((dtype, D, blk, mask, score))
+
+
+@pytest.mark.parametrize("dtype,D,blk,mask,score", SMALL)
+def test_small_full_rows(dtype, D, blk, mask, score):
+    # several tiles plus a ragged tail on both sequence axes, q_len != kv_len,
+    # grouped heads
+    ql, kl = 3 * blk + 37, 2 * blk + 101
+    w = WL.Workload("small", dtype, 2, 4, 2, ql, kl, D, mask, blk, blk,
+                    seed=0, window=blk + 13 if mask == "sliding_window" else None,
+                    score=score, softcap=3.0 if score == "softcap" else None)
+    rng = np.random.default_rng(zlib.crc32(f"{dtype}{D}{blk}{mask}{score}".encode()))
+    doc = (np.sort(rng.integers(0, 4, max(ql, kl))).astype(np.int32)
+           if mask == "document" else None)
+    q, k, v = _inputs(w, 17)
+    print(f"[fwd small] {dtype} D={D} blk={blk} {mask} {score}", flush=True)
+    for sep in (True, False):
+        o, lse = run_gpu(w, q, k, v, doc, sep=sep)
+        o_ref, l_ref = oracle_case(q, k, v, w, doc)
+        assert_close(o, lse, o_ref, l_ref, TOL[dtype],
+                     f"{dtype} D={D} blk={blk} {mask} {score} sep={sep}")
+
+
+@pytest.fixture(scope="module")
+def workload_inputs():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache.clear()
+            w = WL.get(name)
+            q, k, v, doc = WL.make_inputs(w)
+            cache[name] = (w, q, k, v, doc)
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_workload_parity(name, workload_inputs):
+    w, q, k, v, doc = workload_inputs(name)
+    print(f"[fwd workload] {name}", flush=True)
+    o, lse = run_gpu(w, q, k, v, doc)
+    if name == "c1":
+        rows = None
+        o_s, l_s = o, lse
+    else:
+        rows = sample_rows(w.q_len, w.block_m, doc,
+                           n_random=64 if name in ("c2", "c3") else 24,
+                           seed=w.seed)
+        idx = torch.from_numpy(rows).to(DEV)
+        o_s, l_s = o.index_select(2, idx), lse.index_select(2, idx)
+    o_ref, l_ref = oracle_case(q, k, v, w, doc, rows=rows)
+    e_o, e_l = assert_close(o_s, l_s, o_ref, l_ref, TOL[w.dtype], name)
+    print(f"[fwd workload] {name}: max|dO|={e_o:.3g} max|dLSE|={e_l:.3g}",
+          flush=True)
+    # every row, not only the sampled ones, is finite
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_separate_full_blocks_agree_at_full_size(workload_inputs):
+    w, q, k, v, doc = workload_inputs("c3")
+    o1, l1 = run_gpu(w, q, k, v, doc, sep=True)
+    o2, l2 = run_gpu(w, q, k, v, doc, sep=False)
+    assert (o1.float() - o2.float()).abs().max().item() <= TOL["bf16"]
+    assert (l1 - l2).abs().max().item() <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,D,blk", [("bf16", 128, 128), ("bf16", 64, 64),
+                                         ("fp32", 64, 64)])
+@pytest.mark.parametrize("score", ["none", "softcap", "alibi"])
+def test_window_one_copies_values(dtype, D, blk, score):
+    # W = 1: every query sees only itself, so O_i = v_i exactly and
+    # LSE_i = score_mod(scale * q_i . k_i)
+    w = WL.Workload("w1", dtype, 1, 2, 2, 2 * blk + 5, 2 * blk + 5, D,
+                    "sliding_window", blk, blk, seed=0, window=1, score=score,
+                    softcap=2.0)
+    q, k, v = _inputs(w, 3)
+    o, lse = run_gpu(w, q, k, v)
+    assert torch.equal(o.cpu(), v), "O must equal V bit for bit"
+    _, l_ref = oracle_case(q, k, v, w)
+    assert np.abs(lse.cpu().double().numpy() - l_ref).max() <= TOL[dtype]
+
+
+@pytest.mark.parametrize("mask", ["causal", "sliding_window", "document"])
+def test_uniform_keys_give_log_counts(mask):
+    # K = 0, no score_mod: LSE_i = ln(number of allowed keys)
+    w = WL.Workload("k0", "bf16", 1, 2, 2, 600, 600, 128, mask, 128, 128,
+                    seed=0, window=150 if mask == "sliding_window" else None)
+    q, k, v = _inputs(w, 4)
+    k = torch.zeros_like(k)
+    doc = np.repeat(np.arange(3, dtype=np.int32), [100, 333, 167]) \
+        if mask == "document" else None
+    o, lse = run_gpu(w, q, k, v, doc)
+    allowed = O.dense_mask(mask, 600, 600, window=w.window, doc_id=doc)
+    n = allowed.sum(axis=1)
+    got = lse.cpu().double().numpy()
+    assert np.abs(got - np.log(n)[None, None]).max() < 1e-5
+    vo = torch.ones_like(v)
+    o1, _ = run_gpu(w, q, k, vo, doc)
+    assert (o1.float() - 1).abs().max().item() <= 2 ** -7
+
+
+def test_masked_positions_do_not_change_outputs():
+    # changing keys/values a query may not see leaves its output bit-identical
+    w = WL.Workload("inv", "bf16", 1, 2, 2, 512, 512, 128, "sliding_window",
+                    128, 128, seed=0, window=100)
+    q, k, v = _inputs(w, 5)
+    o, lse = run_gpu(w, q, k, v)
+    k2, v2 = k.clone(), v.clone()
+    k2[:, :, :50] += 7.0
+    v2[:, :, :50] -= 3.0
+    o2, l2 = run_gpu(w, q, k2, v2)
+    # rows >= 149 cannot see keys 0..49
+    assert torch.equal(o[:, :, 149:], o2[:, :, 149:])
+    assert torch.equal(lse[:, :, 149:], l2[:, :, 149:])
+    assert not torch.equal(o[:, :, :149], o2[:, :, :149])
+
+
+def test_rows_without_keys():
+    # q_len > kv_len with a sliding window: rows i >= kv_len + W - 1 have no
+    # allowed key, giving O = 0 and LSE = -inf
+    for dtype, blk in (("bf16", 128), ("fp32", 64)):
+        w = WL.Workload("empty", dtype, 1, 1, 1, 400, 150, 64,
+                        "sliding_window", blk, blk, seed=0, window=60)
+        q, k, v = _inputs(w, 6)
+        o, lse = run_gpu(w, q, k, v)
+        o_ref, l_ref = oracle_case(q, k, v, w)
+        assert np.isneginf(l_ref[0, 0, 209:]).all()
+        assert_close(o, lse, o_ref, l_ref, TOL[dtype], f"empty rows {dtype}")
+        assert (o[0, 0, 209:] == 0).all()
+
+
+def test_zero_length_keys():
+    w = WL.Workload("nokeys", "bf16", 1, 2, 2, 130, 0, 128, "causal", 128,
+                    128, seed=0)
+    q = torch.randn(1, 2, 130, 128).to(torch.bfloat16)
+    k = torch.zeros(1, 2, 0, 128, dtype=torch.bfloat16)
+    o, lse = run_gpu(w, q, k, k)
+    assert (o == 0).all() and torch.isneginf(lse).all()
+
+
+def test_repeated_runs_bit_identical(workload_inputs):
+    w, q, k, v, doc = workload_inputs("c3")
+    o1, l1 = run_gpu(w, q, k, v, doc)
+    for _ in range(3):
+        o2, l2 = run_gpu(w, q, k, v, doc)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_noncontiguous_views():
+    # q/k/v as (B, S, H, D) memory viewed as (B, H, S, D): strides are honoured
+    w = WL.Workload("view", "bf16", 2, 4, 4, 300, 300, 64, "causal", 64, 64,
+                    seed=0, score="alibi")
+    base = torch.randn(3, 2, 300, 4, 64).to(torch.bfloat16)
+    q, k, v = (base[i].transpose(1, 2) for i in range(3))
+    bm = fa.create_block_mask("causal", None, None, 300, 300, device=DEV,
+                              BLOCK_SIZE=64)
+    o, lse = fa.flex_attention(q.contiguous().to(DEV), k.contiguous().to(DEV),
+                               v.contiguous().to(DEV), bm, score_mod="alibi")
+    dq = base.to(DEV)
+    o2, l2 = fa.flex_attention(*(dq[i].transpose(1, 2) for i in range(3)), bm,
+                               score_mod="alibi")
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_case(q, k, v, w)
+    assert_close(o, lse, o_ref, l_ref, TOL["bf16"], "contiguous copy")
+    assert_close(o2, l2, o_ref, l_ref, TOL["bf16"], "strided view")
+
+
+def test_errors_surface_as_exceptions():
+    bm = fa.create_block_mask("causal", None, None, 256, 256, device=DEV,
+                              BLOCK_SIZE=128)
+    q = torch.randn(1, 1, 128, 128, device=DEV).to(torch.bfloat16)
+    with pytest.raises(fa.FlexAttnError, match="SHAPE_MISMATCH"):
+        fa.flex_attention(q, q, q, bm)
+    q = torch.randn(1, 1, 256, 96, device=DEV).to(torch.bfloat16)
+    with pytest.raises(fa.FlexAttnError, match="UNSUPPORTED"):
+        fa.flex_attention(q, q, q, bm)

@@ -1,0 +1,117 @@
+"""GPU parity of fa_create_block_mask: bit-exact against the oracle on every
+array, tails included, for the five workloads and random small cases."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_masked_fa_amd as fa
+import workloads as WL
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def gpu_mask(kind, B, H, ql, kl, bm_, bn_, window=None, doc=None, sep=True):
+    doc_t = (torch.from_numpy(np.ascontiguousarray(doc, np.int32)).to(DEV)
+             if doc is not None else None)
+    m = fa.create_block_mask(kind, B, H, ql, kl, device=DEV,
+                             BLOCK_SIZE=(bm_, bn_), separate_full_blocks=sep,
+                             window=window, doc_id=doc_t)
+    torch.cuda.synchronize()
+    out = {"kv_num_blocks": m.kv_num_blocks.cpu().numpy(),
+           "kv_indices": m.kv_indices.cpu().numpy()}
+    if sep:
+        out["full_kv_num_blocks"] = m.full_kv_num_blocks.cpu().numpy()
+        out["full_kv_indices"] = m.full_kv_indices.cpu().numpy()
+    return out
+
+
+def assert_same(got, want, label):
+    for key, arr in got.items():
+        ref = want[key]
+        assert arr.dtype == np.int32 and arr.shape == ref.shape, (label, key)
+        if not np.array_equal(arr, ref):
+            bad = np.argwhere(arr != ref)[:5]
+            raise AssertionError(f"{label} {key} differs at {bad.tolist()}")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_block_mask_workloads_bit_exact(name):
+    w = WL.get(name)
+    doc = None
+    if w.mask == "document":
+        rng = np.random.default_rng(w.seed)
+        doc = WL.doc_ids(WL.doc_lengths(rng, w.kv_len, w.n_docs,
+                                        w.min_doc_len))
+    print(f"[block mask] {name}", flush=True)
+    got = gpu_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_m, w.block_n,
+                   w.window, doc)
+    want = O.create_block_mask(w.mask, 1, 1, w.q_len, w.kv_len, w.block_m,
+                               w.block_n, window=w.window, doc_id=doc)
+    assert_same(got, want, name)
+
+
+def test_block_mask_known_counts():
+    # the hand counts of the oracle pins, now from the GPU builder
+    got = gpu_mask("sliding_window", 1, 1, 8192, 8192, 128, 128, window=1024)
+    assert got["kv_num_blocks"].sum() == 120
+    assert got["full_kv_num_blocks"].sum() == 420
+    got = gpu_mask("causal", 1, 1, 16384, 16384, 128, 128)
+    assert got["kv_num_blocks"].sum() == 128
+    assert got["full_kv_num_blocks"].sum() == 8128
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_block_mask_random_small(seed):
+    rng = np.random.default_rng(1000 + seed)
+    for _ in range(8):
+        ql = int(rng.integers(1, 700))
+        kl = int(rng.integers(1, 700))
+        bm_ = int(rng.choice([1, 3, 16, 32, 64, 100, 128]))
+        bn_ = int(rng.choice([1, 5, 16, 32, 64, 128, 200]))
+        if -(-kl // bn_) > 4096:
+            continue
+        kind = str(rng.choice(O.MASK_KINDS))
+        W = int(rng.integers(1, 300))
+        L = max(ql, kl)
+        doc = np.sort(rng.integers(0, 6, size=L)).astype(np.int32)
+        sep = bool(rng.integers(0, 2))
+        B, H = (int(x) for x in rng.choice([1, 2, 3], size=2))
+        label = f"{kind} ql={ql} kl={kl} bm={bm_} bn={bn_} W={W} sep={sep}"
+        print(f"[block mask] {label}", flush=True)
+        got = gpu_mask(kind, B, H, ql, kl, bm_, bn_, W, doc, sep)
+        want = O.create_block_mask(kind, B, H, ql, kl, bm_, bn_, window=W,
+                                   doc_id=doc, separate_full_blocks=sep)
+        assert_same(got, want, label)
+
+
+def test_block_mask_unsorted_document_ids():
+    # document ids need not be sorted or contiguous
+    rng = np.random.default_rng(7)
+    doc = rng.integers(0, 3, size=500).astype(np.int32)
+    got = gpu_mask("document", 1, 1, 500, 500, 32, 32, doc=doc)
+    want = O.create_block_mask("document", 1, 1, 500, 500, 32, 32,
+                               doc_id=doc)
+    assert_same(got, want, "unsorted docs")
+
+
+def test_block_mask_empty_lengths():
+    got = gpu_mask("causal", 1, 1, 0, 256, 128, 128)
+    assert got["kv_num_blocks"].shape == (1, 1, 0)
+    got = gpu_mask("causal", 1, 2, 256, 0, 128, 128)
+    assert got["kv_num_blocks"].shape == (1, 2, 2)
+    assert (got["kv_num_blocks"] == 0).all()
+    assert (got["full_kv_num_blocks"] == 0).all()
+    assert got["kv_indices"].shape == (1, 2, 2, 0)
+
+
+def test_block_mask_reuse_and_stream_order():
+    # building twice into fresh buffers on a side stream gives the same bits
+    a = gpu_mask("sliding_window", 2, 3, 1000, 1000, 64, 64, window=200)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        b = gpu_mask("sliding_window", 2, 3, 1000, 1000, 64, 64, window=200)
+    for k in a:
+        assert np.array_equal(a[k], b[k])
