@@ -1,0 +1,294 @@
+"""Benchmark of the block-sparse masked attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+build the block mask from the mask_mod (fa_create_block_mask) and run the
+fused forward (fa_flex_attention_fwd). Inputs are resident in HBM before the
+timed region starts. The JSON line reports live-block TFLOP/s:
+
+    sum over (b, h) of live blocks x 4 * BM * BN * D  /  time per step
+
+(partial blocks count their full area), its fraction of the bf16 MFMA peak,
+the speedup of the same kernel over a dense causal block mask at the same
+shape, and the oracle timed on the host cores as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as WL  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (published)
+FWD_KERNEL = "fwd_bf16_kernel"
+KERNEL_SOURCES = ["fwd_common.hpp", "fwd_bf16.hpp", "fwd_bf16_d64.hip",
+                  "fwd_bf16_d128.hip", "fwd_fp32.hpp", "fwd_fp32.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_masked_fa_amd", "csrc",
+                               name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def live_blocks(bm) -> int:
+    n = int(bm.kv_num_blocks.sum().item())
+    if bm.full_kv_num_blocks is not None:
+        n += int(bm.full_kv_num_blocks.sum().item())
+    return n
+
+
+def describe(w: WL.Workload) -> str:
+    s = (f"{w.name}: {w.dtype} B={w.B} H={w.H} Q=KV={w.q_len} D={w.D} "
+         f"{w.mask}")
+    if w.window:
+        s += f" W={w.window}"
+    if w.n_docs:
+        s += f" docs={w.n_docs}"
+    if w.score != "none":
+        s += f" score_mod={w.score}" + (f"({w.softcap:g})" if w.softcap
+                                         else "")
+    return s + f" BLOCK={w.block_m}"
+
+
+def traffic_for(workload: str):
+    """HBM bytes per forward launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"fwd_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, doc, live_flops, budget_s):
+    """Time the fp64 oracle on a bounded sample of query rows of the first
+    head and scale to the whole workload."""
+    from oracle import oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info
+                     if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    q1, k1, v1 = q[:1, :1], k[:1, :1], v[:1, :1]
+    kw = dict(mask=w.mask, score=w.score, scale=w.scale, window=w.window,
+              doc_id=doc, softcap=w.softcap)
+    rng = np.random.default_rng(123)
+    probe = np.sort(rng.choice(w.q_len, size=min(64, w.q_len), replace=False))
+    t0 = time.perf_counter()
+    O.attention(q1, k1, v1, rows=probe, **kw)
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n = int(min(w.q_len, max(64, budget_s / max(per_row, 1e-9))))
+    rows = np.sort(rng.choice(w.q_len, size=n, replace=False))
+    t0 = time.perf_counter()
+    O.attention(q1, k1, v1, rows=rows, **kw)
+    t = time.perf_counter() - t0
+    total_rows = w.B * w.H * w.q_len
+    t_full = t / n * total_rows
+    return {"value": live_flops / t_full / 1e12, "unit": "TFLOP/s",
+            "cores": int(cores), "kind": "oracle",
+            "sample": (f"{n} random query rows of head (0,0), dense fp64 "
+                       f"numpy, {t:.1f} s measured, scaled by "
+                       f"{total_rows}/{n} rows to {t_full:.0f} s")}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c3", choices=sorted(WL.CONFIGS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reference-masks", action="store_true",
+                    help="skip the dense-causal and no-skip timings")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB copy kernel (for counter "
+                         "calibration under rocprofv3 --pmc)")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        log("bench.py measures one GPU: this build has no multi-GPU path "
+            "(run with --gpus 1).")
+        return 2
+
+    import torch
+    import block_sparse_masked_fa_amd as fa
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WL.get(a.config)
+    log(f"[bench] generating inputs for {describe(w)}")
+    q, k, v, doc = WL.make_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    doc_t = torch.from_numpy(doc).to(dev) if doc is not None else None
+    score = {"none": None, "alibi": "alibi",
+             "softcap": ("softcap", w.softcap)}[w.score]
+    o = torch.empty_like(qd)
+    lse = torch.empty(qd.shape[:3], dtype=torch.float32, device=dev)
+
+    def build(mask_kind=w.mask):
+        return fa.create_block_mask(mask_kind, None, None, w.q_len, w.kv_len,
+                                    device=dev, BLOCK_SIZE=w.block_m,
+                                    window=w.window, doc_id=doc_t)
+
+    def fwd(bm):
+        fa.flex_attention(qd, kd, vd, bm, score_mod=score, scale=w.scale,
+                          out=o, lse=lse)
+
+    bm = build()
+    torch.cuda.synchronize()
+    live_bh = live_blocks(bm)                      # per (b, h): broadcast
+    flops_per_block = 4 * w.block_m * w.block_n * w.D
+    live_flops = live_bh * w.B * w.H * flops_per_block
+
+    for _ in range(a.warmup):
+        build()
+        fwd(bm)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+          for _ in range(a.steps)]
+    log(f"[bench] timing {a.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(a.steps):
+        ev[s][0].record(stream)
+        bm_s = build()
+        ev[s][1].record(stream)
+        fwd(bm_s)
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mask_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    fwd_ms = [e[1].elapsed_time(e[2]) for e in ev]
+    step_ms = ev[0][0].elapsed_time(ev[-1][2]) / a.steps
+    fwd_avg = float(np.mean(fwd_ms))
+    log(f"[bench] step {step_ms:.4f} ms (wall {wall / a.steps * 1e3:.4f}), "
+        f"fwd avg {fwd_avg:.4f} ms min {min(fwd_ms):.4f}, mask avg "
+        f"{np.mean(mask_ms):.4f} ms")
+
+    value = live_flops / (step_ms * 1e-3) / 1e12
+    achieved = live_flops / (fwd_avg * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    extra = {}
+    if not a.no_reference_masks:
+        def time_fwd(bm_x, reps=20):
+            for _ in range(3):
+                fwd(bm_x)
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for _ in range(reps):
+                fwd(bm_x)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            return s0.elapsed_time(s1) / reps
+
+        bm_c = build("causal")
+        torch.cuda.synchronize()
+        live_c = live_blocks(bm_c)
+        t_c = time_fwd(bm_c)
+        t_x = time_fwd(bm)
+        # no-skip: every key block listed as partial, mask_mod applied
+        nqb, nkvb = bm.num_q_blocks, bm.num_kv_blocks
+        allnum = torch.full((1, 1, nqb), nkvb, dtype=torch.int32, device=dev)
+        allidx = torch.arange(nkvb, dtype=torch.int32, device=dev).repeat(
+            1, 1, nqb, 1).contiguous()
+        bm_ns = fa.BlockMask.from_kv_blocks(
+            allnum, allidx, mask_mod=bm.mask, q_len=w.q_len, kv_len=w.kv_len,
+            BLOCK_SIZE=w.block_m)
+        t_ns = time_fwd(bm_ns, reps=5)
+        fl_c = live_c * w.B * w.H * flops_per_block
+        extra = {
+            "fwd_ms_config": round(t_x, 5),
+            "fwd_ms_dense_causal": round(t_c, 5),
+            "speedup_vs_dense_causal": round(t_c / t_x, 3),
+            "ideal_speedup_vs_dense_causal": round(live_c / live_bh, 3),
+            "dense_causal_tflops": round(fl_c / (t_c * 1e-3) / 1e12, 1),
+            "fwd_ms_no_skip": round(t_ns, 5),
+            "speedup_vs_no_skip": round(t_ns / t_x, 3),
+        }
+        log(f"[bench] causal {t_c:.4f} ms, config {t_x:.4f} ms, no-skip "
+            f"{t_ns:.4f} ms")
+
+    if a.copy_calibration:
+        # an elementwise kernel that reads 256 MiB and writes 256 MiB
+        x = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 1.0, out=y)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        cpu = cpu_baseline(w, q, k, v, doc, live_flops, a.cpu_budget)
+        log(f"[bench] oracle {cpu['value']:.3g} TFLOP/s ({cpu['sample']})")
+
+    traffic = traffic_for(w.name)
+    line = {
+        "metric": "live-block TFLOP/s (fraction of bf16 MFMA peak; speedup "
+                  "vs dense causal)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": describe(w), "global_batch": w.B,
+                   "seq_len": w.q_len, "heads": w.H, "head_dim": w.D,
+                   "block": w.block_m,
+                   "live_blocks_per_head": live_bh,
+                   "blocks_per_head": bm.num_q_blocks * bm.num_kv_blocks,
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(value / peak, 4),
+        "fwd_ms": round(fwd_avg, 5),
+        "mask_build_ms": round(float(np.mean(mask_ms)), 5),
+        **extra,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4),
+                     "traffic": traffic,
+                     "kernel": FWD_KERNEL,
+                     "per_launch_flops": live_flops},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,5 +1,6 @@
 // bf16 attention forward instances for head dimension 64.
 #include "fwd_bf16.hpp"
+#include "fwd_bf16_v2.hpp"
 
 namespace fa {
 
@@ -16,9 +17,14 @@ int launch_fwd_bf16_d64(const FwdLaunch& p, void* stream) {
     FA_CASE(64, FA_SCORE_NONE)
     FA_CASE(64, FA_SCORE_SOFTCAP)
     FA_CASE(64, FA_SCORE_ALIBI)
-    FA_CASE(128, FA_SCORE_NONE)
-    FA_CASE(128, FA_SCORE_SOFTCAP)
-    FA_CASE(128, FA_SCORE_ALIBI)
+#define FA_CASE2(SC)                                                          \
+  case 128 * 4 + SC:                                                          \
+    hipLaunchKernelGGL((fwd_bf16_v2_kernel<64, SC>), grid, dim3(512), 0, s, p); \
+    break;
+    FA_CASE2(FA_SCORE_NONE)
+    FA_CASE2(FA_SCORE_SOFTCAP)
+    FA_CASE2(FA_SCORE_ALIBI)
+#undef FA_CASE2
 #undef FA_CASE
     default:
       return hipErrorInvalidValue;
