@@ -1,71 +1,136 @@
-// Fused block-sparse attention forward, bf16 inputs, fp32 accumulation, on
-// gfx950 MFMA (v_mfma_f32_32x32x16_bf16).
+// Fused block-sparse attention forward, bf16 inputs, fp32 accumulation, for
+// gfx950 (MFMA v_mfma_f32_32x32x16_bf16, LDS DMA, transposed LDS reads).
 //
-// One workgroup computes one query block (BLK rows) of one head; BLK / 32
-// wavefronts each own 32 query rows. For every live key block of the row's
-// lists (full blocks first, then partial ones) the workgroup:
-//   1. stages the K tile [BLK keys][D] and the V tile, transposed to
-//      [D][BLK keys], in LDS from 16-byte coalesced global loads;
-//   2. computes S^T = K Q^T on MFMA. With keys on the MFMA row axis and
-//      queries on the column axis, each lane's 16 accumulator values belong
-//      to ONE query (column lane % 32), so a query row is spread over only
-//      two lanes (l and l + 32): row statistics are in-lane reductions plus
-//      one cross-half exchange;
-//   3. applies score_mod to every position and, on partial blocks only, the
-//      mask_mod (full blocks skip it: tensorplay create_block_mask page,
-//      separate_full_blocks);
-//   4. updates the online softmax (running max m, running sum l, rescale of
-//      the output accumulator by exp2(m_old - m_new)), so no score matrix is
-//      ever stored;
-//   5. rounds P to bf16 and accumulates O^T += V^T P^T on MFMA. The P values
-//      of step 2's accumulator are already laid out as the MFMA B operand;
-//      the MFMA contracts over its k slots in any consistent order, so the V^T
-//      tile is stored with keys permuted inside each group of 16 so that a
-//      lane's 8 slots are one 16-byte LDS read.
-// The epilogue writes O = acc / l (bf16) and LSE = m + ln l (fp32).
+// Work split. One workgroup computes one query block (BLK = 64 or 128 rows)
+// of one head with BLK / 32 wavefronts; wave w owns query rows
+// [32w, 32w + 32). Key blocks are consumed in stages of 64 keys. Two
+// workgroups share a CU (registers <= 256 per lane, 64 KB of LDS each at
+// D = 128), so while one is in its MFMA phase the other's softmax arithmetic
+// can issue: the two are independent and drift apart.
+//
+// Block order. A row's live key blocks are visited partial list first, then
+// the full list from the last block to the first. Under causal-style masks
+// this visits the keys nearest the query first; with a distance penalty
+// (ALiBi) the running maximum is then found early and later blocks rarely
+// raise it, so the output accumulator is rarely rescaled.
+//
+// Data movement. For each stage the K and V tiles [64 keys][D] go HBM -> LDS
+// with global_load_lds_dwordx4 (no register staging), double-buffered so the
+// next stage is in flight while this one is computed. In LDS a tile is
+// row-major with its 16-byte chunks XOR-swizzled per row; the swizzle makes
+// both read patterns conflict-free on the 64 LDS banks:
+//   * S^T = K Q^T takes K as the MFMA A operand: ds_read_b128, 16 rows x one
+//     chunk per 16 lanes;
+//   * O^T += V^T P^T needs V with keys along each lane's k slots:
+//     ds_read_b64_tr_b16 transposes on the fly from the row-major tile
+//     (4 rows x 4 chunks per 32 lanes).
+// Q^T is the B operand of S^T for the whole row and stays in registers. With
+// keys on the MFMA row axis, every accumulator value of a lane belongs to the
+// same query (column lane % 32), so row reductions are in-lane plus one
+// exchange with lane ^ 32, and P leaves the accumulator already laid out as
+// the B operand of the PV product (the MFMA contracts over its k slots in any
+// order that A and B agree on; the transposed V reads follow that order).
+//
+// Online softmax (log2 domain, exp2 on v_exp_f32). Per stage: s2 = score_mod
+// (scale * q.k) * log2(e); mask_mod on partial / sequence-tail blocks only;
+// row max; p = exp2(s2 - m_ref). The reference m_ref is raised only when the
+// row max exceeds it by more than kRescaleSlack (then l and the accumulator
+// are multiplied by exp2(m_old - m_new)); otherwise p may exceed 1 by at most
+// 2^kRescaleSlack, which fp32 and bf16 represent with the same relative
+// precision. The row sum adds the bf16-rounded p (v_dot2c_f32_bf16 against
+// ones), i.e. exactly the weights the PV product uses.
 #pragma once
 
 #include "fwd_common.hpp"
 
 namespace fa {
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void gbl_void;
+
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kStageKeys = 64;
+
+template <int D>
+__device__ __forceinline__ int kv_swizzle(int r) {
+  if constexpr (D == 128) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  }
+}
+
+__device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
+}
+
+// Workgroup -> (head, query block). Workgroups are dispatched round-robin over
+// the 8 XCDs (wg % 8). Logical items are dealt to XCDs in contiguous ranges so
+// that the query blocks of one head run on one XCD and share its L2; within a
+// head the heaviest query blocks (last rows under causal masks) come first.
+__device__ __forceinline__ bool xcd_work_item(const FwdLaunch& p, WorkItem& w) {
+  const int total = p.B * p.H * p.nqb;
+  const int per_xcd = (total + 7) >> 3;
+  const int wg = blockIdx.x;
+  const int logical = (wg & 7) * per_xcd + (wg >> 3);
+  if (logical >= total) return false;
+  w.m = p.nqb - 1 - (logical % p.nqb);
+  const int bh = logical / p.nqb;
+  w.h = bh % p.H;
+  w.b = bh / p.H;
+  return true;
+}
+
 template <int D, int BLK, int SCORE>
 __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) {
-  constexpr int NT = BLK * 2;     // threads: BLK / 32 waves of 64
-  constexpr int JT = BLK / 32;    // 32-key MFMA tiles per key block
-  constexpr int DK = D / 16;      // k-steps of QK^T
-  constexpr int DT = D / 32;      // 32-wide d tiles of the output
-  constexpr int KS = BLK / 16;    // k-steps of PV
-  constexpr int KST = D + 8;      // LDS row stride of K (elements)
-  constexpr int VST = BLK + 8;    // LDS row stride of V^T (elements)
+  constexpr int NW = BLK / 32;            // wavefronts
+  constexpr int NT = NW * 64;             // threads
+  constexpr int SPB = BLK / kStageKeys;   // stages per key block
+  constexpr int RB = D * 2;               // bytes per LDS row
+  constexpr int CPR = D / 8;              // 16-byte chunks per row
+  constexpr int RPK = 1024 / RB;          // rows per 1 KB DMA segment
+  constexpr int STAGE_BYTES = kStageKeys * RB;
+  constexpr int ROUNDS = STAGE_BYTES / (NT * 16);
+  constexpr int DK = D / 16;
+  constexpr int DT = D / 32;
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[BLK * KST];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[D * VST];
-  __shared__ int sDoc[BLK];
+  __shared__ __attribute__((aligned(1024))) char sK0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) int sDoc0[kStageKeys];
+  __shared__ __attribute__((aligned(16))) int sDoc1[kStageKeys];
+
+  WorkItem w;
+  if (!xcd_work_item(p, w)) return;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lq = lane & 31;
   const int g = lane >> 5;
 
-  const WorkItem w = work_item(p);
   const int hk = w.h / (p.H / p.H_kv);
-  const int i = w.m * BLK + wave * 32 + lq;  // this lane's query row
+  const int i = w.m * BLK + wave * 32 + lq;
   const bool i_ok = i < p.q_len;
   const int kv_len = p.kv_len;
   const int mkind = p.mask.kind;
   const int window = p.mask.window;
   const int* doc = p.mask.doc_id;
+  const bool doc_mask = mkind == FA_MASK_DOCUMENT;
 
   const __bf16* qp = static_cast<const __bf16*>(p.q) + w.b * p.qs[0] + w.h * p.qs[1];
-  const __bf16* kp = static_cast<const __bf16*>(p.k) + w.b * p.ks[0] + hk * p.ks[1];
-  const __bf16* vp = static_cast<const __bf16*>(p.v) + w.b * p.vs[0] + hk * p.vs[1];
-  const int64_t ks2 = p.ks[2];
-  const int64_t vs2 = p.vs[2];
+  const char* kbase = reinterpret_cast<const char*>(
+      static_cast<const __bf16*>(p.k) + w.b * p.ks[0] + hk * p.ks[1]);
+  const char* vbase = reinterpret_cast<const char*>(
+      static_cast<const __bf16*>(p.v) + w.b * p.vs[0] + hk * p.vs[1]);
+  const int64_t kstride = p.ks[2] * 2;  // bytes
+  const int64_t vstride = p.vs[2] * 2;
 
-  // Q^T as the MFMA B operand: column = query lq, k slots = d in
-  // [dk*16 + g*8, +8).
+  // Q^T as the MFMA B operand: column = query lq, k slots d in [16dk + 8g, +8)
   bf16x8 qf[DK];
   {
     const __bf16* row = qp + static_cast<int64_t>(i_ok ? i : 0) * p.qs[2];
@@ -76,9 +141,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
       qf[dk] = __builtin_bit_cast(bf16x8, x);
     }
   }
-  const int di = (mkind == FA_MASK_DOCUMENT) ? doc[i_ok ? i : 0] : 0;
+  const int di = doc_mask ? doc[i_ok ? i : 0] : 0;
 
-  // The row's block lists (broadcast over batch / head when Bm / Hm is 1).
+  // the row's block lists (broadcast over batch / head when Bm / Hm is 1)
   const int bb = p.Bm == 1 ? 0 : w.b;
   const int hh = p.Hm == 1 ? 0 : w.h;
   const int64_t lrow = (static_cast<int64_t>(bb) * p.Hm + hh) * p.nqb + w.m;
@@ -87,153 +152,237 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
   const int np = min(max(p.num[lrow], 0), nkvb);
   const int32_t* fl = p.fidx ? p.fidx + lrow * nkvb : nullptr;
   const int32_t* pl = p.idx + lrow * nkvb;
+  const int nblocks = nf + np;
+  const int nstages = nblocks * SPB;
 
   const ScoreConsts sc = make_score_consts(p, w.h);
 
-  float m_run = FA_NEG_INF;  // running max, log2 domain
-  float l_run = 0.0f;        // this lane's share of the running sum
+  // ---- per-lane byte offsets, fixed for the whole row
+  int k_rd[DK];  // K operand: row lq (+32 jt), chunk 2dk + g
+  {
+    const int s = kv_swizzle<D>(lq);
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) k_rd[dk] = lq * RB + (((2 * dk + g) ^ s) << 4);
+  }
+  int v_rd[2][DT];  // V^T operand: row 8*t2 + 4g + (lane%16)/4 (+16 kk)
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2) {
+    const int r = 8 * t2 + 4 * g + ((lane & 15) >> 2);
+    const int s = kv_swizzle<D>(r);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      v_rd[t2][dt] = r * RB + (((d >> 3) ^ s) << 4) + ((d & 7) << 1);
+    }
+  }
+  int dma_row[ROUNDS];      // DMA: row of this lane's chunk in each round
+  uint32_t dma_k[ROUNDS];   // byte offset from the stage's first K row
+  uint32_t dma_v[ROUNDS];
+  uint32_t dma_col[ROUNDS];
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    const int r = (rd * NW + wave) * RPK + lane / CPR;
+    const uint32_t col = static_cast<uint32_t>(((lane % CPR) ^ kv_swizzle<D>(r)) * 16);
+    dma_row[rd] = r;
+    dma_col[rd] = col;
+    dma_k[rd] = static_cast<uint32_t>(r * kstride) + col;
+    dma_v[rd] = static_cast<uint32_t>(r * vstride) + col;
+  }
+
+  // visiting order: partial blocks ascending, then full blocks descending
+  auto block_at = [&](int it) -> int { return it < np ? pl[it] : fl[nf - 1 - (it - np)]; };
+  auto masked_at = [&](int it, int n) -> bool {
+    return it < np || (n + 1) * BLK > kv_len;
+  };
+
+  // issue the DMA of stage `st` (block visit it = st / SPB) into one buffer
+  auto issue = [&](int st, char* sK, char* sV, int* sD) {
+    const int it = st / SPB;
+    const int n = block_at(it);
+    const int j0 = n * BLK + (st % SPB) * kStageKeys;
+    if (static_cast<unsigned>(n) >= static_cast<unsigned>(nkvb)) return;
+    const char* kb = kbase + j0 * kstride;
+    const char* vb = vbase + j0 * vstride;
+    if (j0 + kStageKeys <= kv_len) {
+#pragma unroll
+      for (int rd = 0; rd < ROUNDS; ++rd) {
+        const int seg = (rd * NW + wave) * 1024;
+        __builtin_amdgcn_global_load_lds((gbl_void*)(kb + dma_k[rd]), (lds_void*)(sK + seg), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(vb + dma_v[rd]), (lds_void*)(sV + seg), 16, 0, 0);
+      }
+    } else {
+      // sequence tail: rows past the end repeat the last row (masked later)
+#pragma unroll
+      for (int rd = 0; rd < ROUNDS; ++rd) {
+        const int seg = (rd * NW + wave) * 1024;
+        const int r = max(min(dma_row[rd], kv_len - 1 - j0), 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(kb + r * kstride + dma_col[rd]),
+                                         (lds_void*)(sK + seg), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gbl_void*)(vb + r * vstride + dma_col[rd]),
+                                         (lds_void*)(sV + seg), 16, 0, 0);
+      }
+    }
+    if (doc_mask && masked_at(it, n) && wave == 0) {
+      const int j = min(j0 + lane, kv_len - 1);
+      __builtin_amdgcn_global_load_lds((gbl_void*)(doc + j), (lds_void*)sD, 4, 0, 0);
+    }
+  };
+
+  float m_run = FA_NEG_INF;  // reference max, log2 domain
+  float l_run = 0.0f;        // this lane's share of the row sum
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  for (int it = 0; it < nf + np; ++it) {
-    const bool from_full = it < nf;
-    const int n = from_full ? fl[it] : pl[it - nf];
-    if (static_cast<unsigned>(n) >= static_cast<unsigned>(nkvb)) continue;
-    const int j0 = n * BLK;
-    const bool masked = !from_full || (j0 + BLK > kv_len);
+  auto compute = [&](int st, const char* sK, const char* sV, const int* sD) {
+    const int it = st / SPB;
+    const int n = block_at(it);
+    if (static_cast<unsigned>(n) >= static_cast<unsigned>(nkvb)) return;
+    const bool masked = masked_at(it, n);
+    const int j0 = n * BLK + (st % SPB) * kStageKeys;
 
-    __syncthreads();  // previous tile fully consumed
-    // ---- stage K [BLK][D]
-#pragma unroll
-    for (int c = tid; c < BLK * (D / 8); c += NT) {
-      const int r = c / (D / 8);
-      const int cc = c % (D / 8);
-      const int j = j0 + r;
-      u32x4 x = u32x4{0u, 0u, 0u, 0u};
-      if (j < kv_len) x = *reinterpret_cast<const u32x4*>(kp + j * ks2 + cc * 8);
-      *reinterpret_cast<u32x4*>(&sK[r * KST + cc * 8]) = x;
-    }
-    // ---- stage V^T [D][BLK] with the in-group key permutation: key
-    // 16G + 8a + 4s + c sits at column 16G + 8s + 4a + c.
-#pragma unroll
-    for (int t = tid; t < (BLK / 8) * (D / 8); t += NT) {
-      const int dc = t % (D / 8);
-      const int js = t / (D / 8);
-      const int G = js >> 1;
-      const int sg = js & 1;
-      u32x4 rv[8];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int j = j0 + 16 * G + 4 * sg + (r & 3) + 8 * (r >> 2);
-        rv[r] = u32x4{0u, 0u, 0u, 0u};
-        if (j < kv_len) rv[r] = *reinterpret_cast<const u32x4*>(vp + j * vs2 + dc * 8);
-      }
-#pragma unroll
-      for (int tt = 0; tt < 8; ++tt) {
-        u32x4 o;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t x = rv[2 * u][tt >> 1];
-          const uint32_t y = rv[2 * u + 1][tt >> 1];
-          o[u] = (tt & 1) ? ((x >> 16) | (y & 0xffff0000u)) : ((x & 0xffffu) | (y << 16));
-        }
-        *reinterpret_cast<u32x4*>(&sV[(dc * 8 + tt) * VST + 16 * G + 8 * sg]) = o;
-      }
-    }
-    if (masked && mkind == FA_MASK_DOCUMENT) {
-      for (int t = tid; t < BLK; t += NT) sDoc[t] = (j0 + t < kv_len) ? doc[j0 + t] : -1;
-    }
-    __syncthreads();
-
-    // ---- S^T = K Q^T
-    f32x16 s[JT];
-#pragma unroll
-    for (int jt = 0; jt < JT; ++jt) s[jt] = f32x16{};
+    // ---- S^T = K Q^T for the stage's 64 keys
+    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
 #pragma unroll
-      for (int jt = 0; jt < JT; ++jt) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&sK[(jt * 32 + lq) * KST + dk * 16 + g * 8]);
+      for (int jt = 0; jt < 2; ++jt) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + k_rd[dk] + jt * 32 * RB);
         s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[dk],
                                                         s[jt], 0, 0, 0);
       }
     }
 
-    // ---- score_mod on every position; key of (jt, r) is
-    // j0 + 4g + jt*32 + 8*(r/4) + r%4
-    const float ibase = static_cast<float>(i - j0 - 4 * g);
+    // ---- score_mod into the log2 domain (NONE keeps raw q.k: c > 0 is
+    // applied in the exponent). Key of (jt, r): j0 + 4g + 32jt + 8(r/4) + r%4.
+    if constexpr (SCORE == FA_SCORE_ALIBI) {
+      const float bias0 = sc.slope2 * static_cast<float>(j0 + 4 * g - i);
 #pragma unroll
-    for (int jt = 0; jt < JT; ++jt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        s[jt][r] = score2<SCORE>(s[jt][r], sc,
-                                 ibase - static_cast<float>(jt * 32 + 8 * (r >> 2) + (r & 3)));
-
-    // ---- mask_mod on partial (and sequence-tail) blocks only
-    if (masked) {
-#pragma unroll
-      for (int jt = 0; jt < JT; ++jt)
+      for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int jl = 4 * g + jt * 32 + 8 * (r >> 2) + (r & 3);
-          const int j = j0 + jl;
-          bool ok = j < kv_len;
-          switch (mkind) {
-            case FA_MASK_CAUSAL: ok &= mask_ok<FA_MASK_CAUSAL>(i, j, window, di, 0); break;
-            case FA_MASK_SLIDING_WINDOW: ok &= mask_ok<FA_MASK_SLIDING_WINDOW>(i, j, window, di, 0); break;
-            case FA_MASK_DOCUMENT: ok &= mask_ok<FA_MASK_DOCUMENT>(i, j, window, di, sDoc[jl]); break;
-            default: break;
-          }
-          s[jt][r] = ok ? s[jt][r] : FA_NEG_INF;
+          const float b = __builtin_fmaf(sc.slope2, static_cast<float>(32 * jt + 8 * (r >> 2) + (r & 3)), bias0);
+          s[jt][r] = __builtin_fmaf(s[jt][r], sc.c, b);
         }
+    } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
+      // cap * tanh(x) * log2e with tanh x = 1 - 2 / (e^{2x} + 1)
+      const float k2 = 2.0f * sc.cap_in * kLog2e;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = exp2_hw(s[jt][r] * k2);
+          const float t = __builtin_amdgcn_rcpf(e + 1.0f);
+          s[jt][r] = __builtin_fmaf(-2.0f * sc.cap_out, t, sc.cap_out);
+        }
+    }
+
+    // ---- mask_mod on partial and sequence-tail blocks only
+    if (masked) {
+      const int jb = j0 + 4 * g;
+#define FA_MASK_STAGE(KIND)                                                    \
+  _Pragma("unroll") for (int jt = 0; jt < 2; ++jt)                             \
+  _Pragma("unroll") for (int r4 = 0; r4 < 4; ++r4) {                           \
+    const int jl = 32 * jt + 8 * r4;                                           \
+    int dj[4] = {0, 0, 0, 0};                                                  \
+    if (KIND == FA_MASK_DOCUMENT) {                                            \
+      const int4 t = *reinterpret_cast<const int4*>(sD + 4 * g + jl);          \
+      dj[0] = t.x; dj[1] = t.y; dj[2] = t.z; dj[3] = t.w;                      \
+    }                                                                          \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c) {                            \
+      const int j = jb + jl + c;                                               \
+      const bool ok = (j < kv_len) & mask_ok<KIND>(i, j, window, di, dj[c]);   \
+      s[jt][4 * r4 + c] = ok ? s[jt][4 * r4 + c] : FA_NEG_INF;                 \
+    }                                                                          \
+  }
+      switch (mkind) {
+        case FA_MASK_CAUSAL: FA_MASK_STAGE(FA_MASK_CAUSAL) break;
+        case FA_MASK_SLIDING_WINDOW: FA_MASK_STAGE(FA_MASK_SLIDING_WINDOW) break;
+        case FA_MASK_DOCUMENT: FA_MASK_STAGE(FA_MASK_DOCUMENT) break;
+        default: FA_MASK_STAGE(FA_MASK_NONE) break;
+      }
+#undef FA_MASK_STAGE
     }
 
     // ---- online softmax
     float mx = FA_NEG_INF;
 #pragma unroll
-    for (int jt = 0; jt < JT; ++jt)
+    for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[jt][r]);
     mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = __builtin_fmaxf(m_run, mx);
-    const float m_use = (m_new == FA_NEG_INF) ? 0.0f : m_new;
-    const float alpha = exp2_hw(m_run - m_use);
-    m_run = m_new;
-    float rs = 0.0f;
+    if constexpr (SCORE == FA_SCORE_NONE) mx *= sc.c;  // raw -> log2 domain
+    const bool raise = mx > m_run + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float m_new = raise ? mx : m_run;
+      const float alpha = (m_new == m_run) ? 1.0f : exp2_hw(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int jt = 0; jt < JT; ++jt)
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == FA_NEG_INF) ? 0.0f : m_run;
+    bf16x8 pb[4];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = exp2_hw(s[jt][r] - m_use);
-        s[jt][r] = e;
-        rs += e;
+    for (int kk = 0; kk < 4; ++kk) {
+      f32x8 pf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = s[kk >> 1][(kk & 1) * 8 + e];
+        if constexpr (SCORE == FA_SCORE_NONE) {
+          pf[e] = exp2_hw(__builtin_fmaf(x, sc.c, -m_use));
+        } else {
+          pf[e] = exp2_hw(x - m_use);
+        }
       }
-    l_run = l_run * alpha + rs;
+      pb[kk] = __builtin_convertvector(pf, bf16x8);
+      const u32x4 pw = __builtin_bit_cast(u32x4, pb[kk]);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+      for (int e = 0; e < 4; ++e) {
+        // copy the word out first: bit-casting a vector element in place
+        // mis-compiles (every iteration reads element 0)
+        const uint32_t word = pw[e];
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, l_run,
+                                                false);
+      }
+    }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T (4 k-steps of 16 keys)
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const f32x16& src = s[kk >> 1];
-      const int h8 = (kk & 1) * 8;
-      const f32x8 pf = {src[h8 + 0], src[h8 + 1], src[h8 + 2], src[h8 + 3],
-                        src[h8 + 4], src[h8 + 5], src[h8 + 6], src[h8 + 7]};
-      const bf16x8 pb = __builtin_convertvector(pf, bf16x8);
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&sV[(dt * 32 + lq) * VST + kk * 16 + g * 8]);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb,
+        const i16x4 lo = lds_read_tr(sV + v_rd[0][dt] + kk * 16 * RB);
+        const i16x4 hi = lds_read_tr(sV + v_rd[1][dt] + kk * 16 * RB);
+        const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[kk],
                                                            oacc[dt], 0, 0, 0);
       }
     }
+  };
+
+  // ---- main loop over stages, unrolled by two so each LDS buffer is its
+  // own object; the DMA of stage st + 1 overlaps the compute of stage st.
+  if (nstages > 0) issue(0, sK0, sV0, sDoc0);
+  for (int st = 0; st < nstages; st += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's DMA landed
+    __syncthreads();                     // every lane's DMA landed; buffer 1 free
+    if (st + 1 < nstages) issue(st + 1, sK1, sV1, sDoc1);
+    compute(st, sK0, sV0, sDoc0);
+    if (st + 1 >= nstages) break;
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    if (st + 2 < nstages) issue(st + 2, sK0, sV0, sDoc0);
+    compute(st + 1, sK1, sV1, sDoc1);
   }
 
-  // ---- epilogue
+  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (i_ok) {
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const int64_t orow = (static_cast<int64_t>(w.b) * p.H + w.h) * p.q_len + i;
     __bf16* op = static_cast<__bf16*>(p.o) + orow * D;
 #pragma unroll

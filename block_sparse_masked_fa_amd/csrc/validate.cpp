@@ -224,6 +224,10 @@ int check_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H, int32_t H_kv,
     if ((st = check_strides("k", k_stride, kd, elt, msg)) != FA_OK) return st;
     if ((st = check_strides("v", v_stride, kd, elt, msg)) != FA_OK) return st;
   }
+  // the bf16 kernels address a 64-row stage of K / V with 32-bit byte offsets
+  if (kv_len > 0 && (k_stride[2] * elt * 64 >= (int64_t(1) << 31) ||
+                     v_stride[2] * elt * 64 >= (int64_t(1) << 31)))
+    return fail(msg, FA_ERR_UNSUPPORTED, "k / v sequence stride too large");
   if (!aligned16(q) || !aligned16(o) ||
       (kv_len > 0 && (!aligned16(k) || !aligned16(v))))
     return fail(msg, FA_ERR_UNSUPPORTED, "q, k, v and o must be 16-byte aligned");
