@@ -1,25 +1,33 @@
-// create_block_mask on gfx950: exact tile classification, then per-row
-// compaction with wavefront ballots and prefix counts.
+// create_block_mask on gfx950: one kernel classifies every tile of a query
+// block row exactly, then compacts the row's index lists with wavefront
+// ballots and prefix counts.
 //
 // The block mask (tensorplay create_block_mask page, parameters BLOCK_SIZE
-// and separate_full_blocks) records, for each query block m, which key blocks
-// hold at least one allowed pair. Only fully masked blocks may be skipped
-// (how-to "How to Use FlexAttention on Apple Silicon", "The two mistakes"),
-// and fully allowed blocks can be listed apart so the attention kernel skips
-// mask_mod on them (tensorplay page, separate_full_blocks).
+// and separate_full_blocks) records, for query block m, which key blocks hold
+// at least one allowed pair. Only fully masked blocks may be skipped (how-to
+// "How to Use FlexAttention on Apple Silicon", "The two mistakes"); fully
+// allowed blocks are listed apart so the attention kernel skips mask_mod on
+// them (tensorplay page, separate_full_blocks).
 //
-// Two launches on the caller's stream:
-//   classify_kernel  one wavefront per (query block, key block) tile. Each
-//                    lane evaluates mask_mod on its columns for every row of
-//                    the tile; the wave combines the per-pair results with
-//                    ballots. Tile state (0 empty, 1 partial, 2 full) is
-//                    written into kv_indices[.., m, n], which serves as the
-//                    state array until the second launch overwrites it.
-//   compact_kernel   one workgroup per query-block row. Loads the row's
-//                    states into LDS, counts, then writes each index list as
-//                    a stable partition (listed blocks ascending, then the
-//                    rest ascending) using ballot + mbcnt prefix counts.
+// Tile state over the in-range pairs (i, j) of a tile: no allowed pair =
+// empty, every pair of a complete (uncut) tile allowed = full, else partial.
+// How the kernel decides it, exactly, per mask kind:
+//   * none, causal, sliding window: the predicate depends only on d = i - j,
+//     and the pairs of a tile realise every integer d in
+//     [i_lo - j_hi, i_hi - j_lo]. "Some pair allowed" and "all pairs allowed"
+//     are therefore interval tests on that range (one thread per tile).
+//   * document: a wavefront per tile. If the key block is one document c,
+//     allowed pairs can only sit on the query rows of document c, and some
+//     (i, j) with i >= j exists among them iff the last such row is >= the
+//     block's first key; all pairs are allowed iff the query block is also
+//     all document c and lies wholly below the diagonal. A key block that
+//     mixes documents has every pair evaluated (ids need not be sorted or
+//     contiguous).
+// Compaction writes, per row, the listed blocks in ascending order followed by
+// the remaining block numbers in ascending order (a stable partition).
 #include <hip/hip_runtime.h>
+
+#include <climits>
 
 #include "../../include/flexattn.h"
 #include "internal.hpp"
@@ -27,79 +35,92 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 16;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kEmpty = 0, kPartial = 1, kFull = 2;
+constexpr unsigned char kEmpty = 0, kPartial = 1, kFull = 2;
 
-// Evaluate the mask over one tile with one wavefront; returns the tile
-// state, uniform across the wave.
-template <int KIND>
-__device__ int classify_tile(const MaskParams& mp, int i0, int rows, int j0,
-                             int cols, int area, int lane) {
+struct Tile {
+  int i_lo, i_hi, j_lo, j_hi;  // inclusive in-range bounds
+  bool complete;               // rows * cols == block area
+};
+
+__device__ __forceinline__ Tile make_tile(const BlockMaskLaunch& p, int m, int n) {
+  Tile t;
+  t.i_lo = m * p.block_m;
+  t.i_hi = min(t.i_lo + p.block_m, p.q_len) - 1;
+  t.j_lo = n * p.block_n;
+  t.j_hi = min(t.j_lo + p.block_n, p.kv_len) - 1;
+  t.complete = (t.i_hi - t.i_lo + 1) == p.block_m && (t.j_hi - t.j_lo + 1) == p.block_n;
+  return t;
+}
+
+// d = i - j over the tile spans [dlo, dhi]; allowed d form [alo, ahi].
+__device__ __forceinline__ unsigned char classify_range(const Tile& t, long long alo,
+                                                        long long ahi) {
+  const long long dlo = static_cast<long long>(t.i_lo) - t.j_hi;
+  const long long dhi = static_cast<long long>(t.i_hi) - t.j_lo;
+  if (dhi < alo || dlo > ahi) return kEmpty;
+  if (dlo >= alo && dhi <= ahi && t.complete) return kFull;
+  return kPartial;
+}
+
+__device__ __forceinline__ unsigned char classify_closed(const BlockMaskLaunch& p, int m, int n) {
+  const Tile t = make_tile(p, m, n);
+  switch (p.mask.kind) {
+    case FA_MASK_CAUSAL:
+      return classify_range(t, 0, 1LL << 40);
+    case FA_MASK_SLIDING_WINDOW:
+      return classify_range(t, 0, static_cast<long long>(p.mask.window) - 1);
+    default:  // none
+      return t.complete ? kFull : kPartial;
+  }
+}
+
+// Document mask, one wavefront per tile. `qdoc` holds the query block's
+// document ids in LDS; `qsingle` is the id when the whole query block is one
+// document, else INT_MIN.
+__device__ unsigned char classify_document(const BlockMaskLaunch& p, int m, int n,
+                                           const int* qdoc, int qsingle, int lane) {
+  const Tile t = make_tile(p, m, n);
+  const int* doc = p.mask.doc_id;
+  const int cols = t.j_hi - t.j_lo + 1;
+  const int rows = t.i_hi - t.i_lo + 1;
+  // is the key block a single document c?
+  const int c = __builtin_amdgcn_readfirstlane(doc[t.j_lo]);
+  bool other = false;
+  for (int jj = lane; jj < cols; jj += 64) other |= doc[t.j_lo + jj] != c;
+  if (!__builtin_amdgcn_ballot_w64(other)) {
+    // pairs can only be allowed on rows of document c; (i, j) with i >= j
+    // exists among them iff the last such row is >= the first key j_lo
+    int last = -1;
+    for (int base = 0; base < rows; base += 64) {
+      const int r = base + lane;
+      const unsigned long long hit =
+          __builtin_amdgcn_ballot_w64(r < rows && qdoc[min(r, rows - 1)] == c);
+      if (hit) last = t.i_lo + base + 63 - __builtin_clzll(hit);
+    }
+    if (last < t.j_lo) return kEmpty;
+    // every pair allowed: one document on both sides and below the diagonal
+    if (qsingle == c && t.i_lo >= t.j_hi && t.complete) return kFull;
+    return kPartial;
+  }
+  // the key block mixes documents: evaluate every pair
   bool any_true = false, any_false = false;
-  const int* doc = mp.doc_id;
   for (int jc = 0; jc < cols; jc += 64) {
     const int jj = jc + lane;
-    const bool in_range = jj < cols;
-    const int j = j0 + (in_range ? jj : 0);
-    int dj = 0;
-    if (KIND == FA_MASK_DOCUMENT) dj = doc[j];
+    const bool in = jj < cols;
+    const int j = t.j_lo + (in ? jj : 0);
+    const int dj = doc[j];
     for (int r = 0; r < rows; ++r) {
-      const int i = i0 + r;
-      bool ok;
-      if (KIND == FA_MASK_NONE) {
-        ok = true;
-      } else if (KIND == FA_MASK_CAUSAL) {
-        ok = i >= j;
-      } else if (KIND == FA_MASK_SLIDING_WINDOW) {
-        const int d = i - j;
-        ok = (d >= 0) & (d < mp.window);
-      } else {
-        ok = (i >= j) & (doc[i] == dj);
-      }
-      const unsigned long long yes = __builtin_amdgcn_ballot_w64(in_range && ok);
-      const unsigned long long no = __builtin_amdgcn_ballot_w64(in_range && !ok);
-      any_true |= yes != 0ull;
-      any_false |= no != 0ull;
+      const int i = t.i_lo + r;
+      const bool ok = (i >= j) & (qdoc[r] == dj);
+      any_true |= __builtin_amdgcn_ballot_w64(in && ok) != 0ull;
+      any_false |= __builtin_amdgcn_ballot_w64(in && !ok) != 0ull;
       if (any_true && any_false) return kPartial;
     }
   }
   if (!any_true) return kEmpty;
-  // every in-range pair allowed: full only if the tile is not cut short
-  return (rows * cols == area) ? kFull : kPartial;
-}
-
-__global__ __launch_bounds__(kThreads) void classify_kernel(BlockMaskLaunch p,
-                                                             int chunks) {
-  const int wave = threadIdx.x / 64;
-  const int lane = threadIdx.x % 64;
-  const int bid = blockIdx.x;
-  const int chunk = bid % chunks;
-  const int row = bid / chunks;            // (b, h, m) flattened
-  const int m = row % p.nqb;
-  const int n = chunk * kWaves + wave;
-  if (n >= p.nkvb) return;
-  const int i0 = m * p.block_m;
-  const int j0 = n * p.block_n;
-  const int rows = min(p.block_m, p.q_len - i0);
-  const int cols = min(p.block_n, p.kv_len - j0);
-  const int area = p.block_m * p.block_n;
-  int state;
-  switch (p.mask.kind) {
-    case FA_MASK_CAUSAL:
-      state = classify_tile<FA_MASK_CAUSAL>(p.mask, i0, rows, j0, cols, area, lane);
-      break;
-    case FA_MASK_SLIDING_WINDOW:
-      state = classify_tile<FA_MASK_SLIDING_WINDOW>(p.mask, i0, rows, j0, cols, area, lane);
-      break;
-    case FA_MASK_DOCUMENT:
-      state = classify_tile<FA_MASK_DOCUMENT>(p.mask, i0, rows, j0, cols, area, lane);
-      break;
-    default:
-      state = classify_tile<FA_MASK_NONE>(p.mask, i0, rows, j0, cols, area, lane);
-      break;
-  }
-  if (lane == 0) p.idx[static_cast<int64_t>(row) * p.nkvb + n] = state;
+  return t.complete ? kFull : kPartial;
 }
 
 // Exclusive prefix count of `flag` over the workgroup for one chunk of
@@ -113,6 +134,7 @@ __device__ int wg_exclusive_count(bool flag, int* wave_counts, int* chunk_total)
   if ((threadIdx.x % 64) == 0) wave_counts[wave] = __builtin_popcountll(mask);
   __syncthreads();
   int before = 0, total = 0;
+#pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     const int c = wave_counts[w];
     before += (w < wave) ? c : 0;
@@ -123,31 +145,53 @@ __device__ int wg_exclusive_count(bool flag, int* wave_counts, int* chunk_total)
   return before + lane_prefix;
 }
 
-__global__ __launch_bounds__(kThreads) void compact_kernel(BlockMaskLaunch p) {
-  extern __shared__ unsigned char states[];   // nkvb bytes
+__global__ __launch_bounds__(kThreads) void block_mask_kernel(BlockMaskLaunch p) {
+  extern __shared__ unsigned char states[];  // nkvb bytes
   __shared__ int wave_counts[kWaves];
   __shared__ int totals[2];
-  const int row = blockIdx.x;
+  __shared__ int qdoc[1024];  // document ids of the query block's rows
+  const int row = blockIdx.x;  // (b, h, m) flattened
+  const int m = row % p.nqb;
   const int nkvb = p.nkvb;
+  const int wave = threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
   const bool sep = p.separate_full != 0;
-  int32_t* idx = p.idx + static_cast<int64_t>(row) * nkvb;
-  int32_t* fidx = sep ? p.fidx + static_cast<int64_t>(row) * nkvb : nullptr;
 
+  // ---- classify
+  if (p.mask.kind == FA_MASK_DOCUMENT) {
+    const int i_lo = m * p.block_m;
+    const int rows = min(i_lo + p.block_m, p.q_len) - i_lo;
+    for (int r = threadIdx.x; r < rows; r += kThreads) qdoc[r] = p.mask.doc_id[i_lo + r];
+    __syncthreads();
+    const int first = qdoc[0];
+    bool other = false;
+    for (int r = threadIdx.x; r < rows; r += kThreads) other |= qdoc[r] != first;
+    const int qsingle = __syncthreads_or(other) ? INT_MIN : first;
+    for (int n = wave; n < nkvb; n += kWaves) {
+      const unsigned char s = classify_document(p, m, n, qdoc, qsingle, lane);
+      if (lane == 0) states[n] = s;
+    }
+  } else {
+    for (int n = threadIdx.x; n < nkvb; n += kThreads) states[n] = classify_closed(p, m, n);
+  }
   if (threadIdx.x < 2) totals[threadIdx.x] = 0;
+  __syncthreads();
+
+  // ---- count, then compact as a stable partition
   int np = 0, nf = 0;
   for (int n = threadIdx.x; n < nkvb; n += kThreads) {
-    const int s = idx[n];
-    states[n] = static_cast<unsigned char>(s);
+    const int s = states[n];
     np += sep ? (s == kPartial) : (s != kEmpty);
     nf += sep && (s == kFull);
   }
-  __syncthreads();
   atomicAdd(&totals[0], np);
   atomicAdd(&totals[1], nf);
   __syncthreads();
   const int tot_p = totals[0];
   const int tot_f = totals[1];
 
+  int32_t* idx = p.idx + static_cast<int64_t>(row) * nkvb;
+  int32_t* fidx = sep ? p.fidx + static_cast<int64_t>(row) * nkvb : nullptr;
   int run_p = 0, run_f = 0;
   for (int base = 0; base < nkvb; base += kThreads) {
     const int n = base + threadIdx.x;
@@ -177,14 +221,7 @@ int launch_block_mask(const BlockMaskLaunch& p, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int rows = p.Bm * p.Hm * p.nqb;
   if (rows == 0) return hipSuccess;
-  if (p.nkvb > 0) {
-    const int chunks = (p.nkvb + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL(classify_kernel, dim3(rows * chunks), dim3(kThreads), 0,
-                       s, p, chunks);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(compact_kernel, dim3(rows), dim3(kThreads),
+  hipLaunchKernelGGL(block_mask_kernel, dim3(rows), dim3(kThreads),
                      static_cast<size_t>(p.nkvb), s, p);
   return hipGetLastError();
 }

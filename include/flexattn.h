@@ -140,11 +140,11 @@ fa_status fa_block_mask_dims(int32_t q_len, int32_t kv_len, int32_t block_m,
  * derived from a mask_mod; separate_full_blocks has the meaning given
  * there).
  *
- * Classifies every (query block, key block) tile exactly, by evaluating
- * mask_mod on each in-range pair of the tile: no allowed pair = empty,
- * all block_m * block_n pairs allowed = full, otherwise partial (how-to,
- * "The two mistakes": only fully masked blocks are skipped). Then writes the
- * index lists described at fa_block_mask.
+ * Classifies every (query block, key block) tile exactly over its in-range
+ * (q_idx, kv_idx) pairs: no allowed pair = empty, all block_m * block_n
+ * pairs allowed = full, otherwise partial (how-to, "The two mistakes": only
+ * fully masked blocks are skipped). Then writes the index lists described at
+ * fa_block_mask.
  *
  *   mask      host pointer; copied into bm->mask.
  *   B, H      1 = broadcast, else the batch / head count (>= 1).
@@ -154,8 +154,7 @@ fa_status fa_block_mask_dims(int32_t q_len, int32_t kv_len, int32_t block_m,
  *             above (full_* may be NULL iff separate_full_blocks == 0).
  *             Out: every other field.
  *   stream    hipStream_t or NULL.
- * Two kernel launches (classify, then compact); asynchronous. kv_indices
- * holds intermediate tile states between the two. */
+ * One kernel launch; asynchronous. */
 fa_status fa_create_block_mask(const fa_mask_mod* mask, int32_t B, int32_t H,
                                int32_t q_len, int32_t kv_len, int32_t block_m,
                                int32_t block_n, int32_t separate_full_blocks,
