@@ -52,6 +52,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void gbl_void;
 
 constexpr float kRescaleSlack = 8.0f;
+// Buffer resource word 3 for raw (unformatted, unswizzled) dword access.
+constexpr int kBufferFlags = 0x00020000;
 constexpr int kStageKeys = 64;
 
 template <int D>
@@ -175,16 +177,12 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
       v_rd[t2][dt] = r * RB + (((d >> 3) ^ s) << 4) + ((d & 7) << 1);
     }
   }
-  int dma_row[ROUNDS];      // DMA: row of this lane's chunk in each round
-  uint32_t dma_k[ROUNDS];   // byte offset from the stage's first K row
-  uint32_t dma_v[ROUNDS];
-  uint32_t dma_col[ROUNDS];
+  uint32_t dma_k[ROUNDS];  // DMA: byte offset of this lane's chunk from the
+  uint32_t dma_v[ROUNDS];  // stage's first K / V row
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     const int r = (rd * NW + wave) * RPK + lane / CPR;
     const uint32_t col = static_cast<uint32_t>(((lane % CPR) ^ kv_swizzle<D>(r)) * 16);
-    dma_row[rd] = r;
-    dma_col[rd] = col;
     dma_k[rd] = static_cast<uint32_t>(r * kstride) + col;
     dma_v[rd] = static_cast<uint32_t>(r * vstride) + col;
   }
@@ -195,32 +193,31 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
     return it < np || (n + 1) * BLK > kv_len;
   };
 
-  // issue the DMA of stage `st` (block visit it = st / SPB) into one buffer
+  // Issue the DMA of stage `st` (block visit st / SPB) into one buffer. Each
+  // tile is read through a buffer resource whose base is the stage's first
+  // row and whose size ends at the sequence end: rows past it read as zeros
+  // (the hardware range check), so the tail needs no special path.
   auto issue = [&](int st, char* sK, char* sV, int* sD) {
     const int it = st / SPB;
     const int n = block_at(it);
-    const int j0 = n * BLK + (st % SPB) * kStageKeys;
     if (static_cast<unsigned>(n) >= static_cast<unsigned>(nkvb)) return;
-    const char* kb = kbase + j0 * kstride;
-    const char* vb = vbase + j0 * vstride;
-    if (j0 + kStageKeys <= kv_len) {
+    const int j0 = n * BLK + (st % SPB) * kStageKeys;
+    const int rows_left = kv_len - j0;  // >= 1
+    const int krec = (rows_left - 1) * static_cast<int>(kstride) + RB;
+    const int vrec = (rows_left - 1) * static_cast<int>(vstride) + RB;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(kbase + j0 * kstride), 0,
+        rows_left >= kStageKeys ? 0x7fffffff : krec, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(vbase + j0 * vstride), 0,
+        rows_left >= kStageKeys ? 0x7fffffff : vrec, kBufferFlags);
 #pragma unroll
-      for (int rd = 0; rd < ROUNDS; ++rd) {
-        const int seg = (rd * NW + wave) * 1024;
-        __builtin_amdgcn_global_load_lds((gbl_void*)(kb + dma_k[rd]), (lds_void*)(sK + seg), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_void*)(vb + dma_v[rd]), (lds_void*)(sV + seg), 16, 0, 0);
-      }
-    } else {
-      // sequence tail: rows past the end repeat the last row (masked later)
-#pragma unroll
-      for (int rd = 0; rd < ROUNDS; ++rd) {
-        const int seg = (rd * NW + wave) * 1024;
-        const int r = max(min(dma_row[rd], kv_len - 1 - j0), 0);
-        __builtin_amdgcn_global_load_lds((gbl_void*)(kb + r * kstride + dma_col[rd]),
-                                         (lds_void*)(sK + seg), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gbl_void*)(vb + r * vstride + dma_col[rd]),
-                                         (lds_void*)(sV + seg), 16, 0, 0);
-      }
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+      const int seg = (rd * NW + wave) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(sK + seg), 16,
+                                               static_cast<int>(dma_k[rd]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(sV + seg), 16,
+                                               static_cast<int>(dma_v[rd]), 0, 0, 0);
     }
     if (doc_mask && masked_at(it, n) && wave == 0) {
       const int j = min(j0 + lane, kv_len - 1);

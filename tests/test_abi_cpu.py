@@ -46,6 +46,17 @@ def test_library_exports_every_declared_symbol():
     assert L.fa_abi_version() == C.ABI_VERSION
 
 
+@needs_lib
+def test_every_kernel_launch_stub_is_defined():
+    # a kernel whose host-side stub was not emitted leaves an undefined
+    # symbol that only fails when the library is loaded for a launch
+    out = subprocess.run(["nm", "-D", C.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    missing = [l for l in out.splitlines()
+               if " U " in l and "__device_stub" in l]
+    assert not missing, missing
+
+
 def test_struct_layout_matches_c(tmp_path):
     src = tmp_path / "layout.c"
     src.write_text(f"""
