@@ -152,8 +152,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
   const int nkvb = p.nkvb;
   const int nf = p.fnum ? min(max(p.fnum[lrow], 0), nkvb) : 0;
   const int np = min(max(p.num[lrow], 0), nkvb);
-  const int32_t* fl = p.fidx ? p.fidx + lrow * nkvb : nullptr;
-  const int32_t* pl = p.idx + lrow * nkvb;
+  // block lists through the constant address space: uniform scalar loads,
+  // tracked by lgkmcnt, so reading them never waits on in-flight tile DMA
+  const const_i32* fl = (const const_i32*)(p.fidx ? p.fidx + lrow * nkvb : p.idx);
+  const const_i32* pl = (const const_i32*)(p.idx + lrow * nkvb);
   const int nblocks = nf + np;
   const int nstages = nblocks * SPB;
 
