@@ -9,16 +9,20 @@
 // can issue: the two are independent and drift apart.
 //
 // Block order. A row's live key blocks are visited partial list first, then
-// the full list from the last block to the first. Under causal-style masks
-// this visits the keys nearest the query first; with a distance penalty
-// (ALiBi) the running maximum is then found early and later blocks rarely
-// raise it, so the output accumulator is rarely rescaled.
+// the full list, each from the last block to the first, and the stages of a
+// block from its last keys to its first. Under causal-style masks (the
+// diagonal block is the last partial one) this visits the keys nearest the
+// query first; with a distance penalty (ALiBi) the running maximum is then
+// found early and later stages rarely raise it, so the output accumulator is
+// rarely rescaled.
 //
 // Data movement. For each stage the K and V tiles [64 keys][D] go HBM -> LDS
-// with global_load_lds_dwordx4 (no register staging), double-buffered so the
-// next stage is in flight while this one is computed. In LDS a tile is
-// row-major with its 16-byte chunks XOR-swizzled per row; the swizzle makes
-// both read patterns conflict-free on the 64 LDS banks:
+// with buffer loads that write LDS directly (no register staging; issued as
+// inline asm, see fwd_asm.hpp), double-buffered so the next stage is in
+// flight while this one is computed. Each tile is read through a buffer
+// descriptor that ends at the sequence end, so rows past it arrive as zeros.
+// In LDS a tile is row-major with its 16-byte chunks XOR-swizzled per row;
+// the swizzle makes both read patterns conflict-free on the 64 LDS banks:
 //   * S^T = K Q^T takes K as the MFMA A operand: ds_read_b128, 16 rows x one
 //     chunk per 16 lanes;
 //   * O^T += V^T P^T needs V with keys along each lane's k slots:
@@ -41,6 +45,7 @@
 // ones), i.e. exactly the weights the PV product uses.
 #pragma once
 
+#include "fwd_asm.hpp"
 #include "fwd_common.hpp"
 
 namespace fa {
@@ -48,12 +53,8 @@ namespace fa {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void gbl_void;
 
 constexpr float kRescaleSlack = 8.0f;
-// Buffer resource word 3 for raw (unformatted, unswizzled) dword access.
-constexpr int kBufferFlags = 0x00020000;
 constexpr int kStageKeys = 64;
 
 template <int D>
@@ -189,8 +190,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
     dma_v[rd] = static_cast<uint32_t>(r * vstride) + col;
   }
 
-  // visiting order: partial blocks ascending, then full blocks descending
-  auto block_at = [&](int it) -> int { return it < np ? pl[it] : fl[nf - 1 - (it - np)]; };
+  // visiting order: partial blocks, then full blocks, each list from the
+  // last block to the first; inside a block the later 64 keys come first
+  auto block_at = [&](int it) -> int {
+    return it < np ? pl[np - 1 - it] : fl[nf - 1 - (it - np)];
+  };
   auto masked_at = [&](int it, int n) -> bool {
     return it < np || (n + 1) * BLK > kv_len;
   };
@@ -203,27 +207,21 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
     const int it = st / SPB;
     const int n = block_at(it);
     if (static_cast<unsigned>(n) >= static_cast<unsigned>(nkvb)) return;
-    const int j0 = n * BLK + (st % SPB) * kStageKeys;
+    const int j0 = n * BLK + (SPB - 1 - st % SPB) * kStageKeys;
     const int rows_left = kv_len - j0;  // >= 1
     const int krec = (rows_left - 1) * static_cast<int>(kstride) + RB;
     const int vrec = (rows_left - 1) * static_cast<int>(vstride) + RB;
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(kbase + j0 * kstride), 0,
-        rows_left >= kStageKeys ? 0x7fffffff : krec, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(vbase + j0 * vstride), 0,
-        rows_left >= kStageKeys ? 0x7fffffff : vrec, kBufferFlags);
+    const hw::i32x4 kr = hw::make_rsrc(kbase + j0 * kstride, rows_left >= kStageKeys ? 0x7fffffff : krec);
+    const hw::i32x4 vr = hw::make_rsrc(vbase + j0 * vstride, rows_left >= kStageKeys ? 0x7fffffff : vrec);
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
       const int seg = (rd * NW + wave) * 1024;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void*)(sK + seg), 16,
-                                               static_cast<int>(dma_k[rd]), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void*)(sV + seg), 16,
-                                               static_cast<int>(dma_v[rd]), 0, 0, 0);
+      hw::dma_tile16(kr, hw::lds_addr(sK + seg), dma_k[rd], 0);
+      hw::dma_tile16(vr, hw::lds_addr(sV + seg), dma_v[rd], 0);
     }
     if (doc_mask && masked_at(it, n) && wave == 0) {
       const int j = min(j0 + lane, kv_len - 1);
-      __builtin_amdgcn_global_load_lds((gbl_void*)(doc + j), (lds_void*)sD, 4, 0, 0);
+      hw::dma_dword(doc, hw::lds_addr(sD), static_cast<uint32_t>(j * 4));
     }
   };
 
@@ -239,7 +237,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
     const int n = block_at(it);
     if (static_cast<unsigned>(n) >= static_cast<unsigned>(nkvb)) return;
     const bool masked = masked_at(it, n);
-    const int j0 = n * BLK + (st % SPB) * kStageKeys;
+    const int j0 = n * BLK + (SPB - 1 - st % SPB) * kStageKeys;
 
     // ---- S^T = K Q^T for the stage's 64 keys
     f32x16 s[2];
@@ -365,6 +363,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
 
   // ---- main loop over stages, unrolled by two so each LDS buffer is its
   // own object; the DMA of stage st + 1 overlaps the compute of stage st.
+  // The setup loads (Q, document id) complete before the first tile DMA, so
+  // the per-stage waits below only ever wait for tiles.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   if (nstages > 0) issue(0, sK0, sV0, sDoc0);
   for (int st = 0; st < nstages; st += 2) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's DMA landed
