@@ -161,6 +161,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
   const int nstages = nblocks * SPB;
 
   const ScoreConsts sc = make_score_consts(p, w.h);
+  // mask_mod as an interval of key indices per row: j in [lo_abs, lo_abs + span)
+  const int hi_abs = mkind == FA_MASK_NONE ? kv_len : min(i + 1, kv_len);
+  const int lo_abs = mkind == FA_MASK_SLIDING_WINDOW ? i - window + 1 : 0;
+  const unsigned span = static_cast<unsigned>(max(hi_abs - lo_abs, 0));
 
   // ---- per-lane byte offsets, fixed for the whole row
   int k_rd[DK];  // K operand: row lq (+32 jt), chunk 2dk + g
@@ -277,31 +281,36 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
         }
     }
 
-    // ---- mask_mod on partial and sequence-tail blocks only
+    // ---- mask_mod on partial and sequence-tail blocks only. Every built-in
+    // mask bounds a row's keys to an interval (causal: j <= i, sliding
+    // window: i - W < j <= i, and j < kv_len), so the test is one unsigned
+    // compare of the key's offset in the interval against its length, plus
+    // the document-id equality for document masks.
     if (masked) {
-      const int jb = j0 + 4 * g;
-#define FA_MASK_STAGE(KIND)                                                    \
-  _Pragma("unroll") for (int jt = 0; jt < 2; ++jt)                             \
-  _Pragma("unroll") for (int r4 = 0; r4 < 4; ++r4) {                           \
-    const int jl = 32 * jt + 8 * r4;                                           \
-    int dj[4] = {0, 0, 0, 0};                                                  \
-    if (KIND == FA_MASK_DOCUMENT) {                                            \
-      const int4 t = *reinterpret_cast<const int4*>(sD + 4 * g + jl);          \
-      dj[0] = t.x; dj[1] = t.y; dj[2] = t.z; dj[3] = t.w;                      \
-    }                                                                          \
-    _Pragma("unroll") for (int c = 0; c < 4; ++c) {                            \
-      const int j = jb + jl + c;                                               \
-      const bool ok = (j < kv_len) & mask_ok<KIND>(i, j, window, di, dj[c]);   \
-      s[jt][4 * r4 + c] = ok ? s[jt][4 * r4 + c] : FA_NEG_INF;                 \
-    }                                                                          \
-  }
-      switch (mkind) {
-        case FA_MASK_CAUSAL: FA_MASK_STAGE(FA_MASK_CAUSAL) break;
-        case FA_MASK_SLIDING_WINDOW: FA_MASK_STAGE(FA_MASK_SLIDING_WINDOW) break;
-        case FA_MASK_DOCUMENT: FA_MASK_STAGE(FA_MASK_DOCUMENT) break;
-        default: FA_MASK_STAGE(FA_MASK_NONE) break;
+      const int lo = lo_abs - (j0 + 4 * g);  // interval start, lane-relative
+      if (doc_mask) {
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int jl = 32 * jt + 8 * r4;
+            const int4 t = *reinterpret_cast<const int4*>(sD + 4 * g + jl);
+            const int dj[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const bool ok = (static_cast<unsigned>(jl + c - lo) < span) & (dj[c] == di);
+              s[jt][4 * r4 + c] = ok ? s[jt][4 * r4 + c] : FA_NEG_INF;
+            }
+          }
+      } else {
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int jl = 32 * jt + 8 * (r >> 2) + (r & 3);
+            s[jt][r] = static_cast<unsigned>(jl - lo) < span ? s[jt][r] : FA_NEG_INF;
+          }
       }
-#undef FA_MASK_STAGE
     }
 
     // ---- online softmax
