@@ -33,7 +33,7 @@ import workloads as WL  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (published)
 FWD_KERNEL = "fwd_bf16_kernel"
-KERNEL_SOURCES = ["fwd_common.hpp", "fwd_bf16.hpp", "fwd_bf16_d64.hip",
+KERNEL_SOURCES = ["fwd_common.hpp", "fwd_asm.hpp", "fwd_bf16.hpp", "fwd_bf16_d64.hip",
                   "fwd_bf16_d128.hip", "fwd_fp32.hpp", "fwd_fp32.hip"]
 
 
