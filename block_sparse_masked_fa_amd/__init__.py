@@ -7,8 +7,10 @@ does not load the library; the first call does, and fails loudly if the
 library has not been built (``python -m block_sparse_masked_fa_amd.build``).
 """
 from .api import (  # noqa: F401
-    BlockMask, FlexAttnError, MaskMod, ScoreMod, alibi, causal,
-    create_block_mask, document, fa_block_mask_dims, fa_create_block_mask,
-    fa_flex_attention_fwd, flex_attention, no_mask, sliding_window, softcap,
+    BlockMask, FlexAttnError, MaskMod, ScoreMod, alibi, auto_num_splits,
+    causal, create_block_mask, document, fa_block_mask_dims,
+    fa_create_block_mask, fa_flex_attention_fwd, fa_flex_attention_fwd_split,
+    fa_split_workspace_bytes, flex_attention, no_mask, sliding_window,
+    softcap,
 )
 from ._capi import LIB_PATH, lib  # noqa: F401

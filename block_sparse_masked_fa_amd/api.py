@@ -5,8 +5,9 @@ device buffers and the current HIP stream, every computation runs in the HIP
 kernels. Two layers:
 
 * the raw entry points with the C names (``fa_block_mask_dims``,
-  ``fa_create_block_mask``, ``fa_flex_attention_fwd``), taking ctypes structs
-  and integer device addresses;
+  ``fa_create_block_mask``, ``fa_flex_attention_fwd``,
+  ``fa_flex_attention_fwd_split``, ``fa_split_workspace_bytes``), taking
+  ctypes structs and integer device addresses;
 * a FlexAttention-style convenience layer: ``create_block_mask(...)`` returns
   a :class:`BlockMask` holding its index tensors, and
   ``flex_attention(q, k, v, block_mask, score_mod)`` returns ``(O, LSE)``.
@@ -27,7 +28,8 @@ __all__ = [
     "MaskMod", "ScoreMod", "causal", "sliding_window", "document",
     "no_mask", "softcap", "alibi", "BlockMask", "create_block_mask",
     "flex_attention", "fa_block_mask_dims", "fa_create_block_mask",
-    "fa_flex_attention_fwd", "FlexAttnError",
+    "fa_flex_attention_fwd", "fa_flex_attention_fwd_split",
+    "fa_split_workspace_bytes", "auto_num_splits", "FlexAttnError",
 ]
 
 FlexAttnError = C.FlexAttnError
@@ -144,6 +146,43 @@ def fa_flex_attention_fwd(dtype: int, B: int, H: int, H_kv: int, q_len: int,
         q, C.Stride3(*q_stride), k, C.Stride3(*k_stride),
         v, C.Stride3(*v_stride), scale, ctypes.byref(bm),
         ctypes.byref(score) if score is not None else None, o, lse, stream)
+
+
+def fa_flex_attention_fwd_split(dtype: int, B: int, H: int, H_kv: int,
+                                q_len: int, kv_len: int, D: int, q: int,
+                                q_stride, k: int, k_stride, v: int, v_stride,
+                                scale: float, bm: C.fa_block_mask,
+                                score: Optional[C.fa_score_mod],
+                                num_splits: int, workspace: Optional[int],
+                                workspace_bytes: int, o: int,
+                                lse: Optional[int],
+                                stream: Optional[int]) -> int:
+    return C.lib().fa_flex_attention_fwd_split(
+        dtype, B, H, H_kv, q_len, kv_len, D,
+        q, C.Stride3(*q_stride), k, C.Stride3(*k_stride),
+        v, C.Stride3(*v_stride), scale, ctypes.byref(bm),
+        ctypes.byref(score) if score is not None else None, num_splits,
+        workspace, workspace_bytes, o, lse, stream)
+
+
+def fa_split_workspace_bytes(B: int, H: int, q_len: int, D: int,
+                             num_splits: int) -> int:
+    n = ctypes.c_uint64()
+    C.check(C.lib().fa_split_workspace_bytes(B, H, q_len, D, num_splits,
+                                             ctypes.byref(n)),
+            "fa_split_workspace_bytes")
+    return n.value
+
+
+def auto_num_splits(dtype: torch.dtype, B: int, H: int, num_q_blocks: int,
+                    num_cus: int) -> int:
+    """Split-KV parts per query block so that the forward launches about two
+    workgroups per compute unit: 1 (no split) when B * H * NQB already gives
+    at least one per unit or the dtype is not bf16."""
+    wgs = B * H * num_q_blocks
+    if dtype != torch.bfloat16 or wgs == 0 or wgs >= num_cus:
+        return 1
+    return max(1, min(C.FA_MAX_SPLITS, -(-2 * num_cus // wgs)))
 
 
 # ------------------------------------------------------------- BlockMask
@@ -266,14 +305,20 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    block_mask: BlockMask, score_mod=None,
                    scale: Optional[float] = None, return_lse: bool = True,
                    out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None):
-    """Fused block-sparse attention forward (one fa_flex_attention_fwd call).
+                   lse: Optional[torch.Tensor] = None,
+                   num_splits: Optional[int] = None):
+    """Fused block-sparse attention forward.
 
     q: (B, H, Q_LEN, D); k, v: (B, H_kv, KV_LEN, D), bf16 or fp32, on the
     same HIP device, last dimension contiguous. ``score_mod``: None,
     "alibi", ("softcap", cap) or a :class:`ScoreMod`. ``scale`` defaults to
     1/sqrt(D). Returns ``(O, LSE)`` (``LSE`` fp32 (B, H, Q_LEN), natural
-    log; ``None`` when ``return_lse`` is False)."""
+    log; ``None`` when ``return_lse`` is False).
+
+    ``num_splits``: split-KV parts per query block (bf16 only). None picks
+    :func:`auto_num_splits` for the device; 1 is one fa_flex_attention_fwd
+    call, more is fa_flex_attention_fwd_split with a workspace allocated
+    here."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, H, S, D)")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
@@ -298,13 +343,29 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         lse = torch.empty((B, H, q_len), dtype=torch.float32, device=q.device)
     if not return_lse:
         lse = None
+    if num_splits is None:
+        num_splits = auto_num_splits(
+            q.dtype, B, H, block_mask.num_q_blocks,
+            torch.cuda.get_device_properties(q.device).multi_processor_count)
     with torch.cuda.device(q.device):
-        st = fa_flex_attention_fwd(
+        if num_splits == 1:
+            st = fa_flex_attention_fwd(
+                _DTYPES[q.dtype], B, H, H_kv, q_len, kv_len, D,
+                q.data_ptr(), q.stride()[:3], k.data_ptr(), k.stride()[:3],
+                v.data_ptr(), v.stride()[:3], float(scale),
+                block_mask.to_c(), score.to_c(), out.data_ptr(),
+                lse.data_ptr() if lse is not None else None,
+                _stream_handle(q.device))
+            C.check(st, "fa_flex_attention_fwd")
+            return out, lse
+        nbytes = fa_split_workspace_bytes(B, H, q_len, D, num_splits)
+        ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+        st = fa_flex_attention_fwd_split(
             _DTYPES[q.dtype], B, H, H_kv, q_len, kv_len, D,
             q.data_ptr(), q.stride()[:3], k.data_ptr(), k.stride()[:3],
             v.data_ptr(), v.stride()[:3], float(scale), block_mask.to_c(),
-            score.to_c(), out.data_ptr(),
+            score.to_c(), num_splits, ws.data_ptr(), nbytes, out.data_ptr(),
             lse.data_ptr() if lse is not None else None,
             _stream_handle(q.device))
-    C.check(st, "fa_flex_attention_fwd")
+    C.check(st, "fa_flex_attention_fwd_split")
     return out, lse

@@ -28,6 +28,7 @@ SOURCES = [
     "fwd_bf16_d64.hip",
     "fwd_bf16_d128.hip",
     "fwd_fp32.hip",
+    "fwd_combine.hip",
 ]
 
 ARCH = "gfx950"

@@ -96,4 +96,44 @@ fa_status fa_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H,
   return hip_status(err, "attention kernel launch");
 }
 
+fa_status fa_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
+                                   int32_t D, int32_t num_splits,
+                                   uint64_t* bytes) {
+  std::string msg;
+  return finish(fa::check_split_workspace_bytes(B, H, q_len, D, num_splits,
+                                                bytes, &msg),
+                msg);
+}
+
+fa_status fa_flex_attention_fwd_split(
+    int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t q_len,
+    int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
+    const void* k, const int64_t k_stride[3], const void* v,
+    const int64_t v_stride[3], float scale, const fa_block_mask* bm,
+    const fa_score_mod* score, int32_t num_splits, void* workspace,
+    uint64_t workspace_bytes, void* o, float* lse, void* stream) {
+  std::string msg;
+  fa::FwdLaunch p{};
+  bool nothing = false;
+  int st = fa::check_flex_attention_fwd(dtype, B, H, H_kv, q_len, kv_len, D, q,
+                                        q_stride, k, k_stride, v, v_stride,
+                                        scale, bm, score, o, lse, &p, &nothing,
+                                        &msg);
+  if (st != FA_OK) return finish(st, msg);
+  fa::CombineLaunch cl{};
+  st = fa::check_split(dtype, num_splits, workspace, workspace_bytes, &p, &cl,
+                       &msg);
+  if (st != FA_OK) return finish(st, msg);
+  if (nothing) return FA_OK;
+  int err;
+  if (dtype == FA_FP32)
+    err = fa::launch_fwd_fp32(p, stream);
+  else if (D == 64)
+    err = fa::launch_fwd_bf16_d64(p, stream);
+  else
+    err = fa::launch_fwd_bf16_d128(p, stream);
+  if (err != 0 || p.nsplit == 1) return hip_status(err, "attention kernel launch");
+  return hip_status(fa::launch_split_combine(cl, stream), "split-KV merge launch");
+}
+
 }  // extern "C"

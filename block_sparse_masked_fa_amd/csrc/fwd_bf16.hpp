@@ -70,18 +70,21 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
 }
 
-// Workgroup -> (head, query block). Workgroups are dispatched round-robin over
-// the 8 XCDs (wg % 8). Logical items are dealt to XCDs in contiguous ranges so
-// that the query blocks of one head run on one XCD and share its L2; within a
-// head the heaviest query blocks (last rows under causal masks) come first.
+// Workgroup -> (head, query block, split part). Workgroups are dispatched
+// round-robin over the 8 XCDs (wg % 8). Logical items are dealt to XCDs in
+// contiguous ranges so that the query blocks of one head run on one XCD and
+// share its L2; within a head the heaviest query blocks (last rows under
+// causal masks) come first.
 __device__ __forceinline__ bool xcd_work_item(const FwdLaunch& p, WorkItem& w) {
-  const int total = p.B * p.H * p.nqb;
+  const int total = p.B * p.H * p.nqb * p.nsplit;
   const int per_xcd = (total + 7) >> 3;
   const int wg = blockIdx.x;
   const int logical = (wg & 7) * per_xcd + (wg >> 3);
   if (logical >= total) return false;
-  w.m = p.nqb - 1 - (logical % p.nqb);
-  const int bh = logical / p.nqb;
+  w.c = logical % p.nsplit;  // the parts of one query block run side by side
+  const int row = logical / p.nsplit;
+  w.m = p.nqb - 1 - (row % p.nqb);
+  const int bh = row / p.nqb;
   w.h = bh % p.H;
   w.b = bh / p.H;
   return true;
@@ -158,7 +161,11 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
   const const_i32* fl = (const const_i32*)(p.fidx ? p.fidx + lrow * nkvb : p.idx);
   const const_i32* pl = (const const_i32*)(p.idx + lrow * nkvb);
   const int nblocks = nf + np;
-  const int nstages = nblocks * SPB;
+  // split-KV part w.c of nsplit: visits [v0, v0 + nvis) of the row's order
+  const int per_part = (nblocks + p.nsplit - 1) / p.nsplit;
+  const int v0 = min(w.c * per_part, nblocks);
+  const int nvis = min(per_part, nblocks - v0);
+  const int nstages = nvis * SPB;
 
   const ScoreConsts sc = make_score_consts(p, w.h);
   // mask_mod as an interval of key indices per row: j in [lo_abs, lo_abs + span)
@@ -196,11 +203,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
 
   // visiting order: partial blocks, then full blocks, each list from the
   // last block to the first; inside a block the later 64 keys come first
+  // (`it` counts the visits of this workgroup's part)
   auto block_at = [&](int it) -> int {
-    return it < np ? pl[np - 1 - it] : fl[nf - 1 - (it - np)];
+    const int v = v0 + it;
+    return v < np ? pl[np - 1 - v] : fl[nf - 1 - (v - np)];
   };
   auto masked_at = [&](int it, int n) -> bool {
-    return it < np || (n + 1) * BLK > kv_len;
+    return v0 + it < np || (n + 1) * BLK > kv_len;
   };
 
   // Issue the DMA of stage `st` (block visit st / SPB) into one buffer. Each
@@ -390,6 +399,27 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (p.nsplit > 1) {
+    // split-KV part: the unnormalised accumulator and (m, l) for the merge
+    if (i_ok) {
+      const int64_t prow =
+          (static_cast<int64_t>(w.c) * p.B * p.H + static_cast<int64_t>(w.b) * p.H + w.h) *
+              p.q_len + i;
+      float* po = p.part_o + prow * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4*>(po + dt * 32 + 8 * q4 + 4 * g) =
+              f32x4{oacc[dt][4 * q4 + 0], oacc[dt][4 * q4 + 1], oacc[dt][4 * q4 + 2],
+                    oacc[dt][4 * q4 + 3]};
+      if (g == 0) {
+        p.part_ml[2 * prow] = m_run;
+        p.part_ml[2 * prow + 1] = l_tot;
+      }
+    }
+    return;
+  }
   if (i_ok) {
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const int64_t orow = (static_cast<int64_t>(w.b) * p.H + w.h) * p.q_len + i;

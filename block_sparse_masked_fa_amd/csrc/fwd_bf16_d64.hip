@@ -5,7 +5,7 @@ namespace fa {
 
 int launch_fwd_bf16_d64(const FwdLaunch& p, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int items = p.B * p.H * p.nqb;
+  const int items = p.B * p.H * p.nqb * p.nsplit;
   const dim3 grid(static_cast<unsigned>((items + 7) / 8 * 8));  // whole XCD rounds
   const int key = p.block * 4 + p.score_kind;
   switch (key) {

@@ -95,6 +95,7 @@ __device__ __forceinline__ bool mask_ok(int i, int j, int window, int di,
 // (heaviest under causal masks) to the first.
 struct WorkItem {
   int b, h, m;
+  int c = 0;  // split-KV part
 };
 
 __device__ __forceinline__ WorkItem work_item(const FwdLaunch& p) {

@@ -46,6 +46,25 @@ struct FwdLaunch {
   float softcap;
   void* o;
   float* lse;           // may be NULL
+  // split-KV: each query block's visit list is cut into nsplit consecutive
+  // parts, one workgroup each (nsplit = 1: no split, o / lse written
+  // directly). With nsplit > 1 the forward writes unnormalised partial
+  // results (part_o [nsplit][B*H*q_len][D] fp32, part_ml [nsplit][B*H*q_len]
+  // {row max in log2 units, row sum}) and a second kernel merges them.
+  int32_t nsplit;
+  float* part_o;
+  float* part_ml;
+};
+
+// Split-KV merge of the partial results described at FwdLaunch.
+struct CombineLaunch {
+  int32_t nsplit;
+  int64_t rows;  // B * H * q_len
+  int32_t D;
+  const float* part_o;
+  const float* part_ml;
+  void* o;       // bf16 [rows][D]
+  float* lse;    // may be NULL
 };
 
 // Kernel launchers: return a hipError_t value (0 = success).
@@ -53,5 +72,6 @@ int launch_block_mask(const BlockMaskLaunch& p, void* stream);
 int launch_fwd_bf16_d64(const FwdLaunch& p, void* stream);
 int launch_fwd_bf16_d128(const FwdLaunch& p, void* stream);
 int launch_fwd_fp32(const FwdLaunch& p, void* stream);
+int launch_split_combine(const CombineLaunch& p, void* stream);
 
 }  // namespace fa

@@ -261,6 +261,62 @@ int check_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H, int32_t H_kv,
   out->softcap = cap;
   out->o = o;
   out->lse = lse;
+  out->nsplit = 1;
+  out->part_o = nullptr;
+  out->part_ml = nullptr;
+  return FA_OK;
+}
+
+int check_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len, int32_t D,
+                                int32_t num_splits, uint64_t* bytes,
+                                std::string* msg) {
+  if (!bytes) return fail(msg, FA_ERR_NULL_POINTER, "bytes is NULL");
+  if (B < 0 || H < 0 || q_len < 0 || D < 0)
+    return fail(msg, FA_ERR_INVALID_VALUE, "negative size");
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(msg, FA_ERR_INVALID_VALUE,
+                "num_splits must be in [1, " + std::to_string(kMaxSplits) + "]");
+  if (num_splits == 1) {
+    *bytes = 0;
+    return FA_OK;
+  }
+  *bytes = static_cast<uint64_t>(num_splits) * static_cast<uint64_t>(B) *
+           static_cast<uint64_t>(H) * static_cast<uint64_t>(q_len) *
+           static_cast<uint64_t>(D + 2) * 4u;
+  return FA_OK;
+}
+
+int check_split(int32_t dtype, int32_t num_splits, void* workspace,
+                uint64_t workspace_bytes, FwdLaunch* p, CombineLaunch* cl,
+                std::string* msg) {
+  uint64_t need = 0;
+  int st = check_split_workspace_bytes(p->B, p->H, p->q_len, p->D, num_splits,
+                                       &need, msg);
+  if (st != FA_OK) return st;
+  if (num_splits == 1) return FA_OK;
+  if (dtype != FA_BF16)
+    return fail(msg, FA_ERR_UNSUPPORTED, "split-KV is built for bf16 only");
+  if (!workspace) return fail(msg, FA_ERR_NULL_POINTER, "workspace is NULL");
+  if (!aligned16(workspace))
+    return fail(msg, FA_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(msg, FA_ERR_INVALID_VALUE,
+                "workspace has " + std::to_string(workspace_bytes) +
+                    " bytes, needs " + std::to_string(need));
+  const int64_t rows = static_cast<int64_t>(p->B) * p->H * p->q_len;
+  if (static_cast<int64_t>(p->B) * p->H * p->nqb * num_splits > INT32_MAX)
+    return fail(msg, FA_ERR_UNSUPPORTED, "too many split-KV workgroups");
+  float* ws = static_cast<float*>(workspace);
+  p->nsplit = num_splits;
+  p->part_o = ws;
+  p->part_ml = ws + static_cast<int64_t>(num_splits) * rows * p->D;
+  cl->nsplit = num_splits;
+  cl->rows = rows;
+  cl->D = p->D;
+  cl->part_o = p->part_o;
+  cl->part_ml = p->part_ml;
+  cl->o = p->o;
+  cl->lse = p->lse;
   return FA_OK;
 }
 

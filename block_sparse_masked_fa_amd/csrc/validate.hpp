@@ -38,4 +38,17 @@ int check_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H, int32_t H_kv,
                              FwdLaunch* out, bool* nothing_to_do,
                              std::string* msg);
 
+// Largest number of split-KV parts per query block.
+constexpr int kMaxSplits = 64;
+
+int check_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len, int32_t D,
+                                int32_t num_splits, uint64_t* bytes,
+                                std::string* msg);
+
+// Checks the split-KV arguments on top of a filled forward descriptor and
+// sets its split fields (and *cl for the merge kernel).
+int check_split(int32_t dtype, int32_t num_splits, void* workspace,
+                uint64_t workspace_bytes, FwdLaunch* p, CombineLaunch* cl,
+                std::string* msg);
+
 }  // namespace fa

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -199,6 +199,44 @@ fa_status fa_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H,
                                 const fa_block_mask* bm,
                                 const fa_score_mod* score, void* o, float* lse,
                                 void* stream);
+
+/* Split-KV forward: the same operation as fa_flex_attention_fwd (same
+ * arguments, results within rounding), executed with each query block's
+ * list of live key blocks cut into num_splits consecutive parts that run as
+ * separate workgroups. Each part keeps its own online softmax over its keys
+ * and writes, per query row, the unnormalised output sum, the row maximum
+ * and the row sum into `workspace`; a second kernel then merges the parts
+ * exactly (the softmax over a union of disjoint key sets: rescale each part
+ * by exp(m_part - m) and renormalise). This fills the GPU when B * H * NQB
+ * is small against its 256 compute units, at the price of the partial
+ * results' round trip through memory.
+ *
+ *   num_splits       1 ... 64. 1 is fa_flex_attention_fwd (workspace may be
+ *                    NULL). A part whose share of a row is empty writes a
+ *                    neutral partial result.
+ *   dtype            FA_BF16 when num_splits > 1 (else FA_ERR_UNSUPPORTED).
+ *   workspace        device memory owned by the caller, 16-byte aligned, at
+ *                    least fa_split_workspace_bytes(...) bytes; overwritten.
+ *                    Calls in flight at the same time need separate
+ *                    workspaces.
+ *   workspace_bytes  its size; FA_ERR_INVALID_VALUE if too small.
+ * Every other argument is as for fa_flex_attention_fwd. Two kernel
+ * launches (num_splits > 1); asynchronous. */
+fa_status fa_flex_attention_fwd_split(
+    int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t q_len,
+    int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
+    const void* k, const int64_t k_stride[3], const void* v,
+    const int64_t v_stride[3], float scale, const fa_block_mask* bm,
+    const fa_score_mod* score, int32_t num_splits, void* workspace,
+    uint64_t workspace_bytes, void* o, float* lse, void* stream);
+
+/* Workspace size of fa_flex_attention_fwd_split: num_splits * B * H * q_len
+ * * (D + 2) * 4 bytes (fp32 partial outputs, then per-row maximum and
+ * sum); 0 when num_splits == 1. Host only; nothing is launched.
+ * FA_ERR_INVALID_VALUE for negative sizes or num_splits outside 1 ... 64. */
+fa_status fa_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
+                                   int32_t D, int32_t num_splits,
+                                   uint64_t* bytes);
 
 /* Static description of a status code. */
 const char* fa_status_string(int32_t status);

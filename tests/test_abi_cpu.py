@@ -252,3 +252,74 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(C, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         C.lib()
+
+
+@needs_lib
+def test_split_workspace_bytes():
+    # num_splits * B * H * q_len * (D + 2) * 4: fp32 partial outputs, then the
+    # per-row maximum and sum
+    assert api.fa_split_workspace_bytes(1, 1, 8192, 64, 8) == 8 * 8192 * 66 * 4
+    assert api.fa_split_workspace_bytes(2, 3, 100, 128, 5) == 5 * 6 * 100 * 130 * 4
+    assert api.fa_split_workspace_bytes(2, 3, 100, 128, 1) == 0
+    assert api.fa_split_workspace_bytes(0, 3, 100, 128, 4) == 0
+    for bad in (dict(num_splits=0), dict(num_splits=C.FA_MAX_SPLITS + 1),
+                dict(B=-1), dict(q_len=-5)):
+        a = dict(B=1, H=1, q_len=64, D=64, num_splits=2)
+        a.update(bad)
+        with pytest.raises(C.FlexAttnError) as e:
+            api.fa_split_workspace_bytes(**a)
+        assert e.value.status == C.FA_ERR_INVALID_VALUE, bad
+    assert C.lib().fa_split_workspace_bytes(1, 1, 64, 64, 2, None) == \
+        C.FA_ERR_NULL_POINTER
+
+
+def _fwd_split(**over):
+    a = dict(dtype=C.FA_BF16, B=2, H=4, H_kv=4, q_len=256, kv_len=256, D=128,
+             q=FAKE, q_stride=(4 * 256 * 128, 256 * 128, 128), k=FAKE,
+             k_stride=(4 * 256 * 128, 256 * 128, 128), v=FAKE,
+             v_stride=(4 * 256 * 128, 256 * 128, 128), scale=0.088,
+             bm=_good_bm(), score=C.fa_score_mod(kind=C.FA_SCORE_NONE),
+             num_splits=4, workspace=FAKE,
+             workspace_bytes=4 * 8 * 256 * 130 * 4, o=FAKE, lse=FAKE,
+             stream=None)
+    a.update(over)
+    return api.fa_flex_attention_fwd_split(**a)
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status", [
+    (dict(num_splits=0), C.FA_ERR_INVALID_VALUE),
+    (dict(num_splits=C.FA_MAX_SPLITS + 1), C.FA_ERR_INVALID_VALUE),
+    (dict(workspace_bytes=4 * 8 * 256 * 130 * 4 - 1), C.FA_ERR_INVALID_VALUE),
+    (dict(workspace=None), C.FA_ERR_NULL_POINTER),
+    (dict(workspace=FAKE + 4), C.FA_ERR_UNSUPPORTED),
+    (dict(dtype=C.FA_FP32, D=64, q_stride=(4 * 256 * 64, 256 * 64, 64),
+          k_stride=(4 * 256 * 64, 256 * 64, 64),
+          v_stride=(4 * 256 * 64, 256 * 64, 64)), C.FA_ERR_UNSUPPORTED),
+    # the forward's own checks come first
+    (dict(D=96), C.FA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), C.FA_ERR_INVALID_VALUE),
+    (dict(bm=_good_bm(B=3)), C.FA_ERR_SHAPE_MISMATCH),
+    (dict(q=None), C.FA_ERR_NULL_POINTER),
+])
+def test_fwd_split_refuses(over, status):
+    st = _fwd_split(**over)
+    assert st == status, C.lib().fa_last_error()
+
+
+@needs_lib
+def test_fwd_split_empty_problem_is_a_noop():
+    assert _fwd_split(B=0, q=None, k=None, v=None, o=None,
+                      workspace_bytes=0, workspace=FAKE) == C.FA_OK
+
+
+def test_auto_num_splits():
+    import torch
+    # two workgroups per compute unit when the grid is short of one per unit
+    assert api.auto_num_splits(torch.bfloat16, 1, 1, 64, 256) == 8
+    assert api.auto_num_splits(torch.bfloat16, 1, 1, 3, 256) == \
+        min(C.FA_MAX_SPLITS, -(-512 // 3))
+    assert api.auto_num_splits(torch.bfloat16, 4, 16, 64, 256) == 1
+    assert api.auto_num_splits(torch.bfloat16, 1, 1, 256, 256) == 1
+    assert api.auto_num_splits(torch.float32, 1, 1, 4, 256) == 1
+    assert api.auto_num_splits(torch.bfloat16, 0, 1, 4, 256) == 1

@@ -28,7 +28,7 @@ def _score_arg(score, cap):
 
 
 def run_gpu(w: WL.Workload, q, k, v, doc=None, sep=True, score=None,
-            cap=None, bm=None):
+            cap=None, bm=None, num_splits=1):
     score = w.score if score is None else score
     cap = w.softcap if cap is None else cap
     doc_t = torch.from_numpy(doc).to(DEV) if doc is not None else None
@@ -39,7 +39,7 @@ def run_gpu(w: WL.Workload, q, k, v, doc=None, sep=True, score=None,
                                   doc_id=doc_t)
     o, lse = fa.flex_attention(q.to(DEV), k.to(DEV), v.to(DEV), bm,
                                score_mod=_score_arg(score, cap),
-                               scale=w.scale)
+                               scale=w.scale, num_splits=num_splits)
     torch.cuda.synchronize()
     return o, lse
 
@@ -80,6 +80,52 @@ def test_small_full_rows(dtype, D, blk, mask, score):
                      f"{dtype} D={D} blk={blk} {mask} {score} sep={sep}")
 
 
+SPLIT_SMALL = []
+for D, blk in ((128, 128), (64, 128), (128, 64), (64, 64)):
+    for mask in ("causal", "sliding_window", "document", "none"):
+        for score in ("none", "softcap", "alibi"):
+            SPLIT_SMALL.append((D, blk, mask, score))
+
+
+@pytest.mark.parametrize("D,blk,mask,score", SPLIT_SMALL)
+def test_small_split_rows(D, blk, mask, score):
+    # split-KV: each row's visit list in several parts (some empty: more
+    # parts than key blocks), merged; every row against the oracle
+    ql, kl = 3 * blk + 37, 4 * blk + 101
+    w = WL.Workload("small", "bf16", 2, 4, 2, ql, kl, D, mask, blk, blk,
+                    seed=0, window=blk + 13 if mask == "sliding_window" else None,
+                    score=score, softcap=3.0 if score == "softcap" else None)
+    rng = np.random.default_rng(zlib.crc32(f"split{D}{blk}{mask}{score}".encode()))
+    doc = (np.sort(rng.integers(0, 4, max(ql, kl))).astype(np.int32)
+           if mask == "document" else None)
+    q, k, v = _inputs(w, 23)
+    o_ref, l_ref = oracle_case(q, k, v, w, doc)
+    for ns in (2, 3, 7):
+        print(f"[fwd split small] D={D} blk={blk} {mask} {score} splits={ns}",
+              flush=True)
+        o, lse = run_gpu(w, q, k, v, doc, sep=ns != 3, num_splits=ns)
+        assert_close(o, lse, o_ref, l_ref, TOL["bf16"],
+                     f"split {ns} D={D} blk={blk} {mask} {score}")
+
+
+def test_split_extremes():
+    # the largest part count, and a single key block per row
+    w = WL.Workload("small", "bf16", 1, 2, 2, 300, 300, 64, "causal", 128,
+                    128, seed=0)
+    q, k, v = _inputs(w, 5)
+    o_ref, l_ref = oracle_case(q, k, v, w, None)
+    for ns in (1, 64):
+        print(f"[fwd split extremes] splits={ns}", flush=True)
+        o, lse = run_gpu(w, q, k, v, num_splits=ns)
+        assert_close(o, lse, o_ref, l_ref, TOL["bf16"], f"split {ns}")
+    w = WL.Workload("small", "bf16", 1, 2, 2, 128, 128, 128, "none", 128,
+                    128, seed=0)
+    q, k, v = _inputs(w, 6)
+    o_ref, l_ref = oracle_case(q, k, v, w, None)
+    o, lse = run_gpu(w, q, k, v, num_splits=4)
+    assert_close(o, lse, o_ref, l_ref, TOL["bf16"], "one block, 4 parts")
+
+
 @pytest.fixture(scope="module")
 def workload_inputs():
     cache = {}
@@ -114,6 +160,30 @@ def test_workload_parity(name, workload_inputs):
           flush=True)
     # every row, not only the sampled ones, is finite
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("name,ns", [("c2", None), ("c3", 2), ("c5", 3)])
+def test_workload_parity_split(name, ns, workload_inputs):
+    # split-KV at full size (None: the binding's automatic choice, 8 parts
+    # for c2 on 256 compute units), on the sampled rows
+    w, q, k, v, doc = workload_inputs(name)
+    if ns is None:
+        ns = fa.auto_num_splits(torch.bfloat16, w.B, w.H, w.q_len // w.block_m,
+                                torch.cuda.get_device_properties(0)
+                                .multi_processor_count)
+        assert ns > 1
+    print(f"[fwd workload split] {name} splits={ns}", flush=True)
+    o, lse = run_gpu(w, q, k, v, doc, num_splits=ns)
+    rows = sample_rows(w.q_len, w.block_m, doc, n_random=24, seed=w.seed)
+    idx = torch.from_numpy(rows).to(DEV)
+    o_ref, l_ref = oracle_case(q, k, v, w, doc, rows=rows)
+    assert_close(o.index_select(2, idx), lse.index_select(2, idx), o_ref,
+                 l_ref, TOL[w.dtype], f"{name} split {ns}")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    # and every row agrees with the unsplit kernel
+    o1, l1 = run_gpu(w, q, k, v, doc, num_splits=1)
+    assert (o.float() - o1.float()).abs().max().item() <= TOL["bf16"]
+    assert (lse - l1).abs().max().item() <= TOL["bf16"]
 
 
 def test_separate_full_blocks_agree_at_full_size(workload_inputs):
