@@ -133,6 +133,9 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default="c3", choices=sorted(WL.CONFIGS))
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--num-splits", type=int, default=None,
+                    help="split-KV parts per query block (default: the "
+                         "binding's automatic choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reference-masks", action="store_true",
                     help="skip the dense-causal and no-skip timings")
@@ -166,9 +169,15 @@ def main(argv=None) -> int:
                                     device=dev, BLOCK_SIZE=w.block_m,
                                     window=w.window, doc_id=doc_t)
 
+    num_splits = a.num_splits
+    if num_splits is None:
+        num_splits = fa.auto_num_splits(
+            qd.dtype, w.B, w.H, -(-w.q_len // w.block_m),
+            torch.cuda.get_device_properties(dev).multi_processor_count)
+
     def fwd(bm):
         fa.flex_attention(qd, kd, vd, bm, score_mod=score, scale=w.scale,
-                          out=o, lse=lse)
+                          out=o, lse=lse, num_splits=num_splits)
 
     bm = build()
     torch.cuda.synchronize()
@@ -282,6 +291,7 @@ def main(argv=None) -> int:
                    "block": w.block_m,
                    "live_blocks_per_head": live_bh,
                    "blocks_per_head": bm.num_q_blocks * bm.num_kv_blocks,
+                   "num_splits": num_splits,
                    "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak, 4),
         "fwd_ms": round(fwd_avg, 5),
