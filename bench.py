@@ -57,6 +57,28 @@ def live_blocks(bm) -> int:
     return n
 
 
+def allowed_pairs(w: WL.Workload, doc) -> int:
+    """Allowed (query, key) pairs of one (b, h), counted from the built-in
+    masks' definitions (exact-work diagnostic: 4 D flops per pair)."""
+    i = np.arange(w.q_len, dtype=np.int64)
+    hi = np.minimum(i + 1, w.kv_len)                  # keys j <= i, j < KV
+    if w.mask == "none":
+        return int(w.q_len) * int(w.kv_len)
+    if w.mask == "causal":
+        return int(hi.sum())
+    if w.mask == "sliding_window":
+        lo = np.maximum(i - w.window + 1, 0)
+        return int(np.maximum(hi - lo, 0).sum())
+    # document: keys j <= i with doc[j] == doc[i]
+    d = np.asarray(doc)
+    total = 0
+    for v in np.unique(d[:w.q_len]):
+        keys = np.flatnonzero(d[:w.kv_len] == v)
+        rows = np.flatnonzero(d[:w.q_len] == v)
+        total += int(np.searchsorted(keys, rows, side="right").sum())
+    return total
+
+
 def describe(w: WL.Workload) -> str:
     s = (f"{w.name}: {w.dtype} B={w.B} H={w.H} Q=KV={w.q_len} D={w.D} "
          f"{w.mask}")
@@ -295,6 +317,10 @@ def main(argv=None) -> int:
                    "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak, 4),
         "fwd_ms": round(fwd_avg, 5),
+        "fwd_ms_median": round(float(np.median(fwd_ms)), 5),
+        "fwd_ms_min": round(float(np.min(fwd_ms)), 5),
+        "exact_work_tflops": round(
+            allowed_pairs(w, doc) * w.B * w.H * 4 * w.D / (fwd_avg * 1e-3) / 1e12, 2),
         "mask_build_ms": round(float(np.mean(mask_ms)), 5),
         **extra,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
