@@ -66,6 +66,24 @@ __device__ __forceinline__ int kv_swizzle(int r) {
   }
 }
 
+// max / sum of x over lanes l and l ^ 32 (the two halves of a query row's
+// keys): v_permlane32_swap exchanges the upper half of one register with the
+// lower half of another, so after swapping two copies of x each lane holds
+// x[l] and x[l ^ 32]. No LDS round trip, unlike a generic shuffle.
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float row_pair_max(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return __builtin_fmaxf(a, b);
+}
+__device__ __forceinline__ float row_pair_sum(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
+}
+
 __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
 }
@@ -239,7 +257,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
   };
 
   float m_run = FA_NEG_INF;  // reference max, log2 domain
-  float l_run = 0.0f;        // this lane's share of the row sum
+  float l_run = 0.0f;        // this lane's share of the row sum, in two
+  float l_run2 = 0.0f;       // independent accumulators
   f32x16 oacc[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
@@ -322,19 +341,22 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
       }
     }
 
-    // ---- online softmax
-    float mx = FA_NEG_INF;
+    // ---- online softmax. Row max: four independent chains, then the
+    // exchange with lane ^ 32 (the other half of the row's keys).
+    float mx4[4] = {FA_NEG_INF, FA_NEG_INF, FA_NEG_INF, FA_NEG_INF};
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[jt][r]);
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 0; r < 8; ++r) mx4[c] = __builtin_fmaxf(mx4[c], s[c >> 1][8 * (c & 1) + r]);
+    float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
+    mx = row_pair_max(mx);
     if constexpr (SCORE == FA_SCORE_NONE) mx *= sc.c;  // raw -> log2 domain
     const bool raise = mx > m_run + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(raise)) {
       const float m_new = raise ? mx : m_run;
       const float alpha = (m_new == m_run) ? 1.0f : exp2_hw(m_run - m_new);
       l_run *= alpha;
+      l_run2 *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
@@ -360,8 +382,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
         // copy the word out first: bit-casting a vector element in place
         // mis-compiles (every iteration reads element 0)
         const uint32_t word = pw[e];
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, l_run,
-                                                false);
+        float& acc = (e & 1) ? l_run2 : l_run;
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, acc,
+                                              false);
       }
     }
 
@@ -398,7 +421,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = row_pair_sum(l_run + l_run2);
   if (p.nsplit > 1) {
     // split-KV part: the unnormalised accumulator and (m, l) for the merge
     if (i_ok) {
