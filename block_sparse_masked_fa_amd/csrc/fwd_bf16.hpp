@@ -1,10 +1,10 @@
 // Fused block-sparse attention forward, bf16 inputs, fp32 accumulation, for
 // gfx950 (MFMA v_mfma_f32_32x32x16_bf16, LDS DMA, transposed LDS reads).
 //
-// Work split. One workgroup computes one query block (BLK = 64 or 128 rows)
-// of one head with BLK / 32 wavefronts; wave w owns query rows
-// [32w, 32w + 32). Key blocks are consumed in stages of 64 keys. Two
-// workgroups share a CU (registers <= 256 per lane, 64 KB of LDS each at
+// Work split. One workgroup computes one query block (BQ = 64 or 128 rows)
+// of one head with BQ / 32 wavefronts; wave w owns query rows
+// [32w, 32w + 32). Key blocks (BK = 64 or 128 keys) are consumed in stages
+// of 64 keys. Two workgroups share a CU (registers <= 256 per lane, 64 KB of LDS each at
 // D = 128), so while one is in its MFMA phase the other's softmax arithmetic
 // can issue: the two are independent and drift apart.
 //
@@ -108,11 +108,11 @@ __device__ __forceinline__ bool xcd_work_item(const FwdLaunch& p, WorkItem& w) {
   return true;
 }
 
-template <int D, int BLK, int SCORE>
-__global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) {
-  constexpr int NW = BLK / 32;            // wavefronts
+template <int D, int BQ, int BK, int SCORE>
+__global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) {
+  constexpr int NW = BQ / 32;             // wavefronts
   constexpr int NT = NW * 64;             // threads
-  constexpr int SPB = BLK / kStageKeys;   // stages per key block
+  constexpr int SPB = BK / kStageKeys;    // stages per key block
   constexpr int RB = D * 2;               // bytes per LDS row
   constexpr int CPR = D / 8;              // 16-byte chunks per row
   constexpr int RPK = 1024 / RB;          // rows per 1 KB DMA segment
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
   const int g = lane >> 5;
 
   const int hk = w.h / (p.H / p.H_kv);
-  const int i = w.m * BLK + wave * 32 + lq;
+  const int i = w.m * BQ + wave * 32 + lq;
   const bool i_ok = i < p.q_len;
   const int kv_len = p.kv_len;
   const int mkind = p.mask.kind;
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
     return v < np ? pl[np - 1 - v] : fl[nf - 1 - (v - np)];
   };
   auto masked_at = [&](int it, int n) -> bool {
-    return v0 + it < np || (n + 1) * BLK > kv_len;
+    return v0 + it < np || (n + 1) * BK > kv_len;
   };
 
   // Issue the DMA of stage `st` (block visit st / SPB) into one buffer. Each
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
     const int it = st / SPB;
     const int n = block_at(it);
     if (static_cast<unsigned>(n) >= static_cast<unsigned>(nkvb)) return;
-    const int j0 = n * BLK + (SPB - 1 - st % SPB) * kStageKeys;
+    const int j0 = n * BK + (SPB - 1 - st % SPB) * kStageKeys;
     const int rows_left = kv_len - j0;  // >= 1
     const int krec = (rows_left - 1) * static_cast<int>(kstride) + RB;
     const int vrec = (rows_left - 1) * static_cast<int>(vstride) + RB;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void fwd_bf16_kernel(const FwdLaunch p)
     const int n = block_at(it);
     if (static_cast<unsigned>(n) >= static_cast<unsigned>(nkvb)) return;
     const bool masked = masked_at(it, n);
-    const int j0 = n * BLK + (SPB - 1 - st % SPB) * kStageKeys;
+    const int j0 = n * BK + (SPB - 1 - st % SPB) * kStageKeys;
 
     // ---- S^T = K Q^T for the stage's 64 keys
     f32x16 s[2];

@@ -6,7 +6,7 @@ namespace fa {
 int launch_fwd_fp32(const FwdLaunch& p, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const dim3 grid(static_cast<unsigned>(p.B * p.H * p.nqb));
-  const int key = (p.D * 1000 + p.block) * 4 + p.score_kind;
+  const int key = (p.D * 1000 + p.block_m) * 4 + p.score_kind;
   switch (key) {
 #define FA_CASE(D, BLK, SC)                                                    \
   case (D * 1000 + BLK) * 4 + SC:                                              \

@@ -36,7 +36,8 @@ struct FwdLaunch {
   float scale;
   MaskParams mask;
   int32_t Bm, Hm;       // block-mask broadcast dims (1 or B / H)
-  int32_t block;        // block_m == block_n
+  int32_t block_m;      // query rows per block
+  int32_t block_n;      // keys per block
   int32_t nqb, nkvb;
   const int32_t* num;
   const int32_t* idx;

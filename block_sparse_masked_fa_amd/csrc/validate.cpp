@@ -188,9 +188,12 @@ int check_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H, int32_t H_kv,
   if (nqb != bm->num_q_blocks || nkvb != bm->num_kv_blocks)
     return fail(msg, FA_ERR_SHAPE_MISMATCH,
                 "block mask block counts disagree with its lengths");
-  if (bm->block_m != bm->block_n || (bm->block_m != 64 && bm->block_m != 128))
+  const bool b64_128 = (bm->block_m == 64 || bm->block_m == 128) &&
+                       (bm->block_n == 64 || bm->block_n == 128);
+  if (!b64_128 || (dtype == FA_FP32 && bm->block_m != bm->block_n))
     return fail(msg, FA_ERR_UNSUPPORTED,
-                "attention needs block_m == block_n in {64, 128}");
+                "attention needs block_m, block_n in {64, 128} "
+                "(and block_m == block_n for fp32)");
   int32_t skind = score ? score->kind : FA_SCORE_NONE;
   float cap = score ? score->softcap : 0.0f;
   if (skind != FA_SCORE_NONE && skind != FA_SCORE_SOFTCAP &&
@@ -250,7 +253,8 @@ int check_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H, int32_t H_kv,
   out->mask = MaskParams{bm->mask.kind, bm->mask.window, bm->mask.doc_id};
   out->Bm = bm->B;
   out->Hm = bm->H;
-  out->block = bm->block_m;
+  out->block_m = bm->block_m;
+  out->block_n = bm->block_n;
   out->nqb = nqb;
   out->nkvb = nkvb;
   out->num = bm->kv_num_blocks;

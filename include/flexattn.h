@@ -178,8 +178,10 @@ fa_status fa_create_block_mask(const fa_mask_mod* mask, int32_t B, int32_t H,
  *   scale      multiplies q.k before score_mod; finite and > 0
  *              (1/sqrt(D) is the usual choice).
  *   bm         host pointer to a block mask for (q_len, kv_len) with
- *              bm->B in {1, B}, bm->H in {1, H}, and
- *              block_m == block_n in {64, 128}. Index arrays may come from
+ *              bm->B in {1, B}, bm->H in {1, H}, and block_m, block_n in
+ *              {64, 128} (BLOCK_SIZE as an int or a (q, kv) pair, on the
+ *              create_block_mask page; FA_FP32 needs block_m == block_n).
+ *              Index arrays may come from
  *              fa_create_block_mask or from the caller; entries outside
  *              [0, NKVB) are skipped and counts are clamped to [0, NKVB].
  *   score      host pointer to the score_mod (NULL = none).

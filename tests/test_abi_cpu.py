@@ -207,6 +207,15 @@ def _fwd(**over):
     (dict(bm=_good_bm(H=2)), C.FA_ERR_SHAPE_MISMATCH),
     (dict(bm=_good_bm(block=32)), C.FA_ERR_UNSUPPORTED),
     (dict(bm=_bm(**{**{f: getattr(_good_bm(), f) for f, _ in
+                       C.fa_block_mask._fields_}, "block_n": 256,
+                    "num_kv_blocks": 1})), C.FA_ERR_UNSUPPORTED),
+    (dict(dtype=C.FA_FP32, D=64, q_stride=(4 * 256 * 64, 256 * 64, 64),
+          k_stride=(4 * 256 * 64, 256 * 64, 64),
+          v_stride=(4 * 256 * 64, 256 * 64, 64),
+          bm=_bm(**{**{f: getattr(_good_bm(), f) for f, _ in
+                       C.fa_block_mask._fields_}, "block_n": 64,
+                    "num_kv_blocks": 4})), C.FA_ERR_UNSUPPORTED),
+    (dict(bm=_bm(**{**{f: getattr(_good_bm(), f) for f, _ in
                        C.fa_block_mask._fields_}, "num_kv_blocks": 5})),
      C.FA_ERR_SHAPE_MISMATCH),
     (dict(score=C.fa_score_mod(kind=C.FA_SCORE_SOFTCAP, softcap=0.0)),

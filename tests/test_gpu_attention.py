@@ -80,6 +80,40 @@ def test_small_full_rows(dtype, D, blk, mask, score):
                      f"{dtype} D={D} blk={blk} {mask} {score} sep={sep}")
 
 
+PAIRS = []
+for D in (128, 64):
+    for bq, bk in ((128, 64), (64, 128)):
+        for mask in ("causal", "sliding_window", "document", "none"):
+            for score in ("none", "alibi"):
+                PAIRS.append((D, bq, bk, mask, score))
+
+
+@pytest.mark.parametrize("D,bq,bk,mask,score", PAIRS)
+def test_small_block_size_pairs(D, bq, bk, mask, score):
+    # BLOCK_SIZE as a (q, kv) pair: query blocks and key blocks of different
+    # sizes, ragged tails on both axes; every row against the oracle, whole
+    # and through split-KV
+    ql, kl = 3 * bq + 29, 3 * bk + 77
+    w = WL.Workload("small", "bf16", 2, 2, 2, ql, kl, D, mask, bq, bk, seed=0,
+                    window=bk + 21 if mask == "sliding_window" else None,
+                    score=score)
+    rng = np.random.default_rng(zlib.crc32(f"pair{D}{bq}{bk}{mask}{score}".encode()))
+    doc = (np.sort(rng.integers(0, 3, max(ql, kl))).astype(np.int32)
+           if mask == "document" else None)
+    q, k, v = _inputs(w, 31)
+    o_ref, l_ref = oracle_case(q, k, v, w, doc)
+    for ns in (1, 3):
+        print(f"[fwd block pair] D={D} ({bq},{bk}) {mask} {score} splits={ns}",
+              flush=True)
+        doc_t = torch.from_numpy(doc).to(DEV) if doc is not None else None
+        bm = fa.create_block_mask(mask, None, None, ql, kl, device=DEV,
+                                  BLOCK_SIZE=(bq, bk), window=w.window,
+                                  doc_id=doc_t)
+        o, lse = run_gpu(w, q, k, v, doc, bm=bm, num_splits=ns)
+        assert_close(o, lse, o_ref, l_ref, TOL["bf16"],
+                     f"pair ({bq},{bk}) D={D} {mask} {score} split {ns}")
+
+
 SPLIT_SMALL = []
 for D, blk in ((128, 128), (64, 128), (128, 64), (64, 64)):
     for mask in ("causal", "sliding_window", "document", "none"):

@@ -115,3 +115,33 @@ def test_block_mask_reuse_and_stream_order():
         b = gpu_mask("sliding_window", 2, 3, 1000, 1000, 64, 64, window=200)
     for k in a:
         assert np.array_equal(a[k], b[k])
+
+
+@pytest.mark.parametrize("kind", ["causal", "sliding_window", "document",
+                                  "none"])
+def test_block_mask_maximum_sizes(kind):
+    # the largest key-block count a row may have (32768: one key per block)
+    # and the largest block size (1024), with ragged tails
+    rng = np.random.default_rng(11)
+    for ql, kl, bm_, bn_ in ((200, 32768, 128, 1), (3000, 9000, 1024, 1024),
+                             (1024, 32768, 1024, 1)):
+        doc = (np.sort(rng.integers(0, 5, size=max(ql, kl))).astype(np.int32)
+               if kind == "document" else None)
+        W = 700 if kind == "sliding_window" else None
+        label = f"{kind} ql={ql} kl={kl} bm={bm_} bn={bn_}"
+        print(f"[block mask max] {label}", flush=True)
+        got = gpu_mask(kind, 1, 1, ql, kl, bm_, bn_, W, doc)
+        want = O.create_block_mask(kind, 1, 1, ql, kl, bm_, bn_, window=W,
+                                   doc_id=doc)
+        assert_same(got, want, label)
+
+
+def test_block_mask_limits_refused():
+    # one key block too many, and a block size above 1024, are refused on
+    # the host before any launch
+    with pytest.raises(fa.FlexAttnError):
+        fa.create_block_mask("causal", 1, 1, 64, 32769, device=DEV,
+                             BLOCK_SIZE=(64, 1))
+    with pytest.raises(fa.FlexAttnError):
+        fa.create_block_mask("causal", 1, 1, 2048, 2048, device=DEV,
+                             BLOCK_SIZE=2048)
