@@ -234,10 +234,15 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
   // tile is read through a buffer resource whose base is the stage's first
   // row and whose size ends at the sequence end: rows past it read as zeros
   // (the hardware range check), so the tail needs no special path.
-  auto issue = [&](int st, char* sK, char* sV, int* sD) {
+  // block of stage st (one scalar load per key block: the stages of a block
+  // share it), -1 for an index outside [0, nkvb)
+  auto stage_block = [&](int st) -> int {
+    const int b = block_at(st / SPB);
+    return static_cast<unsigned>(b) < static_cast<unsigned>(nkvb) ? b : -1;
+  };
+  auto issue = [&](int st, int n, char* sK, char* sV, int* sD) {
     const int it = st / SPB;
-    const int n = block_at(it);
-    if (static_cast<unsigned>(n) >= static_cast<unsigned>(nkvb)) return;
+    if (n < 0) return;
     const int j0 = n * BK + (SPB - 1 - st % SPB) * kStageKeys;
     const int rows_left = kv_len - j0;  // >= 1
     const int krec = (rows_left - 1) * static_cast<int>(kstride) + RB;
@@ -264,10 +269,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  auto compute = [&](int st, const char* sK, const char* sV, const int* sD) {
+  auto compute = [&](int st, int n, const char* sK, const char* sV, const int* sD) {
     const int it = st / SPB;
-    const int n = block_at(it);
-    if (static_cast<unsigned>(n) >= static_cast<unsigned>(nkvb)) return;
+    if (n < 0) return;
     const bool masked = masked_at(it, n);
     const int j0 = n * BK + (SPB - 1 - st % SPB) * kStageKeys;
 
@@ -407,17 +411,23 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
   // The setup loads (Q, document id) complete before the first tile DMA, so
   // the per-stage waits below only ever wait for tiles.
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  if (nstages > 0) issue(0, sK0, sV0, sDoc0);
+  // n_cur: block of stage st; n_nxt: of stage st + 1 (loaded with its DMA)
+  int n_cur = nstages > 0 ? stage_block(0) : -1;
+  if (nstages > 0) issue(0, n_cur, sK0, sV0, sDoc0);
   for (int st = 0; st < nstages; st += 2) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's DMA landed
     __syncthreads();                     // every lane's DMA landed; buffer 1 free
-    if (st + 1 < nstages) issue(st + 1, sK1, sV1, sDoc1);
-    compute(st, sK0, sV0, sDoc0);
+    int n_nxt = (st + 1) % SPB == 0 ? stage_block(st + 1) : n_cur;
+    if (st + 1 < nstages) issue(st + 1, n_nxt, sK1, sV1, sDoc1);
+    compute(st, n_cur, sK0, sV0, sDoc0);
     if (st + 1 >= nstages) break;
+    n_cur = n_nxt;
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
-    if (st + 2 < nstages) issue(st + 2, sK0, sV0, sDoc0);
-    compute(st + 1, sK1, sV1, sDoc1);
+    n_nxt = (st + 2) % SPB == 0 ? stage_block(st + 2) : n_cur;
+    if (st + 2 < nstages) issue(st + 2, n_nxt, sK0, sV0, sDoc0);
+    compute(st + 1, n_cur, sK1, sV1, sDoc1);
+    n_cur = n_nxt;
   }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
