@@ -18,6 +18,8 @@ def allowed(kind, i, j, window=None, doc=None):
         return i >= j
     if kind == "sliding_window":
         return 0 <= i - j < window
+    if kind == "local_window":
+        return -window < i - j < window
     if kind == "document":
         return i >= j and doc[i] == doc[j]
     raise ValueError(kind)

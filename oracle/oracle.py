@@ -21,6 +21,9 @@ What is computed, and where the pages fix it
     section "State the boundary precisely");
   - document, causal and ``doc[q_idx] == doc[kv_idx]`` with one int32 id
     array indexed by both positions (how-to, "Mask 3: document-packed");
+  - local window, ``|q_idx - kv_idx| < W``: the symmetric window, a bound
+    on the absolute distance that the crackedaicode page names as the
+    alternative to the causal window (same section);
   - none: every pair allowed (how-to, "The two hooks": either hook may be
     omitted).
 
@@ -72,7 +75,7 @@ import math
 
 import numpy as np
 
-MASK_KINDS = ("none", "causal", "sliding_window", "document")
+MASK_KINDS = ("none", "causal", "sliding_window", "document", "local_window")
 SCORE_KINDS = ("none", "softcap", "alibi")
 
 EMPTY, PARTIAL, FULL = 0, 1, 2
@@ -104,6 +107,13 @@ def mask_mod(kind: str, q_idx, kv_idx, window=None, doc_id=None):
             raise ValueError("sliding window needs W >= 1")
         d = i - j
         return (d >= 0) & (d < int(window))
+    if kind == "local_window":
+        # symmetric local window: a bound on the absolute distance
+        # (crackedaicode "Sliding-Window Self-Attention", "State the
+        # boundary precisely", last paragraph)
+        if window is None or int(window) < 1:
+            raise ValueError("local window needs W >= 1")
+        return np.abs(i - j) < int(window)
     if kind == "document":
         if doc_id is None:
             raise ValueError("document mask needs doc_id")

@@ -83,6 +83,27 @@ def test_sliding_window_special_cases(T):
         O.dense_mask("sliding_window", T, T, window=0)
 
 
+@pytest.mark.parametrize("T", [1, 2, 6, 17])
+def test_local_window_is_the_symmetric_bound(T):
+    # crackedaicode "State the boundary precisely": a symmetric local window
+    # bounds the absolute distance. For square masks it is the causal
+    # window together with its transpose, W = 1 is the identity, and W >= T
+    # allows every pair.
+    for W in (1, 2, 3, T, T + 4):
+        loc = O.dense_mask("local_window", T, T, window=W)
+        sw = O.dense_mask("sliding_window", T, T, window=W)
+        assert np.array_equal(loc, loc.T)
+        assert np.array_equal(loc, sw | sw.T)
+        for i in range(T):
+            assert np.flatnonzero(loc[i]).tolist() == list(
+                range(max(0, i - W + 1), min(T, i + W)))
+    assert np.array_equal(O.dense_mask("local_window", T, T, window=1),
+                          np.eye(T, dtype=bool))
+    assert O.dense_mask("local_window", T, T, window=T).all()
+    with pytest.raises(ValueError):
+        O.dense_mask("local_window", T, T, window=0)
+
+
 def test_document_mask_is_block_diagonal_three_docs():
     # how-to "Mask 3": ids switch at 2048 and 5000 in an 8192 context
     doc = _three_doc_ids()
@@ -239,7 +260,7 @@ def _rand(rng, *shape):
 
 
 def _mask_kw(kind, T, rng):
-    if kind == "sliding_window":
+    if kind in ("sliding_window", "local_window"):
         return {"window": int(rng.integers(1, T + 2))}
     if kind == "document":
         return {"doc_id": np.sort(rng.integers(0, 3, T)).astype(np.int32)}
@@ -351,6 +372,10 @@ def _n_allowed(mask, T, kw):
         return i + 1
     if mask == "sliding_window":
         return np.minimum(i + 1, kw["window"])
+    if mask == "local_window":
+        # W - 1 keys on each side of the diagonal, cut at both sequence ends
+        return (np.minimum(i, kw["window"] - 1)
+                + np.minimum(T - 1 - i, kw["window"] - 1) + 1)
     doc = kw["doc_id"]
     start = np.array([np.flatnonzero(doc == doc[t])[0] for t in range(T)])
     return i - start + 1
