@@ -69,6 +69,9 @@ def allowed_pairs(w: WL.Workload, doc) -> int:
     if w.mask == "sliding_window":
         lo = np.maximum(i - w.window + 1, 0)
         return int(np.maximum(hi - lo, 0).sum())
+    if w.mask == "local_window":
+        lo = np.maximum(i - w.window + 1, 0)
+        return int(np.maximum(np.minimum(i + w.window, w.kv_len) - lo, 0).sum())
     # document: keys j <= i with doc[j] == doc[i]
     d = np.asarray(doc)
     total = 0

@@ -10,7 +10,8 @@ from .api import (  # noqa: F401
     BlockMask, FlexAttnError, MaskMod, ScoreMod, alibi, auto_num_splits,
     causal, create_block_mask, document, fa_block_mask_dims,
     fa_create_block_mask, fa_flex_attention_fwd, fa_flex_attention_fwd_split,
-    fa_split_workspace_bytes, flex_attention, no_mask, sliding_window,
+    fa_split_workspace_bytes, flex_attention, local_window, no_mask,
+    sliding_window,
     softcap,
 )
 from ._capi import LIB_PATH, lib  # noqa: F401

@@ -30,6 +30,7 @@ FA_MASK_NONE = 0
 FA_MASK_CAUSAL = 1
 FA_MASK_SLIDING_WINDOW = 2
 FA_MASK_DOCUMENT = 3
+FA_MASK_LOCAL_WINDOW = 4
 
 # fa_score_kind
 FA_SCORE_NONE = 0

@@ -25,7 +25,8 @@ import torch
 from . import _capi as C
 
 __all__ = [
-    "MaskMod", "ScoreMod", "causal", "sliding_window", "document",
+    "MaskMod", "ScoreMod", "causal", "sliding_window", "local_window",
+    "document",
     "no_mask", "softcap", "alibi", "BlockMask", "create_block_mask",
     "flex_attention", "fa_block_mask_dims", "fa_create_block_mask",
     "fa_flex_attention_fwd", "fa_flex_attention_fwd_split",
@@ -57,6 +58,11 @@ def causal() -> MaskMod:
 
 def sliding_window(window: int) -> MaskMod:
     return MaskMod(C.FA_MASK_SLIDING_WINDOW, window=int(window))
+
+
+def local_window(window: int) -> MaskMod:
+    """|q_idx - kv_idx| < window (symmetric, not causal)."""
+    return MaskMod(C.FA_MASK_LOCAL_WINDOW, window=int(window))
 
 
 def document(doc_id: torch.Tensor) -> MaskMod:
@@ -95,6 +101,8 @@ def _mask_from(spec, window=None, doc_id=None) -> MaskMod:
         return causal()
     if spec == "sliding_window":
         return sliding_window(window)
+    if spec == "local_window":
+        return local_window(window)
     if spec == "document":
         return document(doc_id)
     raise ValueError(f"unknown mask_mod {spec!r}")

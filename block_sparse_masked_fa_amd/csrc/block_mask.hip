@@ -12,7 +12,8 @@
 // Tile state over the in-range pairs (i, j) of a tile: no allowed pair =
 // empty, every pair of a complete (uncut) tile allowed = full, else partial.
 // How the kernel decides it, exactly, per mask kind:
-//   * none, causal, sliding window: the predicate depends only on d = i - j,
+//   * none, causal, sliding and local window: the predicate depends only on
+//     d = i - j (an interval of allowed d),
 //     and the pairs of a tile realise every integer d in
 //     [i_lo - j_hi, i_hi - j_lo]. "Some pair allowed" and "all pairs allowed"
 //     are therefore interval tests on that range (one thread per tile).
@@ -71,6 +72,9 @@ __device__ __forceinline__ unsigned char classify_closed(const BlockMaskLaunch& 
       return classify_range(t, 0, 1LL << 40);
     case FA_MASK_SLIDING_WINDOW:
       return classify_range(t, 0, static_cast<long long>(p.mask.window) - 1);
+    case FA_MASK_LOCAL_WINDOW:
+      return classify_range(t, 1 - static_cast<long long>(p.mask.window),
+                            static_cast<long long>(p.mask.window) - 1);
     default:  // none
       return t.complete ? kFull : kPartial;
   }

@@ -187,8 +187,17 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
 
   const ScoreConsts sc = make_score_consts(p, w.h);
   // mask_mod as an interval of key indices per row: j in [lo_abs, lo_abs + span)
-  const int hi_abs = mkind == FA_MASK_NONE ? kv_len : min(i + 1, kv_len);
-  const int lo_abs = mkind == FA_MASK_SLIDING_WINDOW ? i - window + 1 : 0;
+  // (64-bit so that any window >= 1 is exact; keys are >= 0, so the
+  // interval start is clamped there)
+  const int hi_abs =
+      mkind == FA_MASK_NONE ? kv_len
+      : mkind == FA_MASK_LOCAL_WINDOW
+          ? static_cast<int>(min(static_cast<int64_t>(i) + window, static_cast<int64_t>(kv_len)))
+          : min(i + 1, kv_len);
+  const int lo_abs =
+      (mkind == FA_MASK_SLIDING_WINDOW || mkind == FA_MASK_LOCAL_WINDOW)
+          ? static_cast<int>(max(static_cast<int64_t>(i) - window + 1, static_cast<int64_t>(0)))
+          : 0;
   const unsigned span = static_cast<unsigned>(max(hi_abs - lo_abs, 0));
 
   // ---- per-lane byte offsets, fixed for the whole row
@@ -315,7 +324,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
 
     // ---- mask_mod on partial and sequence-tail blocks only. Every built-in
     // mask bounds a row's keys to an interval (causal: j <= i, sliding
-    // window: i - W < j <= i, and j < kv_len), so the test is one unsigned
+    // window: i - W < j <= i, local window: |i - j| < W, and j < kv_len),
+    // so the test is one unsigned
     // compare of the key's offset in the interval against its length, plus
     // the document-id equality for document masks.
     if (masked) {

@@ -83,6 +83,9 @@ __device__ __forceinline__ bool mask_ok(int i, int j, int window, int di,
   } else if constexpr (KIND == FA_MASK_SLIDING_WINDOW) {
     const int d = i - j;
     return (d >= 0) & (d < window);
+  } else if constexpr (KIND == FA_MASK_LOCAL_WINDOW) {
+    const int d = i - j;
+    return (d < window) & (-d < window);
   } else if constexpr (KIND == FA_MASK_DOCUMENT) {
     return (i >= j) & (di == dj);
   } else {

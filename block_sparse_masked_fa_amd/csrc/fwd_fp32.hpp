@@ -122,6 +122,7 @@ __global__ __launch_bounds__(BLK * 2) void fwd_fp32_kernel(const FwdLaunch p) {
           switch (mkind) {
             case FA_MASK_CAUSAL: ok &= mask_ok<FA_MASK_CAUSAL>(i, j, window, di, 0); break;
             case FA_MASK_SLIDING_WINDOW: ok &= mask_ok<FA_MASK_SLIDING_WINDOW>(i, j, window, di, 0); break;
+            case FA_MASK_LOCAL_WINDOW: ok &= mask_ok<FA_MASK_LOCAL_WINDOW>(i, j, window, di, 0); break;
             case FA_MASK_DOCUMENT: ok &= mask_ok<FA_MASK_DOCUMENT>(i, j, window, di, sDoc[jl]); break;
             default: break;
           }

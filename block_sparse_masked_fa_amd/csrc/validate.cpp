@@ -21,9 +21,10 @@ int check_mask_mod(const fa_mask_mod* mask, int32_t q_len, int32_t kv_len,
     case FA_MASK_CAUSAL:
       return FA_OK;
     case FA_MASK_SLIDING_WINDOW:
+    case FA_MASK_LOCAL_WINDOW:
       if (mask->window < 1)
         return fail(msg, FA_ERR_INVALID_VALUE,
-                    "sliding window needs window >= 1, got " +
+                    "window masks need window >= 1, got " +
                         std::to_string(mask->window));
       return FA_OK;
     case FA_MASK_DOCUMENT: {

@@ -66,12 +66,17 @@ typedef enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
  *                   precisely")
  *   DOCUMENT        q_idx >= kv_idx and doc_id[q_idx] == doc_id[kv_idx]
  *                   (how-to, "Mask 3: document-packed")
+ *   LOCAL_WINDOW    |q_idx - kv_idx| < window: the symmetric local window,
+ *                   a bound on the absolute distance (crackedaicode
+ *                   "Sliding-Window Self-Attention", "State the boundary
+ *                   precisely")
  * None of them depends on the batch or head index. */
 typedef enum fa_mask_kind {
   FA_MASK_NONE = 0,
   FA_MASK_CAUSAL = 1,
   FA_MASK_SLIDING_WINDOW = 2,
-  FA_MASK_DOCUMENT = 3
+  FA_MASK_DOCUMENT = 3,
+  FA_MASK_LOCAL_WINDOW = 4
 } fa_mask_kind;
 
 /* Built-in score_mods, applied to the scaled score s = scale * q.k of
@@ -88,7 +93,7 @@ typedef enum fa_score_kind {
 
 typedef struct fa_mask_mod {
   int32_t kind;          /* fa_mask_kind                                  */
-  int32_t window;        /* SLIDING_WINDOW: W >= 1; ignored otherwise      */
+  int32_t window;        /* SLIDING_ / LOCAL_WINDOW: W >= 1; else ignored  */
   const int32_t* doc_id; /* DOCUMENT: device int32 [doc_len], indexed by
                             both q_idx and kv_idx; must outlive every use of
                             a block mask built from it. NULL otherwise.    */

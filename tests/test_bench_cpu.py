@@ -18,6 +18,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
                                          ("sliding_window", 5),
                                          ("sliding_window", 1),
                                          ("sliding_window", 400),
+                                         ("local_window", 1),
+                                         ("local_window", 6),
+                                         ("local_window", 300),
                                          ("document", None)])
 @pytest.mark.parametrize("ql,kl", [(37, 37), (50, 23), (23, 50)])
 def test_allowed_pairs_matches_dense_mask(mask, window, ql, kl):

@@ -55,7 +55,7 @@ SMALL = []
 for dtype, D, blk in (("bf16", 128, 128), ("bf16", 64, 128),
                       ("bf16", 128, 64), ("bf16", 64, 64), ("fp32", 64, 64),
                       ("fp32", 128, 128)):
-    for mask in ("causal", "sliding_window", "document", "none"):
+    for mask in ("causal", "sliding_window", "document", "none", "local_window"):
         for score in ("none", "softcap", "alibi"):
             SMALL.append((dtype, D, blk, mask, score))
 
@@ -66,7 +66,7 @@ def test_small_full_rows(dtype, D, blk, mask, score):
     # grouped heads
     ql, kl = 3 * blk + 37, 2 * blk + 101
     w = WL.Workload("small", dtype, 2, 4, 2, ql, kl, D, mask, blk, blk,
-                    seed=0, window=blk + 13 if mask == "sliding_window" else None,
+                    seed=0, window=blk + 13 if "window" in mask else None,
                     score=score, softcap=3.0 if score == "softcap" else None)
     rng = np.random.default_rng(zlib.crc32(f"{dtype}{D}{blk}{mask}{score}".encode()))
     doc = (np.sort(rng.integers(0, 4, max(ql, kl))).astype(np.int32)
@@ -83,7 +83,7 @@ def test_small_full_rows(dtype, D, blk, mask, score):
 PAIRS = []
 for D in (128, 64):
     for bq, bk in ((128, 64), (64, 128)):
-        for mask in ("causal", "sliding_window", "document", "none"):
+        for mask in ("causal", "sliding_window", "document", "none", "local_window"):
             for score in ("none", "alibi"):
                 PAIRS.append((D, bq, bk, mask, score))
 
@@ -95,7 +95,7 @@ def test_small_block_size_pairs(D, bq, bk, mask, score):
     # and through split-KV
     ql, kl = 3 * bq + 29, 3 * bk + 77
     w = WL.Workload("small", "bf16", 2, 2, 2, ql, kl, D, mask, bq, bk, seed=0,
-                    window=bk + 21 if mask == "sliding_window" else None,
+                    window=bk + 21 if "window" in mask else None,
                     score=score)
     rng = np.random.default_rng(zlib.crc32(f"pair{D}{bq}{bk}{mask}{score}".encode()))
     doc = (np.sort(rng.integers(0, 3, max(ql, kl))).astype(np.int32)
@@ -116,7 +116,7 @@ def test_small_block_size_pairs(D, bq, bk, mask, score):
 
 SPLIT_SMALL = []
 for D, blk in ((128, 128), (64, 128), (128, 64), (64, 64)):
-    for mask in ("causal", "sliding_window", "document", "none"):
+    for mask in ("causal", "sliding_window", "document", "none", "local_window"):
         for score in ("none", "softcap", "alibi"):
             SPLIT_SMALL.append((D, blk, mask, score))
 
@@ -127,7 +127,7 @@ def test_small_split_rows(D, blk, mask, score):
     # parts than key blocks), merged; every row against the oracle
     ql, kl = 3 * blk + 37, 4 * blk + 101
     w = WL.Workload("small", "bf16", 2, 4, 2, ql, kl, D, mask, blk, blk,
-                    seed=0, window=blk + 13 if mask == "sliding_window" else None,
+                    seed=0, window=blk + 13 if "window" in mask else None,
                     score=score, softcap=3.0 if score == "softcap" else None)
     rng = np.random.default_rng(zlib.crc32(f"split{D}{blk}{mask}{score}".encode()))
     doc = (np.sort(rng.integers(0, 4, max(ql, kl))).astype(np.int32)
@@ -244,11 +244,12 @@ def test_window_one_copies_values(dtype, D, blk, score):
     assert np.abs(lse.cpu().double().numpy() - l_ref).max() <= TOL[dtype]
 
 
-@pytest.mark.parametrize("mask", ["causal", "sliding_window", "document"])
+@pytest.mark.parametrize("mask", ["causal", "sliding_window", "document",
+                                  "local_window"])
 def test_uniform_keys_give_log_counts(mask):
     # K = 0, no score_mod: LSE_i = ln(number of allowed keys)
     w = WL.Workload("k0", "bf16", 1, 2, 2, 600, 600, 128, mask, 128, 128,
-                    seed=0, window=150 if mask == "sliding_window" else None)
+                    seed=0, window=150 if "window" in mask else None)
     q, k, v = _inputs(w, 4)
     k = torch.zeros_like(k)
     doc = np.repeat(np.arange(3, dtype=np.int32), [100, 333, 167]) \

@@ -118,7 +118,7 @@ def test_block_mask_reuse_and_stream_order():
 
 
 @pytest.mark.parametrize("kind", ["causal", "sliding_window", "document",
-                                  "none"])
+                                  "none", "local_window"])
 def test_block_mask_maximum_sizes(kind):
     # the largest key-block count a row may have (32768: one key per block)
     # and the largest block size (1024), with ragged tails
@@ -127,7 +127,7 @@ def test_block_mask_maximum_sizes(kind):
                              (1024, 32768, 1024, 1)):
         doc = (np.sort(rng.integers(0, 5, size=max(ql, kl))).astype(np.int32)
                if kind == "document" else None)
-        W = 700 if kind == "sliding_window" else None
+        W = 700 if "window" in kind else None
         label = f"{kind} ql={ql} kl={kl} bm={bm_} bn={bn_}"
         print(f"[block mask max] {label}", flush=True)
         got = gpu_mask(kind, 1, 1, ql, kl, bm_, bn_, W, doc)
