@@ -67,7 +67,7 @@ typedef enum fa_dtype { FA_BF16 = 0, FA_FP32 = 1 } fa_dtype;
  *   DOCUMENT        q_idx >= kv_idx and doc_id[q_idx] == doc_id[kv_idx]
  *                   (how-to, "Mask 3: document-packed")
  *   LOCAL_WINDOW    |q_idx - kv_idx| < window: the symmetric local window,
- *                   a bound on the absolute distance (crackedaicode
+ *                   limiting |i - j| instead of i - j (crackedaicode
  *                   "Sliding-Window Self-Attention", "State the boundary
  *                   precisely")
  * None of them depends on the batch or head index. */

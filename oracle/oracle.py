@@ -21,9 +21,9 @@ What is computed, and where the pages fix it
     section "State the boundary precisely");
   - document, causal and ``doc[q_idx] == doc[kv_idx]`` with one int32 id
     array indexed by both positions (how-to, "Mask 3: document-packed");
-  - local window, ``|q_idx - kv_idx| < W``: the symmetric window, a bound
-    on the absolute distance that the crackedaicode page names as the
-    alternative to the causal window (same section);
+  - local window, ``|q_idx - kv_idx| < W``: the symmetric variant, which the
+    crackedaicode page mentions in passing as limiting |i - j| rather than
+    i - j (same section);
   - none: every pair allowed (how-to, "The two hooks": either hook may be
     omitted).
 
@@ -108,7 +108,7 @@ def mask_mod(kind: str, q_idx, kv_idx, window=None, doc_id=None):
         d = i - j
         return (d >= 0) & (d < int(window))
     if kind == "local_window":
-        # symmetric local window: a bound on the absolute distance
+        # symmetric local window: |i - j| limited instead of i - j
         # (crackedaicode "Sliding-Window Self-Attention", "State the
         # boundary precisely", last paragraph)
         if window is None or int(window) < 1:

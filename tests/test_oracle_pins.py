@@ -85,8 +85,8 @@ def test_sliding_window_special_cases(T):
 
 @pytest.mark.parametrize("T", [1, 2, 6, 17])
 def test_local_window_is_the_symmetric_bound(T):
-    # crackedaicode "State the boundary precisely": a symmetric local window
-    # bounds the absolute distance. For square masks it is the causal
+    # crackedaicode "State the boundary precisely": the symmetric variant
+    # limits |i - j|. For square masks it is the causal
     # window together with its transpose, W = 1 is the identity, and W >= T
     # allows every pair.
     for W in (1, 2, 3, T, T + 4):
