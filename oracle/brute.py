@@ -46,6 +46,9 @@ def attention(q, k, v, mask="none", score="none", scale=None, window=None,
         scale = 1.0 / math.sqrt(D)
     O, L = [], []
     for b in range(B):
+        # doc: one id list for every batch entry, or a list of lists (one
+        # per entry)
+        doc_b = doc[b] if doc is not None and isinstance(doc[0], list) else doc
         Ob, Lb = [], []
         for h in range(H):
             hk = h // (H // Hk)
@@ -53,7 +56,7 @@ def attention(q, k, v, mask="none", score="none", scale=None, window=None,
             for i in range(len(q[b][h])):
                 live = []
                 for j in range(len(k[b][hk])):
-                    if not allowed(mask, i, j, window, doc):
+                    if not allowed(mask, i, j, window, doc_b):
                         continue
                     dot = 0.0
                     for d in range(D):

@@ -21,6 +21,8 @@ What is computed, and where the pages fix it
     section "State the boundary precisely");
   - document, causal and ``doc[q_idx] == doc[kv_idx]`` with one int32 id
     array indexed by both positions (how-to, "Mask 3: document-packed");
+    a batch of packed sequences may give each entry b its own array
+    ``doc[b]`` (mask_mod receives b, tensorplay page, parameter mask_mod);
   - local window, ``|q_idx - kv_idx| < W``: the symmetric variant, which the
     crackedaicode page mentions in passing as limiting |i - j| rather than
     i - j (same section);
@@ -190,11 +192,29 @@ def create_block_mask(kind, B, H, q_len, kv_len, block_m, block_n=None,
     """Block mask arrays as int32 numpy arrays.
 
     ``B``/``H`` of 1 broadcast one mask over every batch entry / head
-    (``B=None, H=None`` on the how-to's "Mask 1: causal"). Returns a dict
+    (``B=None, H=None`` on the how-to's "Mask 1: causal"). A 2-D ``doc_id``
+    ``[B, L]`` gives each batch entry its own document ids (mask_mod takes the
+    batch index, tensorplay page, parameter ``mask_mod``). Returns a dict
     with ``kv_num_blocks [B,H,NQB]``, ``kv_indices [B,H,NQB,NKVB]`` and,
     when ``separate_full_blocks``, ``full_kv_num_blocks`` and
     ``full_kv_indices`` of the same shapes (else ``None``)."""
     block_n = block_m if block_n is None else block_n
+    if doc_id is not None and np.ndim(doc_id) == 2:
+        # one id array per batch entry: the mask depends on b, so each entry
+        # gets its own rows (no broadcast over the batch)
+        if np.shape(doc_id)[0] != B:
+            raise ValueError("per-batch doc_id needs one row per batch entry")
+        parts = [create_block_mask(kind, 1, H, q_len, kv_len, block_m, block_n,
+                                   window=window, doc_id=np.asarray(doc_id)[b],
+                                   separate_full_blocks=separate_full_blocks)
+                 for b in range(B)]
+        out = {key: (None if parts[0][key] is None
+                     else np.concatenate([pt[key] for pt in parts], axis=0))
+               for key in ("kv_num_blocks", "kv_indices", "full_kv_num_blocks",
+                           "full_kv_indices")}
+        out["num_q_blocks"] = parts[0]["num_q_blocks"]
+        out["num_kv_blocks"] = parts[0]["num_kv_blocks"]
+        return out
     st = block_states(kind, q_len, kv_len, block_m, block_n, window, doc_id)
     if separate_full_blocks:
         num, idx = _lists(st == PARTIAL)
@@ -222,7 +242,8 @@ def attention(q, k, v, mask="none", score="none", scale=None, window=None,
     """Dense masked softmax attention in fp64.
 
     ``q [B,H,Q,D]``, ``k``/``v [B,H_kv,KV,D]`` (H a multiple of H_kv; query
-    head h reads key head ``h // (H // H_kv)``). ``rows``: optional query
+    head h reads key head ``h // (H // H_kv)``). ``doc_id``: ``[L]`` shared
+    by every batch entry, or ``[B, L]`` per entry. ``rows``: optional query
     positions to evaluate (all by default). Returns
     ``O [B,H,len(rows),D]`` and ``LSE [B,H,len(rows)]`` in fp64."""
     q = _as_f64(q)
@@ -241,6 +262,8 @@ def attention(q, k, v, mask="none", score="none", scale=None, window=None,
     cols = np.arange(kv_len)
     step = max(1, chunk_bytes // (8 * max(kv_len, 1)))
     for b in range(B):
+        doc_b = (np.asarray(doc_id)[b]
+                 if doc_id is not None and np.ndim(doc_id) == 2 else doc_id)
         for h in range(H):
             kb = k[b, h // group]
             vb = v[b, h // group]
@@ -250,7 +273,7 @@ def attention(q, k, v, mask="none", score="none", scale=None, window=None,
                 s = score_mod(score, s, h, H, ri[:, None], cols[None, :],
                               softcap=softcap)
                 allowed = mask_mod(mask, ri[:, None], cols[None, :],
-                                   window=window, doc_id=doc_id)
+                                   window=window, doc_id=doc_b)
                 t = np.where(allowed, s, -np.inf)
                 live = allowed.any(axis=1)
                 mx = np.where(live, t.max(axis=1, initial=-np.inf), 0.0)

@@ -291,6 +291,43 @@ def test_attention_matches_brute_force(seed, mask, score):
     np.testing.assert_allclose(l, np.array(bl), rtol=0, atol=1e-12)
 
 
+def test_per_batch_document_ids():
+    # a batch of packed sequences: entry b uses its own ids. Brute force
+    # (independent loops) agrees, each entry equals the shared-id
+    # computation on its ids, and an entry that is one document is causal.
+    rng = np.random.default_rng(77)
+    B, H, T, D = 3, 2, 13, 4
+    q = _rand(rng, B, H, T, D)
+    k = _rand(rng, B, H, T, D)
+    v = _rand(rng, B, H, T, D)
+    doc = np.stack([np.sort(rng.integers(0, 3, T)),
+                    np.sort(rng.integers(0, 5, T)),
+                    np.zeros(T, dtype=np.int64)]).astype(np.int32)
+    o, l = O.attention(q, k, v, mask="document", doc_id=doc)
+    bo, bl = brute.attention(_nested(q), _nested(k), _nested(v),
+                             mask="document", doc=doc.tolist())
+    np.testing.assert_allclose(o, np.array(bo), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l, np.array(bl), rtol=0, atol=1e-12)
+    for b in range(B):
+        ob, lb = O.attention(q[b:b + 1], k[b:b + 1], v[b:b + 1],
+                             mask="document", doc_id=doc[b])
+        assert np.array_equal(o[b:b + 1], ob) and np.array_equal(l[b:b + 1], lb)
+    oc, lc = O.attention(q[2:], k[2:], v[2:], mask="causal")
+    np.testing.assert_allclose(o[2:], oc, rtol=0, atol=1e-14)
+    # block masks: one set of rows per entry, each the entry's own mask
+    bm = O.create_block_mask("document", B, H, T, T, 4, 4, doc_id=doc)
+    assert bm["kv_num_blocks"].shape == (B, H, 4)
+    for b in range(B):
+        one = O.create_block_mask("document", 1, H, T, T, 4, 4, doc_id=doc[b])
+        for key in ("kv_num_blocks", "kv_indices", "full_kv_num_blocks",
+                    "full_kv_indices"):
+            assert np.array_equal(bm[key][b], one[key][0])
+        num, idx, fnum, fidx = brute.block_lists("document", T, T, 4, 4,
+                                                 doc=doc[b].tolist())
+        assert bm["kv_num_blocks"][b, 0].tolist() == num
+        assert bm["full_kv_indices"][b, 1].tolist() == fidx
+
+
 def test_attention_rectangular_and_row_subset():
     rng = np.random.default_rng(5)
     q = _rand(rng, 1, 2, 9, 4)
