@@ -40,14 +40,15 @@ FA_SCORE_ALIBI = 2
 # largest num_splits of fa_flex_attention_fwd_split
 FA_MAX_SPLITS = 64
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 class fa_mask_mod(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32),
                 ("window", ctypes.c_int32),
                 ("doc_id", ctypes.c_void_p),
-                ("doc_len", ctypes.c_int64)]
+                ("doc_len", ctypes.c_int64),
+                ("doc_stride", ctypes.c_int64)]
 
 
 class fa_score_mod(ctypes.Structure):

@@ -39,17 +39,24 @@ FlexAttnError = C.FlexAttnError
 # ------------------------------------------------------------------ mods
 @dataclasses.dataclass(frozen=True)
 class MaskMod:
-    """A built-in mask_mod. ``doc_id`` is an int32 tensor on the device."""
+    """A built-in mask_mod. ``doc_id`` is an int32 tensor on the device:
+    ``[L]`` shared by every batch entry, or ``[B, L]`` with one row per
+    entry (a batch of packed sequences)."""
     kind: int
     window: int = 0
     doc_id: Optional[torch.Tensor] = None
+
+    @property
+    def per_batch(self) -> bool:
+        return self.doc_id is not None and self.doc_id.dim() == 2
 
     def to_c(self) -> C.fa_mask_mod:
         doc = self.doc_id
         return C.fa_mask_mod(
             kind=self.kind, window=int(self.window),
             doc_id=doc.data_ptr() if doc is not None else None,
-            doc_len=doc.numel() if doc is not None else 0)
+            doc_len=doc.shape[-1] if doc is not None else 0,
+            doc_stride=doc.stride(0) if self.per_batch else 0)
 
 
 def causal() -> MaskMod:
@@ -66,8 +73,10 @@ def local_window(window: int) -> MaskMod:
 
 
 def document(doc_id: torch.Tensor) -> MaskMod:
-    if doc_id.dtype != torch.int32 or doc_id.dim() != 1:
-        raise ValueError("doc_id must be a 1-D int32 tensor")
+    """Document mask: ``doc_id`` int32 ``[L]`` (one packed sequence layout
+    for every batch entry) or ``[B, L]`` (one per entry)."""
+    if doc_id.dtype != torch.int32 or doc_id.dim() not in (1, 2):
+        raise ValueError("doc_id must be a 1-D or 2-D int32 tensor")
     return MaskMod(C.FA_MASK_DOCUMENT, doc_id=doc_id.contiguous())
 
 
@@ -273,9 +282,10 @@ def create_block_mask(mask_mod, B: Optional[int], H: Optional[int],
                       doc_id=None) -> BlockMask:
     """Build a block mask on the device (one call of fa_create_block_mask).
 
-    ``mask_mod``: a :class:`MaskMod` or one of "causal", "sliding_window"
-    (with ``window``), "document" (with ``doc_id``), "none". ``B``/``H``
-    None broadcast the mask over every batch entry / head."""
+    ``mask_mod``: a :class:`MaskMod` or one of "causal", "sliding_window" /
+    "local_window" (with ``window``), "document" (with ``doc_id``, ``[L]`` or
+    per batch entry ``[B, L]``), "none". ``B``/``H`` None broadcast the mask
+    over every batch entry / head."""
     mask = _mask_from(mask_mod, window, doc_id)
     device = torch.device(device)
     if device.type != "cuda":
@@ -284,6 +294,10 @@ def create_block_mask(mask_mod, B: Optional[int], H: Optional[int],
                 else BLOCK_SIZE)
     Bm = 1 if B is None else int(B)
     Hm = 1 if H is None else int(H)
+    if mask.kind == C.FA_MASK_DOCUMENT and mask.per_batch and \
+            mask.doc_id.shape[0] != Bm:
+        raise ValueError("per-batch doc_id [B, L] needs B = its first "
+                         "dimension (the mask depends on the batch entry)")
     nqb, nkvb = fa_block_mask_dims(Q_LEN, KV_LEN, bm_, bn_)
     opts = dict(dtype=torch.int32, device=device)
     num = torch.empty((Bm, Hm, nqb), **opts)

@@ -83,10 +83,9 @@ __device__ __forceinline__ unsigned char classify_closed(const BlockMaskLaunch& 
 // Document mask, one wavefront per tile. `qdoc` holds the query block's
 // document ids in LDS; `qsingle` is the id when the whole query block is one
 // document, else INT_MIN.
-__device__ unsigned char classify_document(const BlockMaskLaunch& p, int m, int n,
-                                           const int* qdoc, int qsingle, int lane) {
+__device__ unsigned char classify_document(const BlockMaskLaunch& p, const int* doc, int m,
+                                           int n, const int* qdoc, int qsingle, int lane) {
   const Tile t = make_tile(p, m, n);
-  const int* doc = p.mask.doc_id;
   const int cols = t.j_hi - t.j_lo + 1;
   const int rows = t.i_hi - t.i_lo + 1;
   // is the key block a single document c?
@@ -165,14 +164,17 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(BlockMaskLaunch p)
   if (p.mask.kind == FA_MASK_DOCUMENT) {
     const int i_lo = m * p.block_m;
     const int rows = min(i_lo + p.block_m, p.q_len) - i_lo;
-    for (int r = threadIdx.x; r < rows; r += kThreads) qdoc[r] = p.mask.doc_id[i_lo + r];
+    // this row's batch entry (rows are (b, h, m) flattened) and its ids
+    const int b = row / (p.Hm * p.nqb);
+    const int* doc = p.mask.doc_id + static_cast<int64_t>(b) * p.mask.doc_stride;
+    for (int r = threadIdx.x; r < rows; r += kThreads) qdoc[r] = doc[i_lo + r];
     __syncthreads();
     const int first = qdoc[0];
     bool other = false;
     for (int r = threadIdx.x; r < rows; r += kThreads) other |= qdoc[r] != first;
     const int qsingle = __syncthreads_or(other) ? INT_MIN : first;
     for (int n = wave; n < nkvb; n += kWaves) {
-      const unsigned char s = classify_document(p, m, n, qdoc, qsingle, lane);
+      const unsigned char s = classify_document(p, doc, m, n, qdoc, qsingle, lane);
       if (lane == 0) states[n] = s;
     }
   } else {

@@ -143,7 +143,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
   const int kv_len = p.kv_len;
   const int mkind = p.mask.kind;
   const int window = p.mask.window;
-  const int* doc = p.mask.doc_id;
+  // document ids of this batch entry (one shared array when the stride is 0)
+  const int* doc = p.mask.doc_id + static_cast<int64_t>(w.b) * p.mask.doc_stride;
   const bool doc_mask = mkind == FA_MASK_DOCUMENT;
 
   const __bf16* qp = static_cast<const __bf16*>(p.q) + w.b * p.qs[0] + w.h * p.qs[1];
@@ -253,11 +254,18 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
     const int it = st / SPB;
     if (n < 0) return;
     const int j0 = n * BK + (SPB - 1 - st % SPB) * kStageKeys;
-    const int rows_left = kv_len - j0;  // >= 1
-    const int krec = (rows_left - 1) * static_cast<int>(kstride) + RB;
-    const int vrec = (rows_left - 1) * static_cast<int>(vstride) + RB;
-    const hw::i32x4 kr = hw::make_rsrc(kbase + j0 * kstride, rows_left >= kStageKeys ? 0x7fffffff : krec);
-    const hw::i32x4 vr = hw::make_rsrc(vbase + j0 * vstride, rows_left >= kStageKeys ? 0x7fffffff : vrec);
+    // Rows of the stage inside the sequence. A stage of the last, ragged
+    // key block may lie wholly past the end (its later keys come first):
+    // then the buffers have size 0 and the tiles arrive as zeros.
+    const int rows_left = kv_len - j0;
+    const int krec = rows_left >= kStageKeys ? 0x7fffffff
+                     : rows_left <= 0       ? 0
+                                            : (rows_left - 1) * static_cast<int>(kstride) + RB;
+    const int vrec = rows_left >= kStageKeys ? 0x7fffffff
+                     : rows_left <= 0       ? 0
+                                            : (rows_left - 1) * static_cast<int>(vstride) + RB;
+    const hw::i32x4 kr = hw::make_rsrc(kbase + (rows_left > 0 ? j0 * kstride : 0), krec);
+    const hw::i32x4 vr = hw::make_rsrc(vbase + (rows_left > 0 ? j0 * vstride : 0), vrec);
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
       const int seg = (rd * NW + wave) * 1024;

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(BLK * 2) void fwd_fp32_kernel(const FwdLaunch p) {
   const int kv_len = p.kv_len;
   const int mkind = p.mask.kind;
   const int window = p.mask.window;
-  const int* doc = p.mask.doc_id;
+  const int* doc = p.mask.doc_id + static_cast<int64_t>(w.b) * p.mask.doc_stride;
 
   const float* qp = static_cast<const float*>(p.q) + w.b * p.qs[0] + w.h * p.qs[1];
   const float* kp = static_cast<const float*>(p.k) + w.b * p.ks[0] + hk * p.ks[1];

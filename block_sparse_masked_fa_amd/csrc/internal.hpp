@@ -9,8 +9,9 @@ namespace fa {
 
 struct MaskParams {
   int32_t kind;           // fa_mask_kind
-  int32_t window;         // sliding window W
+  int32_t window;         // sliding / local window W
   const int32_t* doc_id;  // device, document mask only
+  int64_t doc_stride;     // elements between batch entries' ids (0: shared)
 };
 
 struct BlockMaskLaunch {

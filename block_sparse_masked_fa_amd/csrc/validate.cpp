@@ -35,6 +35,8 @@ int check_mask_mod(const fa_mask_mod* mask, int32_t q_len, int32_t kv_len,
         return fail(msg, FA_ERR_SHAPE_MISMATCH,
                     "doc_len " + std::to_string(mask->doc_len) +
                         " < max(q_len, kv_len) = " + std::to_string(need));
+      if (mask->doc_stride < 0)
+        return fail(msg, FA_ERR_INVALID_VALUE, "doc_stride must be >= 0");
       return FA_OK;
     }
     default:
@@ -130,7 +132,8 @@ int check_create_block_mask(const fa_mask_mod* mask, int32_t B, int32_t H,
     bm->full_kv_num_blocks = nullptr;
     bm->full_kv_indices = nullptr;
   }
-  out->mask = MaskParams{mask->kind, mask->window, mask->doc_id};
+  out->mask = MaskParams{mask->kind, mask->window, mask->doc_id,
+                         mask->kind == FA_MASK_DOCUMENT ? mask->doc_stride : 0};
   out->Bm = B;
   out->Hm = H;
   out->q_len = q_len;
@@ -182,6 +185,10 @@ int check_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H, int32_t H_kv,
       bm->B < 1 || bm->H < 1)
     return fail(msg, FA_ERR_SHAPE_MISMATCH,
                 "block mask batch/head dims must be 1 or equal to B/H");
+  if (bm->mask.kind == FA_MASK_DOCUMENT && bm->mask.doc_stride != 0 && bm->B != B)
+    return fail(msg, FA_ERR_SHAPE_MISMATCH,
+                "per-batch document ids: the block mask must be built for B = " +
+                    std::to_string(B) + " (it depends on the batch entry)");
   int32_t nqb = 0, nkvb = 0;
   st = check_block_mask_dims(q_len, kv_len, bm->block_m, bm->block_n, &nqb,
                              &nkvb, msg);
@@ -251,7 +258,8 @@ int check_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H, int32_t H_kv,
     out->vs[d] = kv_len > 0 ? v_stride[d] : 0;
   }
   out->scale = scale;
-  out->mask = MaskParams{bm->mask.kind, bm->mask.window, bm->mask.doc_id};
+  out->mask = MaskParams{bm->mask.kind, bm->mask.window, bm->mask.doc_id,
+                         bm->mask.kind == FA_MASK_DOCUMENT ? bm->mask.doc_stride : 0};
   out->Bm = bm->B;
   out->Hm = bm->H;
   out->block_m = bm->block_m;

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -98,6 +98,12 @@ typedef struct fa_mask_mod {
                             both q_idx and kv_idx; must outlive every use of
                             a block mask built from it. NULL otherwise.    */
   int64_t doc_len;       /* DOCUMENT: >= max(q_len, kv_len)                */
+  int64_t doc_stride;    /* DOCUMENT: elements between the id arrays of
+                            consecutive batch entries (a batch of packed
+                            sequences: entry b reads doc_id + b * doc_stride);
+                            0 = one array for every entry. With a stride the
+                            mask depends on b: block masks are built with the
+                            batch count (no broadcast over B).           */
 } fa_mask_mod;
 
 typedef struct fa_score_mod {

@@ -64,8 +64,8 @@ def test_struct_layout_matches_c(tmp_path):
 #include <stddef.h>
 #include "{HEADER}"
 int main(void) {{
-  printf("%zu %zu %zu\\n", sizeof(fa_mask_mod), offsetof(fa_mask_mod, doc_id),
-         offsetof(fa_mask_mod, doc_len));
+  printf("%zu %zu %zu %zu\\n", sizeof(fa_mask_mod), offsetof(fa_mask_mod, doc_id),
+         offsetof(fa_mask_mod, doc_len), offsetof(fa_mask_mod, doc_stride));
   printf("%zu %zu\\n", sizeof(fa_score_mod), offsetof(fa_score_mod, softcap));
   printf("%zu %zu %zu %zu %zu\\n", sizeof(fa_block_mask),
          offsetof(fa_block_mask, B), offsetof(fa_block_mask, separate_full_blocks),
@@ -81,7 +81,8 @@ int main(void) {{
                            check=True).stdout.split("\n")
     got = [list(map(int, l.split())) for l in lines if l.strip()]
     assert got[0] == [ctypes.sizeof(C.fa_mask_mod), C.fa_mask_mod.doc_id.offset,
-                      C.fa_mask_mod.doc_len.offset]
+                      C.fa_mask_mod.doc_len.offset,
+                      C.fa_mask_mod.doc_stride.offset]
     assert got[1] == [ctypes.sizeof(C.fa_score_mod),
                       C.fa_score_mod.softcap.offset]
     assert got[2] == [ctypes.sizeof(C.fa_block_mask), C.fa_block_mask.B.offset,
@@ -139,6 +140,11 @@ def _bm(**kw):
      C.FA_ERR_NULL_POINTER),
     (C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT, doc_id=FAKE, doc_len=63), 1, 1,
      64, 64, 64, 64, C.FA_ERR_SHAPE_MISMATCH),
+    (C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT, doc_id=FAKE, doc_len=64,
+                   doc_stride=-64), 2, 1, 64, 64, 64, 64,
+     C.FA_ERR_INVALID_VALUE),
+    (C.fa_mask_mod(kind=C.FA_MASK_LOCAL_WINDOW, window=0), 1, 1, 64, 64,
+     64, 64, C.FA_ERR_INVALID_VALUE),
     (C.fa_mask_mod(kind=7), 1, 1, 64, 64, 64, 64, C.FA_ERR_INVALID_VALUE),
     (C.fa_mask_mod(kind=C.FA_MASK_CAUSAL), 0, 1, 64, 64, 64, 64,
      C.FA_ERR_INVALID_VALUE),
@@ -245,6 +251,19 @@ def test_fwd_refuses(over, status):
         return
     st = _fwd(**over)
     assert st == status, C.lib().fa_last_error()
+
+
+@needs_lib
+def test_fwd_refuses_broadcast_of_per_batch_document_mask():
+    bm = _good_bm()
+    bm.mask = C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT, doc_id=FAKE, doc_len=256,
+                            doc_stride=256)
+    assert _fwd(bm=bm) == C.FA_ERR_SHAPE_MISMATCH       # bm.B = 1, call B = 2
+    bm.mask.doc_stride = 0
+    bm2 = _good_bm(B=2)
+    bm2.mask = C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT, doc_id=FAKE, doc_len=255,
+                             doc_stride=256)
+    assert _fwd(bm=bm2) == C.FA_ERR_SHAPE_MISMATCH      # doc_len < q_len
 
 
 @needs_lib

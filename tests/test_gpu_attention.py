@@ -142,6 +142,59 @@ def test_small_split_rows(D, blk, mask, score):
                      f"split {ns} D={D} blk={blk} {mask} {score}")
 
 
+@pytest.mark.parametrize("dtype,D,blk", [("bf16", 128, 128), ("bf16", 64, 64),
+                                         ("fp32", 64, 64)])
+def test_per_batch_document_ids(dtype, D, blk):
+    # a batch of packed sequences with a different packing per entry
+    # (doc_id [B, L]); every row against the oracle, whole and split
+    B, H, T = 3, 2, 3 * blk + 45
+    w = WL.Workload("small", dtype, B, H, H, T, T, D, "document", blk, blk,
+                    seed=0)
+    rng = np.random.default_rng(D + blk)
+    doc = np.stack([np.sort(rng.integers(0, n, T)) for n in (3, 6, 1)]
+                   ).astype(np.int32)
+    q, k, v = _inputs(w, 41)
+    o_ref, l_ref = oracle_case(q, k, v, w, doc)
+    bm = fa.create_block_mask("document", B, None, T, T, device=DEV,
+                              BLOCK_SIZE=blk,
+                              doc_id=torch.from_numpy(doc).to(DEV))
+    for ns in ((1, 4) if dtype == "bf16" else (1,)):
+        print(f"[fwd per-batch docs] {dtype} D={D} blk={blk} splits={ns}",
+              flush=True)
+        o, lse = run_gpu(w, q, k, v, doc, bm=bm, num_splits=ns)
+        assert_close(o, lse, o_ref, l_ref, TOL[dtype],
+                     f"per-batch docs {dtype} D={D} split {ns}")
+
+
+@pytest.mark.parametrize("D,bq,bk", [(128, 128, 128), (64, 128, 64),
+                                     (128, 64, 128), (64, 64, 64)])
+@pytest.mark.parametrize("mask", ["causal", "none", "local_window"])
+def test_keys_past_the_sequence_end_are_never_used(D, bq, bk, mask):
+    # K and V are views into buffers whose rows after KV_LEN hold NaN: any
+    # read of a key past the end (the last key block is ragged, and its
+    # later stage lies wholly past the end) would poison the output
+    ql, kl = 300, 300 if bk == 128 else 290
+    w = WL.Workload("tail", "bf16", 1, 2, 2, ql, kl, D, mask, bq, bk, seed=0,
+                    window=70 if mask == "local_window" else None)
+    q, k, v = _inputs(w, 53)
+    o_ref, l_ref = oracle_case(q, k, v, w, None)
+    pad = 512
+    kp = torch.full((1, 2, pad, D), float("nan"), dtype=torch.bfloat16)
+    vp = torch.full((1, 2, pad, D), float("nan"), dtype=torch.bfloat16)
+    kp[:, :, :kl] = k
+    vp[:, :, :kl] = v
+    kd, vd = kp.to(DEV)[:, :, :kl], vp.to(DEV)[:, :, :kl]
+    bm = fa.create_block_mask(mask, None, None, ql, kl, device=DEV,
+                              BLOCK_SIZE=(bq, bk), window=w.window)
+    for ns in (1, 3):
+        print(f"[fwd tail] D={D} ({bq},{bk}) {mask} splits={ns}", flush=True)
+        o, lse = fa.flex_attention(q.to(DEV), kd, vd, bm, scale=w.scale,
+                                   num_splits=ns)
+        torch.cuda.synchronize()
+        assert_close(o, lse, o_ref, l_ref, TOL["bf16"],
+                     f"tail D={D} ({bq},{bk}) {mask} split {ns}")
+
+
 def test_split_extremes():
     # the largest part count, and a single key block per row
     w = WL.Workload("small", "bf16", 1, 2, 2, 300, 300, 64, "causal", 128,

@@ -145,3 +145,22 @@ def test_block_mask_limits_refused():
     with pytest.raises(fa.FlexAttnError):
         fa.create_block_mask("causal", 1, 1, 2048, 2048, device=DEV,
                              BLOCK_SIZE=2048)
+
+
+def test_block_mask_per_batch_document_ids():
+    # a batch of packed sequences: each entry's own ids, one set of rows per
+    # entry, bit-exact against the oracle
+    rng = np.random.default_rng(19)
+    for ql, kl, bm_, bn_ in ((700, 700, 64, 64), (1000, 600, 128, 32)):
+        B, H = 3, 2
+        L = max(ql, kl)
+        doc = np.stack([np.sort(rng.integers(0, n, L)) for n in (2, 5, 1)]
+                       ).astype(np.int32)
+        label = f"per-batch docs ql={ql} kl={kl} bm={bm_} bn={bn_}"
+        print(f"[block mask] {label}", flush=True)
+        got = gpu_mask("document", B, H, ql, kl, bm_, bn_, doc=doc)
+        want = O.create_block_mask("document", B, H, ql, kl, bm_, bn_,
+                                   doc_id=doc)
+        assert_same(got, want, label)
+    with pytest.raises(ValueError):
+        gpu_mask("document", 1, 1, 700, 700, 64, 64, doc=doc)
