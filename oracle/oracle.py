@@ -285,3 +285,71 @@ def attention(q, k, v, mask="none", score="none", scale=None, window=None,
                 lse[b, h, r0:r0 + len(ri)] = np.where(
                     live, mx + np.log(safe), -np.inf)
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------
+def score_mod_grad(kind: str, s, softcap=None):
+    """d score_mod / d s at the scaled score ``s`` (fp64): 1 for the additive
+    mods, 1 - tanh(s / cap)**2 for the soft-cap (the derivative of
+    cap * tanh(s / cap))."""
+    if kind in ("none", "alibi"):
+        return np.ones_like(s)
+    if kind == "softcap":
+        return 1.0 - np.tanh(s / softcap) ** 2
+    raise ValueError(f"unknown score kind {kind!r}")
+
+
+def attention_backward(q, k, v, do, mask="none", score="none", scale=None,
+                       window=None, doc_id=None, softcap=None):
+    """Gradients (dQ, dK, dV) of ``O = attention(q, k, v, ...)`` for an
+    upstream gradient ``do`` of O (LSE treated as not differentiated), in
+    fp64, by the chain rule through the definition above:
+
+        t = scale * q . k;  s = score_mod(t);  P = softmax over A_i of s;
+        dV_j = sum_i P_ij dO_i;  dP_ij = dO_i . v_j;
+        dS_ij = P_ij (dP_ij - sum_j' P_ij' dP_ij');
+        dT = dS * score_mod'(t);  dQ_i = scale sum_j dT_ij k_j;
+        dK_j = scale sum_i dT_ij q_i.
+
+    Masked pairs have P = 0 and contribute nothing; a row with no allowed
+    key has P = 0 everywhere. With grouped heads, dK / dV of a key head sum
+    over the query heads that read it."""
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    do = _as_f64(do)
+    B, H, q_len, D = q.shape
+    H_kv, kv_len = k.shape[1], k.shape[2]
+    group = H // H_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    rows = np.arange(q_len)
+    cols = np.arange(kv_len)
+    for b in range(B):
+        doc_b = (np.asarray(doc_id)[b]
+                 if doc_id is not None and np.ndim(doc_id) == 2 else doc_id)
+        allowed = mask_mod(mask, rows[:, None], cols[None, :], window=window,
+                           doc_id=doc_b)
+        live = allowed.any(axis=1)
+        for h in range(H):
+            hk = h // group
+            t = scale * (q[b, h] @ k[b, hk].T)
+            s = score_mod(score, t, h, H, rows[:, None], cols[None, :],
+                          softcap=softcap)
+            z = np.where(allowed, s, -np.inf)
+            mx = np.where(live, z.max(axis=1, initial=-np.inf), 0.0)
+            w = np.exp(z - mx[:, None])
+            den = np.where(live, w.sum(axis=1), 1.0)
+            p = w / den[:, None]
+            dv[b, hk] += p.T @ do[b, h]
+            dp = do[b, h] @ v[b, hk].T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dt = ds * score_mod_grad(score, t, softcap=softcap)
+            dq[b, h] = scale * (dt @ k[b, hk])
+            dk[b, hk] += scale * (dt.T @ q[b, h])
+    return dq, dk, dv
