@@ -302,7 +302,7 @@ def score_mod_grad(kind: str, s, softcap=None):
 
 
 def attention_backward(q, k, v, do, mask="none", score="none", scale=None,
-                       window=None, doc_id=None, softcap=None):
+                       window=None, doc_id=None, softcap=None, rows=None):
     """Gradients (dQ, dK, dV) of ``O = attention(q, k, v, ...)`` for an
     upstream gradient ``do`` of O (LSE treated as not differentiated), in
     fp64, by the chain rule through the definition above:
@@ -315,7 +315,12 @@ def attention_backward(q, k, v, do, mask="none", score="none", scale=None,
 
     Masked pairs have P = 0 and contribute nothing; a row with no allowed
     key has P = 0 everywhere. With grouped heads, dK / dV of a key head sum
-    over the query heads that read it."""
+    over the query heads that read it.
+
+    ``rows``: optional query-row indices. Row i's dQ depends on row i alone
+    (its softmax, its dO), so then only those rows are evaluated and
+    ``(dQ [B,H,len(rows),D], None, None)`` is returned; dK and dV, sums
+    over every row, are not formed."""
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
@@ -325,10 +330,11 @@ def attention_backward(q, k, v, do, mask="none", score="none", scale=None,
     group = H // H_kv
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    dq = np.zeros_like(q)
+    only_rows = rows is not None
+    rows = np.arange(q_len) if rows is None else np.asarray(rows, np.int64)
+    dq = np.zeros((B, H, len(rows), D))
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    rows = np.arange(q_len)
     cols = np.arange(kv_len)
     for b in range(B):
         doc_b = (np.asarray(doc_id)[b]
@@ -338,7 +344,7 @@ def attention_backward(q, k, v, do, mask="none", score="none", scale=None,
         live = allowed.any(axis=1)
         for h in range(H):
             hk = h // group
-            t = scale * (q[b, h] @ k[b, hk].T)
+            t = scale * (q[b, h][rows] @ k[b, hk].T)
             s = score_mod(score, t, h, H, rows[:, None], cols[None, :],
                           softcap=softcap)
             z = np.where(allowed, s, -np.inf)
@@ -346,10 +352,13 @@ def attention_backward(q, k, v, do, mask="none", score="none", scale=None,
             w = np.exp(z - mx[:, None])
             den = np.where(live, w.sum(axis=1), 1.0)
             p = w / den[:, None]
-            dv[b, hk] += p.T @ do[b, h]
-            dp = do[b, h] @ v[b, hk].T
+            dp = do[b, h][rows] @ v[b, hk].T
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
             dt = ds * score_mod_grad(score, t, softcap=softcap)
             dq[b, h] = scale * (dt @ k[b, hk])
-            dk[b, hk] += scale * (dt.T @ q[b, h])
+            if not only_rows:
+                dv[b, hk] += p.T @ do[b, h]
+                dk[b, hk] += scale * (dt.T @ q[b, h])
+    if only_rows:
+        return dq, None, None
     return dq, dk, dv

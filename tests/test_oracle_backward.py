@@ -119,3 +119,21 @@ def test_backward_special_cases():
                                       mask="causal") for h in (2 * hk, 2 * hk + 1)]
         np.testing.assert_allclose(dv1[:, hk], parts[0][2][:, 0] + parts[1][2][:, 0],
                                    atol=1e-13)
+
+
+@pytest.mark.parametrize("mask", O.MASK_KINDS)
+@pytest.mark.parametrize("score", O.SCORE_KINDS)
+def test_backward_row_sample_matches_all_rows(mask, score):
+    # rows=: the sampled rows' dQ equals those rows of the full gradient
+    # (each row's dQ is a function of that row alone); unsorted, repeated
+    # and boundary rows
+    rng = np.random.default_rng(7)
+    q, k, v, do = _case(rng, B=2, H=4, Hk=2, T=11, D=5)
+    kw = _kw(mask, q.shape[2], rng)
+    full, _, _ = O.attention_backward(q, k, v, do, mask=mask, score=score,
+                                      softcap=1.7, **kw)
+    rows = np.array([10, 0, 3, 3, 7])
+    part, dk, dv = O.attention_backward(q, k, v, do, mask=mask, score=score,
+                                        softcap=1.7, rows=rows, **kw)
+    assert dk is None and dv is None
+    np.testing.assert_allclose(part, full[:, :, rows], rtol=1e-12, atol=1e-14)
