@@ -317,10 +317,11 @@ def attention_backward(q, k, v, do, mask="none", score="none", scale=None,
     key has P = 0 everywhere. With grouped heads, dK / dV of a key head sum
     over the query heads that read it.
 
-    ``rows``: optional query-row indices. Row i's dQ depends on row i alone
-    (its softmax, its dO), so then only those rows are evaluated and
-    ``(dQ [B,H,len(rows),D], None, None)`` is returned; dK and dV, sums
-    over every row, are not formed."""
+    ``rows``: optional distinct query-row indices. Row i's dQ depends on
+    row i alone (its softmax, its dO), so then only those rows are
+    evaluated: dQ is ``[B,H,len(rows),D]`` and dK, dV hold the sums over
+    those rows only, which are the full gradients of every key j whose
+    allowed rows all lie in ``rows``."""
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
@@ -330,8 +331,9 @@ def attention_backward(q, k, v, do, mask="none", score="none", scale=None,
     group = H // H_kv
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    only_rows = rows is not None
     rows = np.arange(q_len) if rows is None else np.asarray(rows, np.int64)
+    if len(np.unique(rows)) != len(rows):
+        raise ValueError("rows must be distinct")
     dq = np.zeros((B, H, len(rows), D))
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -356,9 +358,6 @@ def attention_backward(q, k, v, do, mask="none", score="none", scale=None,
             ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
             dt = ds * score_mod_grad(score, t, softcap=softcap)
             dq[b, h] = scale * (dt @ k[b, hk])
-            if not only_rows:
-                dv[b, hk] += p.T @ do[b, h]
-                dk[b, hk] += scale * (dt.T @ q[b, h])
-    if only_rows:
-        return dq, None, None
+            dv[b, hk] += p.T @ do[b, h][rows]
+            dk[b, hk] += scale * (dt.T @ q[b, h][rows])
     return dq, dk, dv

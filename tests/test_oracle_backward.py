@@ -125,15 +125,28 @@ def test_backward_special_cases():
 @pytest.mark.parametrize("score", O.SCORE_KINDS)
 def test_backward_row_sample_matches_all_rows(mask, score):
     # rows=: the sampled rows' dQ equals those rows of the full gradient
-    # (each row's dQ is a function of that row alone); unsorted, repeated
-    # and boundary rows
+    # (each row's dQ is a function of that row alone), and dK / dV of keys
+    # seen only by sampled rows equal the full gradients; unsorted and
+    # boundary rows
     rng = np.random.default_rng(7)
     q, k, v, do = _case(rng, B=2, H=4, Hk=2, T=11, D=5)
     kw = _kw(mask, q.shape[2], rng)
-    full, _, _ = O.attention_backward(q, k, v, do, mask=mask, score=score,
-                                      softcap=1.7, **kw)
-    rows = np.array([10, 0, 3, 3, 7])
-    part, dk, dv = O.attention_backward(q, k, v, do, mask=mask, score=score,
-                                        softcap=1.7, rows=rows, **kw)
-    assert dk is None and dv is None
-    np.testing.assert_allclose(part, full[:, :, rows], rtol=1e-12, atol=1e-14)
+    full = O.attention_backward(q, k, v, do, mask=mask, score=score,
+                                softcap=1.7, **kw)
+    rows = np.array([10, 0, 3, 7])
+    dq, _, _ = O.attention_backward(q, k, v, do, mask=mask, score=score,
+                                    softcap=1.7, rows=rows, **kw)
+    np.testing.assert_allclose(dq, full[0][:, :, rows], rtol=1e-12, atol=1e-14)
+    # the last three keys: every row allowed to see them is in `tail`
+    T = q.shape[2]
+    cols = np.arange(T - 3, T)
+    seen = O.mask_mod(mask, np.arange(T)[:, None], cols[None, :],
+                      window=kw.get("window"), doc_id=kw.get("doc_id")).any(axis=1)
+    tail = np.flatnonzero(seen)
+    part = O.attention_backward(q, k, v, do, mask=mask, score=score,
+                                softcap=1.7, rows=tail, **kw)
+    for g, r in zip(part[1:], full[1:]):
+        np.testing.assert_allclose(g[:, :, cols], r[:, :, cols], rtol=1e-12,
+                                   atol=1e-14)
+    with pytest.raises(ValueError):
+        O.attention_backward(q, k, v, do, rows=[1, 1])
