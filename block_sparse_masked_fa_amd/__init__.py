@@ -1,5 +1,5 @@
 """block_sparse_masked_fa_amd: FlexAttention-style block-sparse masked
-attention forward for MI355X (gfx950).
+attention (forward and backward) for MI355X (gfx950).
 
 The work runs in ``libflexattn.so`` (hand-written HIP kernels behind a C ABI,
 ``include/flexattn.h``); this package is its Python binding. Importing it
@@ -9,8 +9,10 @@ library has not been built (``python -m block_sparse_masked_fa_amd.build``).
 from .api import (  # noqa: F401
     BlockMask, FlexAttnError, MaskMod, ScoreMod, alibi, auto_num_splits,
     causal, create_block_mask, document, fa_block_mask_dims,
-    fa_create_block_mask, fa_flex_attention_fwd, fa_flex_attention_fwd_split,
-    fa_split_workspace_bytes, flex_attention, local_window, no_mask,
+    fa_bwd_workspace_bytes, fa_create_block_mask, fa_flex_attention_bwd,
+    fa_flex_attention_fwd, fa_flex_attention_fwd_split,
+    fa_split_workspace_bytes, flex_attention, flex_attention_backward,
+    local_window, no_mask,
     sliding_window,
     softcap,
 )

@@ -6,11 +6,13 @@ kernels. Two layers:
 
 * the raw entry points with the C names (``fa_block_mask_dims``,
   ``fa_create_block_mask``, ``fa_flex_attention_fwd``,
-  ``fa_flex_attention_fwd_split``, ``fa_split_workspace_bytes``), taking
+  ``fa_flex_attention_fwd_split``, ``fa_split_workspace_bytes``,
+  ``fa_flex_attention_bwd``, ``fa_bwd_workspace_bytes``), taking
   ctypes structs and integer device addresses;
 * a FlexAttention-style convenience layer: ``create_block_mask(...)`` returns
   a :class:`BlockMask` holding its index tensors, and
-  ``flex_attention(q, k, v, block_mask, score_mod)`` returns ``(O, LSE)``.
+  ``flex_attention(q, k, v, block_mask, score_mod)`` returns ``(O, LSE)``
+  and ``flex_attention_backward(...)`` returns ``(dQ, dK, dV)``.
   The shapes follow scaled_dot_product_attention: (B, H, S, D).
 """
 from __future__ import annotations
@@ -31,6 +33,8 @@ __all__ = [
     "flex_attention", "fa_block_mask_dims", "fa_create_block_mask",
     "fa_flex_attention_fwd", "fa_flex_attention_fwd_split",
     "fa_split_workspace_bytes", "auto_num_splits", "FlexAttnError",
+    "flex_attention_backward", "fa_flex_attention_bwd",
+    "fa_bwd_workspace_bytes",
 ]
 
 FlexAttnError = C.FlexAttnError
@@ -188,6 +192,31 @@ def fa_split_workspace_bytes(B: int, H: int, q_len: int, D: int,
     C.check(C.lib().fa_split_workspace_bytes(B, H, q_len, D, num_splits,
                                              ctypes.byref(n)),
             "fa_split_workspace_bytes")
+    return n.value
+
+
+def fa_flex_attention_bwd(dtype: int, B: int, H: int, H_kv: int, q_len: int,
+                          kv_len: int, D: int, q: int, q_stride, k: int,
+                          k_stride, v: int, v_stride, scale: float,
+                          bm: C.fa_block_mask, score: Optional[C.fa_score_mod],
+                          o: int, lse: int, dout: int,
+                          workspace: Optional[int], workspace_bytes: int,
+                          dq: int, dk: int, dv: int,
+                          stream: Optional[int]) -> int:
+    return C.lib().fa_flex_attention_bwd(
+        dtype, B, H, H_kv, q_len, kv_len, D,
+        q, C.Stride3(*q_stride), k, C.Stride3(*k_stride),
+        v, C.Stride3(*v_stride), scale, ctypes.byref(bm),
+        ctypes.byref(score) if score is not None else None, o, lse, dout,
+        workspace, workspace_bytes, dq, dk, dv, stream)
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, q_len: int,
+                           bm: C.fa_block_mask) -> int:
+    n = ctypes.c_uint64()
+    C.check(C.lib().fa_bwd_workspace_bytes(B, H, q_len, ctypes.byref(bm),
+                                           ctypes.byref(n)),
+            "fa_bwd_workspace_bytes")
     return n.value
 
 
@@ -391,3 +420,57 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             _stream_handle(q.device))
     C.check(st, "fa_flex_attention_fwd_split")
     return out, lse
+
+
+def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                            o: torch.Tensor, lse: torch.Tensor,
+                            dout: torch.Tensor, block_mask: BlockMask,
+                            score_mod=None, scale: Optional[float] = None):
+    """Gradients ``(dQ, dK, dV)`` of ``O = flex_attention(q, k, v,
+    block_mask, score_mod, scale)`` for the upstream gradient ``dout``.
+
+    bf16 only; ``o`` and ``lse`` are what the forward returned for the same
+    arguments; ``block_mask`` needs equal query and key block sizes (64 or
+    128). One fa_flex_attention_bwd call with a workspace allocated here;
+    the results are deterministic."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D (B, H, S, D)")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype
+            == torch.bfloat16):
+        raise ValueError("the backward takes bf16 q, k, v, o and dout")
+    for t in (q, k, v, o, lse, dout):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("all tensors must be on q's HIP device")
+    B, H, q_len, D = q.shape
+    Bk, H_kv, kv_len, Dk = k.shape
+    if k.shape != v.shape or Bk != B or Dk != D:
+        raise ValueError("k and v must be (B, H_kv, KV_LEN, D)")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have q's shape")
+    if lse.shape != (B, H, q_len) or lse.dtype != torch.float32:
+        raise ValueError("lse must be fp32 (B, H, Q_LEN)")
+    for t in (q, k, v):
+        if t.numel() and t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    o = o.contiguous()
+    dout = dout.contiguous()
+    lse = lse.contiguous()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    score = _score_from(score_mod)
+    dq = torch.empty((B, H, q_len, D), dtype=q.dtype, device=q.device)
+    dk = torch.empty((B, H_kv, kv_len, D), dtype=q.dtype, device=q.device)
+    dv = torch.empty_like(dk)
+    bm = block_mask.to_c()
+    nbytes = fa_bwd_workspace_bytes(B, H, q_len, bm)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        st = fa_flex_attention_bwd(
+            C.FA_BF16, B, H, H_kv, q_len, kv_len, D,
+            q.data_ptr(), q.stride()[:3], k.data_ptr(), k.stride()[:3],
+            v.data_ptr(), v.stride()[:3], float(scale), bm, score.to_c(),
+            o.data_ptr(), lse.data_ptr(), dout.data_ptr(), ws.data_ptr(),
+            nbytes, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+            _stream_handle(q.device))
+    C.check(st, "fa_flex_attention_bwd")
+    return dq, dk, dv

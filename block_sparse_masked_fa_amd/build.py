@@ -29,6 +29,9 @@ SOURCES = [
     "fwd_bf16_d128.hip",
     "fwd_fp32.hip",
     "fwd_combine.hip",
+    "bwd_prepare.hip",
+    "bwd_bf16_d64.hip",
+    "bwd_bf16_d128.hip",
 ]
 
 ARCH = "gfx950"

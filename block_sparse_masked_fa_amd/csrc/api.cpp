@@ -136,4 +136,43 @@ fa_status fa_flex_attention_fwd_split(
   return hip_status(fa::launch_split_combine(cl, stream), "split-KV merge launch");
 }
 
+fa_status fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
+                                 const fa_block_mask* bm, uint64_t* bytes) {
+  std::string msg;
+  if (!bytes) return finish(FA_ERR_NULL_POINTER, "bytes is NULL");
+  fa::BwdWorkspace ws{};
+  int st = fa::bwd_workspace_layout(B, H, q_len, bm, &ws, &msg);
+  if (st != FA_OK) return finish(st, msg);
+  *bytes = ws.total;
+  return FA_OK;
+}
+
+fa_status fa_flex_attention_bwd(
+    int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t q_len,
+    int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
+    const void* k, const int64_t k_stride[3], const void* v,
+    const int64_t v_stride[3], float scale, const fa_block_mask* bm,
+    const fa_score_mod* score, const void* o, const float* lse,
+    const void* dout, void* workspace, uint64_t workspace_bytes, void* dq,
+    void* dk, void* dv, void* stream) {
+  std::string msg;
+  fa::BwdLaunch p{};
+  bool nothing = false;
+  int st = fa::check_flex_attention_bwd(
+      dtype, B, H, H_kv, q_len, kv_len, D, q, q_stride, k, k_stride, v,
+      v_stride, scale, bm, score, o, lse, dout, workspace, workspace_bytes, dq,
+      dk, dv, &p, &nothing, &msg);
+  if (st != FA_OK) return finish(st, msg);
+  if (nothing) {
+    if (p.zero_bytes == 0) return FA_OK;
+    int err = fa::launch_zero_fill(p.dk, p.zero_bytes, stream);
+    if (err == 0) err = fa::launch_zero_fill(p.dv, p.zero_bytes, stream);
+    return hip_status(err, "gradient clear launch");
+  }
+  int err = fa::launch_bwd_prepare(p, stream);
+  if (err != 0) return hip_status(err, "backward preparation launch");
+  err = D == 64 ? fa::launch_bwd_bf16_d64(p, stream) : fa::launch_bwd_bf16_d128(p, stream);
+  return hip_status(err, "attention backward launch");
+}
+
 }  // extern "C"

@@ -1,0 +1,624 @@
+// Backward of the fused block-sparse attention, bf16 inputs and gradients,
+// fp32 accumulation, for gfx950. Gradients of O = attention(Q, K, V) for an
+// upstream dO (the LSE output is not differentiated), over the same block
+// mask as the forward, by the chain rule through the masked softmax and the
+// score_mod:
+//
+//   t = scale q.k,  s = score_mod(t),  P_ij = exp(s_ij - LSE_i) (allowed),
+//   dV_j = sum_i P_ij dO_i,       dP_ij = dO_i . v_j,
+//   dS_ij = P_ij (dP_ij - delta_i) with delta_i = dO_i . O_i,
+//   dT = dS * score_mod'(t)  (1 for none / ALiBi, 1 - tanh^2 for soft-cap),
+//   dQ_i = scale sum_j dT_ij k_j,  dK_j = scale sum_i dT_ij q_i.
+//
+// The forward's LSE makes P available per tile with no running maximum, so
+// every tile is independent and two kernels avoid atomics:
+//   * bwd_dq_kernel: one workgroup per (query block, head), the forward's
+//     work split and key-block lists. Per 64-key stage: S^T = K Q^T and
+//     dP^T = V dO^T (K and V rows as MFMA A operands from LDS, Q^T and dO^T
+//     resident as B operands), then dQ^T += K^T dT^T (K read transposed,
+//     ds_read_b64_tr_b16, exactly as the forward reads V).
+//   * bwd_dkdv_kernel: one workgroup per (key block, key head), wave w owns
+//     keys [32w, 32w + 32); it walks the transposed lists (the query blocks
+//     that name the key block) and, with grouped heads, every query head of
+//     the group. Per 64-row stage of Q and dO in LDS: S = Q K^T and
+//     dP = dO V^T (K^T and V^T resident as B operands), then
+//     dV^T += dO^T P and dK^T += Q^T dT (dO and Q read transposed).
+// The layouts, swizzles and loads are the forward's (fwd_bf16.hpp). With
+// the roles of queries and keys exchanged in bwd_dkdv_kernel, a lane's
+// accumulator values share one key and span 16 query rows, so the per-row
+// terms (LSE, delta, document id) come from LDS and mask_mod is an interval
+// of query rows per key.
+#pragma once
+
+#include "fwd_bf16.hpp"
+
+namespace fa {
+
+// Workgroup -> (batch, key head, key block) for the dK / dV kernel: dealt to
+// the 8 XCDs in contiguous ranges (one head's blocks share an L2).
+__device__ __forceinline__ bool xcd_kv_item(const FwdLaunch& p, int& b, int& hk, int& n) {
+  const int total = p.B * p.H_kv * p.nkvb;
+  const int per_xcd = (total + 7) >> 3;
+  const int wg = blockIdx.x;
+  const int logical = (wg & 7) * per_xcd + (wg >> 3);
+  if (logical >= total) return false;
+  n = logical % p.nkvb;
+  const int bh = logical / p.nkvb;
+  hk = bh % p.H_kv;
+  b = bh / p.H_kv;
+  return true;
+}
+
+// ---------------------------------------------------------------- dQ
+template <int D, int BLK, int SCORE>
+__global__ __launch_bounds__(BLK * 2, 1) void bwd_dq_kernel(const BwdLaunch bp) {
+  const FwdLaunch& p = bp.f;
+  constexpr int NW = BLK / 32;
+  constexpr int NT = NW * 64;
+  constexpr int SPB = BLK / kStageKeys;
+  constexpr int RB = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int RPK = 1024 / RB;
+  constexpr int STAGE_BYTES = kStageKeys * RB;
+  constexpr int ROUNDS = STAGE_BYTES / (NT * 16);
+  constexpr int DK = D / 16;
+  constexpr int DT = D / 32;
+
+  __shared__ __attribute__((aligned(1024))) char sK0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) int sDoc0[kStageKeys];
+  __shared__ __attribute__((aligned(16))) int sDoc1[kStageKeys];
+
+  WorkItem w;
+  if (!xcd_work_item(p, w)) return;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lq = lane & 31;
+  const int g = lane >> 5;
+
+  const int hk = w.h / (p.H / p.H_kv);
+  const int i = w.m * BLK + wave * 32 + lq;
+  const bool i_ok = i < p.q_len;
+  const int kv_len = p.kv_len;
+  const int mkind = p.mask.kind;
+  const int window = p.mask.window;
+  const int* doc = p.mask.doc_id + static_cast<int64_t>(w.b) * p.mask.doc_stride;
+  const bool doc_mask = mkind == FA_MASK_DOCUMENT;
+
+  const __bf16* qp = static_cast<const __bf16*>(p.q) + w.b * p.qs[0] + w.h * p.qs[1];
+  const int64_t orow = (static_cast<int64_t>(w.b) * p.H + w.h) * p.q_len + i;
+  const __bf16* dop = static_cast<const __bf16*>(bp.dout) + (i_ok ? orow : 0) * D;
+  const char* kbase = reinterpret_cast<const char*>(
+      static_cast<const __bf16*>(p.k) + w.b * p.ks[0] + hk * p.ks[1]);
+  const char* vbase = reinterpret_cast<const char*>(
+      static_cast<const __bf16*>(p.v) + w.b * p.vs[0] + hk * p.vs[1]);
+  const int64_t kstride = p.ks[2] * 2;
+  const int64_t vstride = p.vs[2] * 2;
+
+  // Q^T and dO^T as MFMA B operands: column = query lq, k slots d in
+  // [16dk + 8g, +8)
+  bf16x8 qf[DK], dof[DK];
+  {
+    const __bf16* row = qp + static_cast<int64_t>(i_ok ? i : 0) * p.qs[2];
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qf[dk] = __builtin_bit_cast(bf16x8, i_ok ? *reinterpret_cast<const u32x4*>(row + dk * 16 + g * 8) : z);
+      dof[dk] = __builtin_bit_cast(bf16x8, i_ok ? *reinterpret_cast<const u32x4*>(dop + dk * 16 + g * 8) : z);
+    }
+  }
+  // log2-domain LSE (a row without keys: +inf, so that every P is 0)
+  const float lse_i = i_ok ? bp.lse[orow] : FA_NEG_INF;
+  const float lse2 = lse_i == FA_NEG_INF ? __builtin_inff() : lse_i * kLog2e;
+  const float delta_i = i_ok ? bp.delta[orow] : 0.0f;
+  const int di = doc_mask ? doc[i_ok ? i : 0] : 0;
+
+  const int bb = p.Bm == 1 ? 0 : w.b;
+  const int hh = p.Hm == 1 ? 0 : w.h;
+  const int64_t lrow = (static_cast<int64_t>(bb) * p.Hm + hh) * p.nqb + w.m;
+  const int nkvb = p.nkvb;
+  const int nf = p.fnum ? min(max(p.fnum[lrow], 0), nkvb) : 0;
+  const int np = min(max(p.num[lrow], 0), nkvb);
+  const const_i32* fl = (const const_i32*)(p.fidx ? p.fidx + lrow * nkvb : p.idx);
+  const const_i32* pl = (const const_i32*)(p.idx + lrow * nkvb);
+  const int nblocks = nf + np;
+  const int nstages = nblocks * SPB;
+
+  const ScoreConsts sc = make_score_consts(p, w.h);
+  const int hi_abs =
+      mkind == FA_MASK_NONE ? kv_len
+      : mkind == FA_MASK_LOCAL_WINDOW
+          ? static_cast<int>(min(static_cast<int64_t>(i) + window, static_cast<int64_t>(kv_len)))
+          : min(i + 1, kv_len);
+  const int lo_abs =
+      (mkind == FA_MASK_SLIDING_WINDOW || mkind == FA_MASK_LOCAL_WINDOW)
+          ? static_cast<int>(max(static_cast<int64_t>(i) - window + 1, static_cast<int64_t>(0)))
+          : 0;
+  const unsigned span = static_cast<unsigned>(max(hi_abs - lo_abs, 0));
+
+  // per-lane LDS offsets, as in the forward: rows as A operands and the
+  // transposed reads
+  int k_rd[DK];
+  {
+    const int s = kv_swizzle<D>(lq);
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) k_rd[dk] = lq * RB + (((2 * dk + g) ^ s) << 4);
+  }
+  int v_rd[2][DT];
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2) {
+    const int r = 8 * t2 + 4 * g + ((lane & 15) >> 2);
+    const int s = kv_swizzle<D>(r);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      v_rd[t2][dt] = r * RB + (((d >> 3) ^ s) << 4) + ((d & 7) << 1);
+    }
+  }
+  uint32_t dma_k[ROUNDS], dma_v[ROUNDS];
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    const int r = (rd * NW + wave) * RPK + lane / CPR;
+    const uint32_t col = static_cast<uint32_t>(((lane % CPR) ^ kv_swizzle<D>(r)) * 16);
+    dma_k[rd] = static_cast<uint32_t>(r * kstride) + col;
+    dma_v[rd] = static_cast<uint32_t>(r * vstride) + col;
+  }
+
+  auto block_at = [&](int it) -> int { return it < np ? pl[it] : fl[it - np]; };
+  auto masked_at = [&](int it, int n) -> bool { return it < np || (n + 1) * BLK > kv_len; };
+  auto stage_block = [&](int st) -> int {
+    const int b = block_at(st / SPB);
+    return static_cast<unsigned>(b) < static_cast<unsigned>(nkvb) ? b : -1;
+  };
+  auto issue = [&](int st, int n, char* sK, char* sV, int* sD) {
+    const int it = st / SPB;
+    if (n < 0) return;
+    const int j0 = n * BLK + (st % SPB) * kStageKeys;
+    const int rows_left = kv_len - j0;
+    const int krec = rows_left >= kStageKeys ? 0x7fffffff
+                     : rows_left <= 0       ? 0
+                                            : (rows_left - 1) * static_cast<int>(kstride) + RB;
+    const int vrec = rows_left >= kStageKeys ? 0x7fffffff
+                     : rows_left <= 0       ? 0
+                                            : (rows_left - 1) * static_cast<int>(vstride) + RB;
+    const hw::i32x4 kr = hw::make_rsrc(kbase + (rows_left > 0 ? j0 * kstride : 0), krec);
+    const hw::i32x4 vr = hw::make_rsrc(vbase + (rows_left > 0 ? j0 * vstride : 0), vrec);
+#pragma unroll
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+      const int seg = (rd * NW + wave) * 1024;
+      hw::dma_tile16(kr, hw::lds_addr(sK + seg), dma_k[rd], 0);
+      hw::dma_tile16(vr, hw::lds_addr(sV + seg), dma_v[rd], 0);
+    }
+    if (doc_mask && masked_at(it, n) && wave == 0) {
+      const int j = min(j0 + lane, kv_len - 1);
+      hw::dma_dword(doc, hw::lds_addr(sD), static_cast<uint32_t>(j * 4));
+    }
+  };
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
+
+  auto compute = [&](int st, int n, const char* sK, const char* sV, const int* sD) {
+    const int it = st / SPB;
+    if (n < 0) return;
+    const bool masked = masked_at(it, n);
+    const int j0 = n * BLK + (st % SPB) * kStageKeys;
+
+    // S^T = K Q^T and dP^T = V dO^T for the stage's 64 keys
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      s[jt] = f32x16{};
+      dp[jt] = f32x16{};
+    }
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + k_rd[dk] + jt * 32 * RB);
+        s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[dk],
+                                                        s[jt], 0, 0, 0);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(sV + k_rd[dk] + jt * 32 * RB);
+        dp[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), dof[dk],
+                                                         dp[jt], 0, 0, 0);
+      }
+    }
+
+    // score_mod into the log2 domain, and its derivative (soft-cap)
+    float fp[2][16];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        fp[jt][r] = 1.0f;
+        if constexpr (SCORE == FA_SCORE_ALIBI) {
+          const float bj = sc.slope2 * static_cast<float>(j0 + 4 * g + 32 * jt + 8 * (r >> 2) + (r & 3) - i);
+          s[jt][r] = __builtin_fmaf(s[jt][r], sc.c, bj);
+        } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
+          const float e = exp2_hw(s[jt][r] * (2.0f * sc.cap_in * kLog2e));
+          const float tt = __builtin_amdgcn_rcpf(e + 1.0f);  // tanh = 1 - 2 tt
+          s[jt][r] = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out);
+          fp[jt][r] = 4.0f * tt * (1.0f - tt);               // 1 - tanh^2
+        } else {
+          s[jt][r] *= sc.c;
+        }
+      }
+    if (masked) {
+      const int lo = lo_abs - (j0 + 4 * g);
+      const unsigned sp = span;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int jl = 32 * jt + 8 * r4;
+          int dj[4] = {di, di, di, di};
+          if (doc_mask) {
+            const int4 t = *reinterpret_cast<const int4*>(sD + 4 * g + jl);
+            dj[0] = t.x; dj[1] = t.y; dj[2] = t.z; dj[3] = t.w;
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const bool ok = (static_cast<unsigned>(jl + c - lo) < sp) & (dj[c] == di);
+            s[jt][4 * r4 + c] = ok ? s[jt][4 * r4 + c] : FA_NEG_INF;
+          }
+        }
+    }
+
+    // P, dS = P (dP - delta), dT = dS score_mod' -> bf16 B operands
+    bf16x8 tb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      f32x8 tf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int jt = kk >> 1, r = (kk & 1) * 8 + e;
+        const float pr = exp2_hw(s[jt][r] - lse2);
+        tf[e] = pr * (dp[jt][r] - delta_i) * fp[jt][r];
+      }
+      tb[kk] = __builtin_convertvector(tf, bf16x8);
+    }
+
+    // dQ^T += K^T dT^T (4 k-steps of 16 keys; K read transposed)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const i16x4 lo = lds_read_tr(sK + v_rd[0][dt] + kk * 16 * RB);
+        const i16x4 hi = lds_read_tr(sK + v_rd[1][dt] + kk * 16 * RB);
+        const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), tb[kk],
+                                                         dq[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): setup loads landed
+  int n_cur = nstages > 0 ? stage_block(0) : -1;
+  if (nstages > 0) issue(0, n_cur, sK0, sV0, sDoc0);
+  for (int st = 0; st < nstages; st += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    int n_nxt = st + 1 >= nstages ? -1 : (st + 1) % SPB == 0 ? stage_block(st + 1) : n_cur;
+    if (st + 1 < nstages) issue(st + 1, n_nxt, sK1, sV1, sDoc1);
+    compute(st, n_cur, sK0, sV0, sDoc0);
+    if (st + 1 >= nstages) break;
+    n_cur = n_nxt;
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    n_nxt = st + 2 >= nstages ? -1 : (st + 2) % SPB == 0 ? stage_block(st + 2) : n_cur;
+    if (st + 2 < nstages) issue(st + 2, n_nxt, sK0, sV0, sDoc0);
+    compute(st + 1, n_cur, sK1, sV1, sDoc1);
+    n_cur = n_nxt;
+  }
+
+  if (i_ok) {
+    __bf16* out = static_cast<__bf16*>(bp.dq) + orow * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v4 = {dq[dt][4 * q4 + 0] * p.scale, dq[dt][4 * q4 + 1] * p.scale,
+                          dq[dt][4 * q4 + 2] * p.scale, dq[dt][4 * q4 + 3] * p.scale};
+        *reinterpret_cast<bf16x4*>(out + dt * 32 + 8 * q4 + 4 * g) = __builtin_convertvector(v4, bf16x4);
+      }
+  }
+}
+
+// ------------------------------------------------------------- dK, dV
+template <int D, int BLK, int SCORE>
+__global__ __launch_bounds__(BLK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp) {
+  const FwdLaunch& p = bp.f;
+  constexpr int NW = BLK / 32;
+  constexpr int NT = NW * 64;
+  constexpr int SPB = BLK / kStageKeys;  // 64-row query stages per query block
+  constexpr int RB = D * 2;
+  constexpr int CPR = D / 8;
+  constexpr int RPK = 1024 / RB;
+  constexpr int STAGE_BYTES = kStageKeys * RB;
+  constexpr int ROUNDS = STAGE_BYTES / (NT * 16);
+  constexpr int DK = D / 16;
+  constexpr int DT = D / 32;
+
+  __shared__ __attribute__((aligned(1024))) char sQ0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sO0[STAGE_BYTES];  // dO
+  __shared__ __attribute__((aligned(1024))) char sQ1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sO1[STAGE_BYTES];
+  // per query row of the stage: LSE, delta, document id
+  __shared__ __attribute__((aligned(16))) float sL0[kStageKeys], sL1[kStageKeys];
+  __shared__ __attribute__((aligned(16))) float sE0[kStageKeys], sE1[kStageKeys];
+  __shared__ __attribute__((aligned(16))) int sD0[kStageKeys], sD1[kStageKeys];
+
+  int b, hk, n;
+  if (!xcd_kv_item(p, b, hk, n)) return;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lq = lane & 31;
+  const int g = lane >> 5;
+  const int group = p.H / p.H_kv;
+
+  const int q_len = p.q_len;
+  const int kv_len = p.kv_len;
+  const int j = n * BLK + wave * 32 + lq;  // this lane's key
+  const bool j_ok = j < kv_len;
+  const int mkind = p.mask.kind;
+  const int window = p.mask.window;
+  const int* doc = p.mask.doc_id + static_cast<int64_t>(b) * p.mask.doc_stride;
+  const bool doc_mask = mkind == FA_MASK_DOCUMENT;
+  const int dj = doc_mask ? doc[j_ok ? j : 0] : 0;
+
+  // K^T and V^T as MFMA B operands: column = key lq, k slots d in [16dk + 8g, +8)
+  bf16x8 kf[DK], vf[DK];
+  {
+    const __bf16* kr = static_cast<const __bf16*>(p.k) + b * p.ks[0] + hk * p.ks[1] +
+                       static_cast<int64_t>(j_ok ? j : 0) * p.ks[2];
+    const __bf16* vr = static_cast<const __bf16*>(p.v) + b * p.vs[0] + hk * p.vs[1] +
+                       static_cast<int64_t>(j_ok ? j : 0) * p.vs[2];
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      kf[dk] = __builtin_bit_cast(bf16x8, j_ok ? *reinterpret_cast<const u32x4*>(kr + dk * 16 + g * 8) : z);
+      vf[dk] = __builtin_bit_cast(bf16x8, j_ok ? *reinterpret_cast<const u32x4*>(vr + dk * 16 + g * 8) : z);
+    }
+  }
+
+  // mask_mod as an interval of query rows per key: i in [ilo, ilo + ispan)
+  const int ihi =
+      !j_ok ? 0
+      : mkind == FA_MASK_NONE ? q_len
+      : mkind == FA_MASK_SLIDING_WINDOW || mkind == FA_MASK_LOCAL_WINDOW
+          ? static_cast<int>(min(static_cast<int64_t>(j) + window, static_cast<int64_t>(q_len)))
+          : q_len;
+  const int ilo = mkind == FA_MASK_LOCAL_WINDOW
+                      ? static_cast<int>(max(static_cast<int64_t>(j) - window + 1, static_cast<int64_t>(0)))
+                      : mkind == FA_MASK_NONE ? 0 : j;
+  const unsigned ispan = static_cast<unsigned>(max(ihi - ilo, 0));
+
+  int k_rd[DK];  // row lq (+32 jt) of a Q / dO tile as the A operand
+  {
+    const int s = kv_swizzle<D>(lq);
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) k_rd[dk] = lq * RB + (((2 * dk + g) ^ s) << 4);
+  }
+  int v_rd[2][DT];  // transposed reads of a Q / dO tile
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2) {
+    const int r = 8 * t2 + 4 * g + ((lane & 15) >> 2);
+    const int s = kv_swizzle<D>(r);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      v_rd[t2][dt] = r * RB + (((d >> 3) ^ s) << 4) + ((d & 7) << 1);
+    }
+  }
+  const int64_t qstride = p.qs[2] * 2;  // bytes
+  const int64_t ostride = static_cast<int64_t>(D) * 2;
+  uint32_t dma_q[ROUNDS], dma_o[ROUNDS];
+#pragma unroll
+  for (int rd = 0; rd < ROUNDS; ++rd) {
+    const int r = (rd * NW + wave) * RPK + lane / CPR;
+    const uint32_t col = static_cast<uint32_t>(((lane % CPR) ^ kv_swizzle<D>(r)) * 16);
+    dma_q[rd] = static_cast<uint32_t>(r * qstride) + col;
+    dma_o[rd] = static_cast<uint32_t>(r * ostride) + col;
+  }
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+
+  const int bb = p.Bm == 1 ? 0 : b;
+  const int nqb = p.nqb;
+  const int nkvb = p.nkvb;
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): setup loads landed
+
+  for (int gi = 0; gi < group; ++gi) {
+    const int h = hk * group + gi;
+    const int hh = p.Hm == 1 ? 0 : h;
+    const int64_t col = (static_cast<int64_t>(bb) * p.Hm + hh) * nkvb + n;
+    const int np = min(max(bp.qnum[col], 0), nqb);
+    const int nf = bp.fqnum ? min(max(bp.fqnum[col], 0), nqb) : 0;
+    const const_i32* pl = (const const_i32*)(bp.qidx + col * nqb);
+    const const_i32* fl = (const const_i32*)(bp.fqidx ? bp.fqidx + col * nqb : bp.qidx);
+    const int nstages = (np + nf) * SPB;
+    const ScoreConsts sc = make_score_consts(p, h);
+    const char* qbase = reinterpret_cast<const char*>(
+        static_cast<const __bf16*>(p.q) + b * p.qs[0] + h * p.qs[1]);
+    const int64_t rowbase = (static_cast<int64_t>(b) * p.H + h) * q_len;  // dO, LSE, delta
+    const char* obase = reinterpret_cast<const char*>(static_cast<const __bf16*>(bp.dout) + rowbase * D);
+
+    auto block_at = [&](int it) -> int { return it < np ? pl[it] : fl[it - np]; };
+    auto stage_block = [&](int st) -> int {
+      const int m = block_at(st / SPB);
+      return static_cast<unsigned>(m) < static_cast<unsigned>(nqb) ? m : -1;
+    };
+    auto masked_at = [&](int st, int m) -> bool {
+      return st / SPB < np || (m + 1) * BLK > q_len || (n + 1) * BLK > kv_len;
+    };
+    auto issue = [&](int st, int m, char* sQ, char* sO, float* sL, float* sE, int* sD) {
+      if (m < 0) return;
+      const int i0 = m * BLK + (st % SPB) * kStageKeys;
+      const int rows_left = q_len - i0;
+      const int qrec = rows_left >= kStageKeys ? 0x7fffffff
+                       : rows_left <= 0       ? 0
+                                              : (rows_left - 1) * static_cast<int>(qstride) + RB;
+      const int orec = rows_left >= kStageKeys ? 0x7fffffff
+                       : rows_left <= 0       ? 0
+                                              : (rows_left - 1) * static_cast<int>(ostride) + RB;
+      const hw::i32x4 qr = hw::make_rsrc(qbase + (rows_left > 0 ? i0 * qstride : 0), qrec);
+      const hw::i32x4 orr = hw::make_rsrc(obase + (rows_left > 0 ? i0 * ostride : 0), orec);
+#pragma unroll
+      for (int rd = 0; rd < ROUNDS; ++rd) {
+        const int seg = (rd * NW + wave) * 1024;
+        hw::dma_tile16(qr, hw::lds_addr(sQ + seg), dma_q[rd], 0);
+        hw::dma_tile16(orr, hw::lds_addr(sO + seg), dma_o[rd], 0);
+      }
+      if (wave == 0) {
+        const uint32_t r4 = static_cast<uint32_t>(min(i0 + lane, q_len - 1)) * 4;
+        hw::dma_dword(reinterpret_cast<const int*>(bp.lse + rowbase), hw::lds_addr(sL), r4);
+        hw::dma_dword(reinterpret_cast<const int*>(bp.delta + rowbase), hw::lds_addr(sE), r4);
+        if (doc_mask) hw::dma_dword(doc, hw::lds_addr(sD), r4);
+      }
+    };
+
+    auto compute = [&](int st, int m, const char* sQ, const char* sO, const float* sL,
+                       const float* sE, const int* sD) {
+      if (m < 0) return;
+      const bool masked = masked_at(st, m);
+      const int i0 = m * BLK + (st % SPB) * kStageKeys;
+
+      // S = Q K^T and dP = dO V^T for the stage's 64 query rows
+      f32x16 s[2], dpm[2];
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        s[it] = f32x16{};
+        dpm[it] = f32x16{};
+      }
+#pragma unroll
+      for (int dd = 0; dd < DK; ++dd) {
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(sQ + k_rd[dd] + it * 32 * RB);
+          s[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), kf[dd],
+                                                          s[it], 0, 0, 0);
+          const u32x4 o = *reinterpret_cast<const u32x4*>(sO + k_rd[dd] + it * 32 * RB);
+          dpm[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o), vf[dd],
+                                                            dpm[it], 0, 0, 0);
+        }
+      }
+
+      // element (it, r): query row i0 + 32 it + 8 (r / 4) + 4 g + r % 4
+      bf16x8 pb[4], tb[4];
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int il = 32 * it + 8 * r4 + 4 * g;  // first of 4 consecutive rows
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(sL + il);
+          const f32x4 del4 = *reinterpret_cast<const f32x4*>(sE + il);
+          int4 d4 = {dj, dj, dj, dj};
+          if (doc_mask && masked) d4 = *reinterpret_cast<const int4*>(sD + il);
+          const int dqs[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int r = 4 * r4 + c;
+            const int irow = i0 + il + c;
+            float x = s[it][r], fp = 1.0f;
+            if constexpr (SCORE == FA_SCORE_ALIBI) {
+              x = __builtin_fmaf(x, sc.c, sc.slope2 * static_cast<float>(j - irow));
+            } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
+              const float e = exp2_hw(x * (2.0f * sc.cap_in * kLog2e));
+              const float tt = __builtin_amdgcn_rcpf(e + 1.0f);
+              x = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out);
+              fp = 4.0f * tt * (1.0f - tt);
+            } else {
+              x *= sc.c;
+            }
+            bool ok = true;
+            if (masked)
+              ok = (static_cast<unsigned>(irow - ilo) < ispan) & (dqs[c] == dj) & (irow < q_len);
+            const float l2 = lse4[c] == FA_NEG_INF ? __builtin_inff() : lse4[c] * kLog2e;
+            const float pr = ok ? exp2_hw(x - l2) : 0.0f;
+            s[it][r] = pr;                                     // P
+            dpm[it][r] = pr * (dpm[it][r] - del4[c]) * fp;     // dT
+          }
+        }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        f32x8 pf, tf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pf[e] = s[kk >> 1][(kk & 1) * 8 + e];
+          tf[e] = dpm[kk >> 1][(kk & 1) * 8 + e];
+        }
+        pb[kk] = __builtin_convertvector(pf, bf16x8);
+        tb[kk] = __builtin_convertvector(tf, bf16x8);
+      }
+
+      // dV^T += dO^T P and dK^T += Q^T dT (4 k-steps of 16 query rows)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const i16x4 olo = lds_read_tr(sO + v_rd[0][dt] + kk * 16 * RB);
+          const i16x4 ohi = lds_read_tr(sO + v_rd[1][dt] + kk * 16 * RB);
+          const i16x8 o8 = {olo[0], olo[1], olo[2], olo[3], ohi[0], ohi[1], ohi[2], ohi[3]};
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o8), pb[kk],
+                                                           dv[dt], 0, 0, 0);
+          const i16x4 qlo = lds_read_tr(sQ + v_rd[0][dt] + kk * 16 * RB);
+          const i16x4 qhi = lds_read_tr(sQ + v_rd[1][dt] + kk * 16 * RB);
+          const i16x8 q8 = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q8), tb[kk],
+                                                           dk[dt], 0, 0, 0);
+        }
+      }
+    };
+
+    int m_cur = nstages > 0 ? stage_block(0) : -1;
+    if (nstages > 0) issue(0, m_cur, sQ0, sO0, sL0, sE0, sD0);
+    for (int st = 0; st < nstages; st += 2) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+      int m_nxt = st + 1 >= nstages ? -1 : (st + 1) % SPB == 0 ? stage_block(st + 1) : m_cur;
+      if (st + 1 < nstages) issue(st + 1, m_nxt, sQ1, sO1, sL1, sE1, sD1);
+      compute(st, m_cur, sQ0, sO0, sL0, sE0, sD0);
+      if (st + 1 >= nstages) break;
+      m_cur = m_nxt;
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      __syncthreads();
+      m_nxt = st + 2 >= nstages ? -1 : (st + 2) % SPB == 0 ? stage_block(st + 2) : m_cur;
+      if (st + 2 < nstages) issue(st + 2, m_nxt, sQ0, sO0, sL0, sE0, sD0);
+      compute(st + 1, m_cur, sQ1, sO1, sL1, sE1, sD1);
+      m_cur = m_nxt;
+    }
+    // the next head's first loads reuse buffer 0
+    __syncthreads();
+  }
+
+  if (j_ok) {
+    const int64_t krow = (static_cast<int64_t>(b) * p.H_kv + hk) * kv_len + j;
+    __bf16* outk = static_cast<__bf16*>(bp.dk) + krow * D;
+    __bf16* outv = static_cast<__bf16*>(bp.dv) + krow * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 k4 = {dk[dt][4 * q4 + 0] * p.scale, dk[dt][4 * q4 + 1] * p.scale,
+                          dk[dt][4 * q4 + 2] * p.scale, dk[dt][4 * q4 + 3] * p.scale};
+        const f32x4 v4 = {dv[dt][4 * q4 + 0], dv[dt][4 * q4 + 1], dv[dt][4 * q4 + 2],
+                          dv[dt][4 * q4 + 3]};
+        *reinterpret_cast<bf16x4*>(outk + dt * 32 + 8 * q4 + 4 * g) = __builtin_convertvector(k4, bf16x4);
+        *reinterpret_cast<bf16x4*>(outv + dt * 32 + 8 * q4 + 4 * g) = __builtin_convertvector(v4, bf16x4);
+      }
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,161 @@
+// Backward preparation, before the gradient kernels:
+//   * delta_i = sum_d dO[i, d] * O[i, d] (fp32): the row term of the softmax
+//     gradient, dS_ij = P_ij (dP_ij - delta_i), since sum_j P_ij dP_ij =
+//     dO_i . O_i;
+//   * the block lists transposed: for each key block n, the query blocks m
+//     whose row lists name n (partial and full apart), in ascending m. The
+//     dK / dV kernel walks them. Built from the forward's lists (whatever
+//     their origin) through a dense byte matrix of tile states: cleared,
+//     scattered per query-block row, then compacted per key-block column
+//     with wavefront ballots and prefix counts.
+#include <hip/hip_runtime.h>
+
+#include "fwd_common.hpp"
+
+namespace fa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+// one wavefront per row
+template <int D>
+__global__ __launch_bounds__(kThreads) void delta_kernel(const BwdLaunch p, int64_t rows) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int lane = threadIdx.x & 63;
+  constexpr int E = D / 64;
+  const __bf16* o = static_cast<const __bf16*>(p.o) + row * D + lane * E;
+  const __bf16* d = static_cast<const __bf16*>(p.dout) + row * D + lane * E;
+  float acc = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    acc = __builtin_fmaf(static_cast<float>(o[e]), static_cast<float>(d[e]), acc);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) p.delta[row] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void clear_kernel(unsigned char* s, int64_t n) {
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; t < n;
+       t += static_cast<int64_t>(gridDim.x) * kThreads)
+    s[t] = 0;
+}
+
+// one workgroup per (b, h, m) row of the forward lists
+__global__ __launch_bounds__(kThreads) void scatter_kernel(const BwdLaunch p) {
+  const FwdLaunch& f = p.f;
+  const int64_t row = blockIdx.x;
+  const int nkvb = f.nkvb;
+  unsigned char* st = p.states + row * nkvb;
+  const int np = min(max(f.num[row], 0), nkvb);
+  const int32_t* pl = f.idx + row * nkvb;
+  for (int t = threadIdx.x; t < np; t += kThreads) {
+    const int n = pl[t];
+    if (static_cast<unsigned>(n) < static_cast<unsigned>(nkvb)) st[n] = 1;
+  }
+  __syncthreads();  // a block named in both lists ends up full, whichever thread wrote first
+  if (f.fnum) {
+    const int nf = min(max(f.fnum[row], 0), nkvb);
+    const int32_t* fl = f.fidx + row * nkvb;
+    for (int t = threadIdx.x; t < nf; t += kThreads) {
+      const int n = fl[t];
+      if (static_cast<unsigned>(n) < static_cast<unsigned>(nkvb)) st[n] = 2;
+    }
+  }
+}
+
+// exclusive prefix count of `flag` over the workgroup; *total: the count
+__device__ int wg_prefix(bool flag, int* wave_counts, int* total) {
+  const int wave = threadIdx.x >> 6;
+  const unsigned long long mask = __builtin_amdgcn_ballot_w64(flag);
+  const int lane_prefix = __builtin_amdgcn_mbcnt_hi(
+      static_cast<unsigned>(mask >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<unsigned>(mask), 0u));
+  if ((threadIdx.x & 63) == 0) wave_counts[wave] = __builtin_popcountll(mask);
+  __syncthreads();
+  int before = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    before += (w < wave) ? wave_counts[w] : 0;
+    sum += wave_counts[w];
+  }
+  __syncthreads();
+  *total = sum;
+  return before + lane_prefix;
+}
+
+// one workgroup per (b, h, n) column
+__global__ __launch_bounds__(kThreads) void transpose_kernel(const BwdLaunch p) {
+  __shared__ int wave_counts[kWaves];
+  const FwdLaunch& f = p.f;
+  const int nqb = f.nqb, nkvb = f.nkvb;
+  const int64_t col = blockIdx.x;  // (b, h) * nkvb + n
+  const int64_t bh = col / nkvb;
+  const int n = static_cast<int>(col % nkvb);
+  const unsigned char* st = p.states + bh * nqb * nkvb + n;
+  int32_t* qi = p.qidx + col * nqb;
+  int32_t* fqi = p.fqidx ? p.fqidx + col * nqb : nullptr;
+  int run_p = 0, run_f = 0;
+  for (int base = 0; base < nqb; base += kThreads) {
+    const int m = base + threadIdx.x;
+    const int s = m < nqb ? st[static_cast<int64_t>(m) * nkvb] : 0;
+    int cp, cf;
+    const int pp = run_p + wg_prefix(s == 1, wave_counts, &cp);
+    const int pf = run_f + wg_prefix(s == 2, wave_counts, &cf);
+    if (s == 1) qi[pp] = m;
+    if (s == 2) fqi[pf] = m;
+    run_p += cp;
+    run_f += cf;
+  }
+  if (threadIdx.x == 0) {
+    p.qnum[col] = run_p;
+    if (p.fqnum) p.fqnum[col] = run_f;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void zero16_kernel(uint4* dst, int64_t n16) {
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; t < n16;
+       t += static_cast<int64_t>(gridDim.x) * kThreads)
+    dst[t] = uint4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace
+
+int launch_zero_fill(void* dst, uint64_t bytes, void* stream) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  if (n16 == 0) return hipSuccess;
+  const int64_t g = (n16 + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(zero16_kernel, dim3(static_cast<unsigned>(g < 8192 ? g : 8192)), dim3(kThreads),
+                     0, static_cast<hipStream_t>(stream), static_cast<uint4*>(dst), n16);
+  return hipGetLastError();
+}
+
+int launch_bwd_prepare(const BwdLaunch& p, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const FwdLaunch& f = p.f;
+  const int64_t rows = static_cast<int64_t>(f.B) * f.H * f.q_len;
+  const dim3 blk(kThreads);
+  if (rows > 0) {
+    const dim3 grid(static_cast<unsigned>((rows + kWaves - 1) / kWaves));
+    if (f.D == 64)
+      hipLaunchKernelGGL((delta_kernel<64>), grid, blk, 0, s, p, rows);
+    else
+      hipLaunchKernelGGL((delta_kernel<128>), grid, blk, 0, s, p, rows);
+  }
+  const int64_t lrows = static_cast<int64_t>(f.Bm) * f.Hm * f.nqb;
+  const int64_t cells = lrows * f.nkvb;
+  if (cells > 0) {
+    const int64_t g = (cells + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(clear_kernel, dim3(static_cast<unsigned>(g < 4096 ? g : 4096)), blk, 0, s,
+                       p.states, cells);
+    hipLaunchKernelGGL(scatter_kernel, dim3(static_cast<unsigned>(lrows)), blk, 0, s, p);
+  }
+  // one workgroup per key-block column; with no query blocks it only
+  // writes zero counts
+  const int64_t cols = static_cast<int64_t>(f.Bm) * f.Hm * f.nkvb;
+  if (cols > 0)
+    hipLaunchKernelGGL(transpose_kernel, dim3(static_cast<unsigned>(cols)), blk, 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace fa

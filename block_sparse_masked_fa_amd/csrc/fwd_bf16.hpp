@@ -435,14 +435,15 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
   for (int st = 0; st < nstages; st += 2) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's DMA landed
     __syncthreads();                     // every lane's DMA landed; buffer 1 free
-    int n_nxt = (st + 1) % SPB == 0 ? stage_block(st + 1) : n_cur;
+    // (no lookup past the last stage: the list index would leave the row)
+    int n_nxt = st + 1 >= nstages ? -1 : (st + 1) % SPB == 0 ? stage_block(st + 1) : n_cur;
     if (st + 1 < nstages) issue(st + 1, n_nxt, sK1, sV1, sDoc1);
     compute(st, n_cur, sK0, sV0, sDoc0);
     if (st + 1 >= nstages) break;
     n_cur = n_nxt;
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
-    n_nxt = (st + 2) % SPB == 0 ? stage_block(st + 2) : n_cur;
+    n_nxt = st + 2 >= nstages ? -1 : (st + 2) % SPB == 0 ? stage_block(st + 2) : n_cur;
     if (st + 2 < nstages) issue(st + 2, n_nxt, sK0, sV0, sDoc0);
     compute(st + 1, n_cur, sK1, sV1, sDoc1);
     n_cur = n_nxt;

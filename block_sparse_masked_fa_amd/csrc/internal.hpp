@@ -69,11 +69,38 @@ struct CombineLaunch {
   float* lse;    // may be NULL
 };
 
+// Backward: the forward's arguments (f: q, k, v, mask, block lists, score)
+// plus the forward's outputs, the upstream gradient and the outputs.
+struct BwdLaunch {
+  FwdLaunch f;           // o / lse / split fields unused
+  const void* o;         // forward output, [B, H, q_len, D] contiguous
+  const float* lse;      // forward LSE, [B, H, q_len]
+  const void* dout;      // dO, [B, H, q_len, D] contiguous
+  float* delta;          // [B, H, q_len]: rowsum(dO * O), written first
+  // per key block, the query blocks that list it ([Bm, Hm, nkvb] and
+  // [Bm, Hm, nkvb, nqb]); full_* NULL when the mask has no full lists
+  int32_t* qnum;
+  int32_t* qidx;
+  int32_t* fqnum;
+  int32_t* fqidx;
+  unsigned char* states; // [Bm, Hm, nqb, nkvb] scratch for the transposition
+  void* dq;              // [B, H, q_len, D] contiguous, bf16
+  void* dk;              // [B, H_kv, kv_len, D] contiguous, bf16
+  void* dv;
+  // no query rows (q_len == 0) but keys: bytes of dk and of dv to clear,
+  // nothing else runs
+  uint64_t zero_bytes;
+};
+
 // Kernel launchers: return a hipError_t value (0 = success).
 int launch_block_mask(const BlockMaskLaunch& p, void* stream);
 int launch_fwd_bf16_d64(const FwdLaunch& p, void* stream);
 int launch_fwd_bf16_d128(const FwdLaunch& p, void* stream);
 int launch_fwd_fp32(const FwdLaunch& p, void* stream);
 int launch_split_combine(const CombineLaunch& p, void* stream);
+int launch_bwd_prepare(const BwdLaunch& p, void* stream);  // delta, transposed lists
+int launch_zero_fill(void* dst, uint64_t bytes, void* stream);  // 16-byte aligned
+int launch_bwd_bf16_d64(const BwdLaunch& p, void* stream);
+int launch_bwd_bf16_d128(const BwdLaunch& p, void* stream);
 
 }  // namespace fa

@@ -333,4 +333,115 @@ int check_split(int32_t dtype, int32_t num_splits, void* workspace,
   return FA_OK;
 }
 
+namespace {
+uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+}  // namespace
+
+int bwd_workspace_layout(int32_t B, int32_t H, int32_t q_len,
+                         const fa_block_mask* bm, BwdWorkspace* ws,
+                         std::string* msg) {
+  if (!bm || !ws) return fail(msg, FA_ERR_NULL_POINTER, "block mask or output is NULL");
+  if (B < 0 || H < 0 || q_len < 0)
+    return fail(msg, FA_ERR_INVALID_VALUE, "negative size");
+  if (bm->B < 1 || bm->H < 1 || bm->num_q_blocks < 0 || bm->num_kv_blocks < 0)
+    return fail(msg, FA_ERR_INVALID_VALUE, "block mask dims must be positive");
+  const uint64_t rows = static_cast<uint64_t>(B) * static_cast<uint64_t>(H) *
+                        static_cast<uint64_t>(q_len);
+  const uint64_t bh = static_cast<uint64_t>(bm->B) * static_cast<uint64_t>(bm->H);
+  const uint64_t nqb = static_cast<uint64_t>(bm->num_q_blocks);
+  const uint64_t nkvb = static_cast<uint64_t>(bm->num_kv_blocks);
+  const bool full = bm->separate_full_blocks != 0;
+  uint64_t at = 0;
+  ws->delta = at;
+  at = align256(at + rows * 4u);
+  ws->states = at;
+  at = align256(at + bh * nqb * nkvb);
+  ws->qnum = at;
+  at = align256(at + bh * nkvb * 4u);
+  ws->qidx = at;
+  at = align256(at + bh * nkvb * nqb * 4u);
+  ws->fqnum = at;
+  at = full ? align256(at + bh * nkvb * 4u) : at;
+  ws->fqidx = at;
+  at = full ? align256(at + bh * nkvb * nqb * 4u) : at;
+  ws->total = at;
+  return FA_OK;
+}
+
+int check_flex_attention_bwd(
+    int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t q_len,
+    int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
+    const void* k, const int64_t k_stride[3], const void* v,
+    const int64_t v_stride[3], float scale, const fa_block_mask* bm,
+    const fa_score_mod* score, const void* o, const float* lse,
+    const void* dout, void* workspace, uint64_t workspace_bytes, void* dq,
+    void* dk, void* dv, BwdLaunch* out, bool* nothing_to_do, std::string* msg) {
+  *nothing_to_do = false;
+  if (dtype != FA_BF16)
+    return fail(msg, FA_ERR_UNSUPPORTED, "the backward is built for bf16 only");
+  // the forward's checks (o is only read here; the descriptor field is unused)
+  int st = check_flex_attention_fwd(dtype, B, H, H_kv, q_len, kv_len, D, q,
+                                    q_stride, k, k_stride, v, v_stride, scale,
+                                    bm, score, const_cast<void*>(o),
+                                    const_cast<float*>(lse), &out->f,
+                                    nothing_to_do, msg);
+  if (st != FA_OK) return st;
+  out->zero_bytes = 0;
+  if (*nothing_to_do) {
+    // no query rows: with keys present, dK and dV are zero and still written
+    const int64_t kv_elems = static_cast<int64_t>(B) * H_kv * kv_len * D;
+    if (kv_elems == 0) return FA_OK;
+    if (!dk || !dv) return fail(msg, FA_ERR_NULL_POINTER, "dk or dv is NULL");
+    if (!aligned16(dk) || !aligned16(dv))
+      return fail(msg, FA_ERR_UNSUPPORTED, "dk and dv must be 16-byte aligned");
+    out->zero_bytes = static_cast<uint64_t>(kv_elems) * 2u;
+    out->dk = dk;
+    out->dv = dv;
+    return FA_OK;
+  }
+  if (bm->block_m != bm->block_n)
+    return fail(msg, FA_ERR_UNSUPPORTED,
+                "the backward needs block_m == block_n (64 or 128)");
+  const int64_t kv_items = static_cast<int64_t>(B) * H_kv * bm->num_kv_blocks;
+  if (kv_items > INT32_MAX)
+    return fail(msg, FA_ERR_UNSUPPORTED, "B * H_kv * num_kv_blocks too large");
+  BwdWorkspace ws{};
+  if ((st = bwd_workspace_layout(B, H, q_len, bm, &ws, msg)) != FA_OK) return st;
+  if (!o || !lse || !dout || !dq)
+    return fail(msg, FA_ERR_NULL_POINTER, "o, lse, dout or dq is NULL");
+  if (kv_len > 0 && (!dk || !dv))
+    return fail(msg, FA_ERR_NULL_POINTER, "dk or dv is NULL");
+  if (ws.total > 0 && !workspace)
+    return fail(msg, FA_ERR_NULL_POINTER, "workspace is NULL");
+  if (workspace_bytes < ws.total)
+    return fail(msg, FA_ERR_INVALID_VALUE,
+                "workspace has " + std::to_string(workspace_bytes) +
+                    " bytes, needs " + std::to_string(ws.total));
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) ||
+      !aligned16(dv) || !aligned16(lse) || (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return fail(msg, FA_ERR_UNSUPPORTED,
+                "o, dout, dq, dk, dv and lse must be 16-byte aligned, the "
+                "workspace 256-byte aligned");
+  // the dK / dV kernel addresses a 64-row stage of Q with 32-bit byte offsets
+  if (q_stride[2] * 2 * 64 >= (int64_t(1) << 31))
+    return fail(msg, FA_ERR_UNSUPPORTED, "q sequence stride too large");
+  char* w = static_cast<char*>(workspace);
+  const bool full = bm->separate_full_blocks != 0;
+  out->f.o = nullptr;
+  out->f.lse = nullptr;
+  out->o = o;
+  out->lse = lse;
+  out->dout = dout;
+  out->delta = reinterpret_cast<float*>(w + ws.delta);
+  out->states = reinterpret_cast<unsigned char*>(w + ws.states);
+  out->qnum = reinterpret_cast<int32_t*>(w + ws.qnum);
+  out->qidx = reinterpret_cast<int32_t*>(w + ws.qidx);
+  out->fqnum = full ? reinterpret_cast<int32_t*>(w + ws.fqnum) : nullptr;
+  out->fqidx = full ? reinterpret_cast<int32_t*>(w + ws.fqidx) : nullptr;
+  out->dq = dq;
+  out->dk = dk;
+  out->dv = dv;
+  return FA_OK;
+}
+
 }  // namespace fa

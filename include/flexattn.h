@@ -2,7 +2,7 @@
  * flexattn.h - C ABI of the MI355X (gfx950) block-sparse masked attention
  * library (libflexattn.so).
  *
- * Two operations, both FlexAttention-style:
+ * FlexAttention-style operations:
  *
  *   fa_create_block_mask   turns a built-in mask_mod(b, h, q_idx, kv_idx)
  *                          into per-query-block lists of partial and full
@@ -19,6 +19,8 @@
  *                          "The two hooks", "Bonus: a score_mod for
  *                          soft-capping"; frontiernews, "What Is
  *                          FlexAttention and Why Does It Matter").
+ *   fa_flex_attention_bwd  its gradients dQ, dK, dV over the same block
+ *                          mask (deterministic).
  *
  * Conventions shared by every entry point
  *   - Every pointer argument named "device" is HIP device memory owned by
@@ -43,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -250,6 +252,61 @@ fa_status fa_flex_attention_fwd_split(
 fa_status fa_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
                                    int32_t D, int32_t num_splits,
                                    uint64_t* bytes);
+
+/* Backward of fa_flex_attention_fwd (bf16): the gradients dQ, dK, dV of
+ * o = attention(q, k, v) for an upstream gradient dout, over the same block
+ * mask and score_mod (the lse output is not differentiated). The pages
+ * presuppose this operation: the tensorplay create_block_mask page's
+ * compute_dq_write_order / dq_kv_order parameters order the dQ writes of a
+ * block-sparse backward over the block mask, and frontiernews ("What Else
+ * Shipped in PyTorch 2.13?") lists a deterministic FlexAttention backward.
+ * With t = scale q.k, s = score_mod(t), P = exp(s - lse) on allowed pairs
+ * (0 elsewhere):
+ *   dV = P^T dO,  dP = dO V^T,  delta_i = dO_i . O_i,
+ *   dS = P * (dP - delta),  dT = dS * score_mod'(t)
+ *        (1 for none and ALiBi, 1 - tanh^2(t / cap) for soft-cap),
+ *   dQ = scale dT K,  dK = scale dT^T Q,
+ * and with H_kv < H the gradients of a key head sum over its query heads.
+ * Deterministic: no atomics; every output row is accumulated by one
+ * workgroup in a fixed order, so repeated calls give identical bits.
+ *
+ *   dtype      FA_BF16 only (FA_ERR_UNSUPPORTED otherwise).
+ *   B ... score  as for fa_flex_attention_fwd, with the block mask's
+ *              block_m == block_n in {64, 128}; bm and score must be the
+ *              ones the forward ran with.
+ *   o          device bf16 [B, H, q_len, D], contiguous: the forward's output.
+ *   lse        device fp32 [B, H, q_len], contiguous: the forward's lse.
+ *              Gradients are only meaningful for the o and lse that the
+ *              same arguments produced; other values give wrong numbers but
+ *              no out-of-bounds access.
+ *   dout       device bf16 [B, H, q_len, D], contiguous.
+ *   workspace  device memory owned by the caller, 256-byte aligned, at
+ *              least fa_bwd_workspace_bytes(...) bytes; overwritten. Calls in
+ *              flight at the same time need separate workspaces.
+ *   workspace_bytes  its size; FA_ERR_INVALID_VALUE if too small.
+ *   dq         device bf16 [B, H, q_len, D], contiguous, written.
+ *   dk, dv     device bf16 [B, H_kv, kv_len, D], contiguous, written (zero
+ *              for keys that no allowed pair reaches).
+ *   All device arrays 16-byte aligned; outputs must not overlap inputs.
+ * Five kernel launches (delta = rowsum(dO * O), two that transpose the
+ * block lists into per-key-block lists of query blocks, then dQ, then
+ * dK / dV); asynchronous. */
+fa_status fa_flex_attention_bwd(
+    int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t q_len,
+    int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
+    const void* k, const int64_t k_stride[3], const void* v,
+    const int64_t v_stride[3], float scale, const fa_block_mask* bm,
+    const fa_score_mod* score, const void* o, const float* lse,
+    const void* dout, void* workspace, uint64_t workspace_bytes, void* dq,
+    void* dk, void* dv, void* stream);
+
+/* Workspace size of fa_flex_attention_bwd for a block mask: B * H * q_len
+ * fp32 (delta), then bm->B * bm->H * NQB * NKVB bytes of tile states and the
+ * transposed lists (per key block a count and NQB indices, int32, twice
+ * when bm->separate_full_blocks), each part rounded up to 256 bytes.
+ * Host only (bm's dims are read, not its arrays); nothing is launched. */
+fa_status fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
+                                 const fa_block_mask* bm, uint64_t* bytes);
 
 /* Static description of a status code. */
 const char* fa_status_string(int32_t status);

@@ -351,3 +351,95 @@ def test_auto_num_splits():
     assert api.auto_num_splits(torch.bfloat16, 1, 1, 256, 256) == 1
     assert api.auto_num_splits(torch.float32, 1, 1, 4, 256) == 1
     assert api.auto_num_splits(torch.bfloat16, 0, 1, 4, 256) == 1
+
+
+def _bwd_ws_bytes(B, H, q_len, nq, nk, Bm=1, Hm=1, full=True):
+    # the documented layout: delta, tile states, then per key block a count
+    # and NQB indices (twice with full lists), each part rounded to 256
+    r = lambda x: -(-x // 256) * 256  # noqa: E731
+    n = r(B * H * q_len * 4) + r(Bm * Hm * nq * nk)
+    n += r(Bm * Hm * nk * 4) + r(Bm * Hm * nk * nq * 4)
+    if full:
+        n += r(Bm * Hm * nk * 4) + r(Bm * Hm * nk * nq * 4)
+    return n
+
+
+@needs_lib
+def test_bwd_workspace_bytes():
+    bm = _good_bm(q_len=300, kv_len=200, block=128)       # 3 x 2 blocks
+    assert api.fa_bwd_workspace_bytes(2, 4, 300, bm) == _bwd_ws_bytes(2, 4, 300, 3, 2)
+    bm.separate_full_blocks = 0
+    assert api.fa_bwd_workspace_bytes(2, 4, 300, bm) == \
+        _bwd_ws_bytes(2, 4, 300, 3, 2, full=False)
+    bm = _good_bm(q_len=8192, kv_len=8192, block=128, B=4, H=16)
+    assert api.fa_bwd_workspace_bytes(4, 16, 8192, bm) == \
+        _bwd_ws_bytes(4, 16, 8192, 64, 64, Bm=4, Hm=16)
+    with pytest.raises(C.FlexAttnError) as e:
+        api.fa_bwd_workspace_bytes(-1, 4, 300, bm)
+    assert e.value.status == C.FA_ERR_INVALID_VALUE
+    assert C.lib().fa_bwd_workspace_bytes(1, 1, 64, None, None) == \
+        C.FA_ERR_NULL_POINTER
+
+
+def _bwd(**over):
+    bm = over.pop("bm", _good_bm())
+    a = dict(dtype=C.FA_BF16, B=2, H=4, H_kv=2, q_len=256, kv_len=256, D=128,
+             q=FAKE, q_stride=(4 * 256 * 128, 256 * 128, 128), k=FAKE,
+             k_stride=(2 * 256 * 128, 256 * 128, 128), v=FAKE,
+             v_stride=(2 * 256 * 128, 256 * 128, 128), scale=0.088,
+             bm=bm, score=C.fa_score_mod(kind=C.FA_SCORE_NONE),
+             o=FAKE, lse=FAKE, dout=FAKE, workspace=FAKE,
+             workspace_bytes=_bwd_ws_bytes(2, 4, 256, 2, 2), dq=FAKE, dk=FAKE,
+             dv=FAKE, stream=None)
+    a.update(over)
+    return api.fa_flex_attention_bwd(**a)
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status", [
+    (dict(dtype=C.FA_FP32), C.FA_ERR_UNSUPPORTED),
+    (dict(bm=_bm(**{**{f: getattr(_good_bm(), f) for f, _ in
+                       C.fa_block_mask._fields_}, "block_n": 64,
+                    "num_kv_blocks": 4})), C.FA_ERR_UNSUPPORTED),
+    (dict(workspace_bytes=_bwd_ws_bytes(2, 4, 256, 2, 2) - 1),
+     C.FA_ERR_INVALID_VALUE),
+    (dict(workspace=None), C.FA_ERR_NULL_POINTER),
+    (dict(workspace=FAKE + 16), C.FA_ERR_UNSUPPORTED),
+    (dict(o=None), C.FA_ERR_NULL_POINTER),
+    (dict(lse=None), C.FA_ERR_NULL_POINTER),
+    (dict(dout=None), C.FA_ERR_NULL_POINTER),
+    (dict(dq=None), C.FA_ERR_NULL_POINTER),
+    (dict(dk=None), C.FA_ERR_NULL_POINTER),
+    (dict(dv=None), C.FA_ERR_NULL_POINTER),
+    (dict(dk=FAKE + 8), C.FA_ERR_UNSUPPORTED),
+    (dict(lse=FAKE + 4), C.FA_ERR_UNSUPPORTED),
+    # the forward's own checks apply
+    (dict(D=96), C.FA_ERR_UNSUPPORTED),
+    (dict(H_kv=3), C.FA_ERR_INVALID_VALUE),
+    (dict(scale=0.0), C.FA_ERR_INVALID_VALUE),
+    (dict(bm=_good_bm(B=3)), C.FA_ERR_SHAPE_MISMATCH),
+    (dict(q=None), C.FA_ERR_NULL_POINTER),
+    (dict(score=C.fa_score_mod(kind=C.FA_SCORE_SOFTCAP, softcap=-1.0)),
+     C.FA_ERR_INVALID_VALUE),
+])
+def test_bwd_refuses(over, status):
+    st = _bwd(**over)
+    assert st == status, C.lib().fa_last_error()
+
+
+@needs_lib
+def test_bwd_empty_problem_is_a_noop():
+    # B = 0, or no keys and no queries: nothing to do, no pointer touched
+    assert _bwd(B=0, q=None, k=None, v=None, o=None, lse=None, dout=None,
+                workspace=None, workspace_bytes=0, dq=None, dk=None,
+                dv=None) == C.FA_OK
+    bm = _good_bm(q_len=0, kv_len=0)
+    bm.num_q_blocks = bm.num_kv_blocks = 0
+    assert _bwd(q_len=0, kv_len=0, bm=bm, q=None, k=None, v=None, o=None,
+                lse=None, dout=None, workspace=None, workspace_bytes=0,
+                dq=None, dk=None, dv=None) == C.FA_OK
+    # no queries but keys: dK and dV must still be given (they are cleared)
+    bm = _good_bm(q_len=0)
+    bm.num_q_blocks = 0
+    assert _bwd(q_len=0, bm=bm, q=None, o=None, lse=None, dout=None,
+                dq=None, dk=None) == C.FA_ERR_NULL_POINTER
