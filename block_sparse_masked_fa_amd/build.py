@@ -34,6 +34,16 @@ SOURCES = [
     "bwd_bf16_d128.hip",
 ]
 
+# Per-source extra flags. The backward kernels keep two fp32 tiles, two
+# accumulator sets and their operands live at one wave per SIMD; LLVM's
+# iterative ILP scheduler keeps their LDS reads ahead of the MFMAs that use
+# them where the default scheduler serialises read, wait and MFMA (measured:
+# about 20% less time for the dK / dV kernel).
+EXTRA_FLAGS = {
+    "bwd_bf16_d64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "bwd_bf16_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
 ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}",
@@ -56,7 +66,8 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *CFLAGS, *EXTRA_FLAGS.get(src, []), "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     t = time.time()

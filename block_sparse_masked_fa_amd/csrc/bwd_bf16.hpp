@@ -440,167 +440,216 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp
   const int nkvb = p.nkvb;
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): setup loads landed
 
-  for (int gi = 0; gi < group; ++gi) {
-    const int h = hk * group + gi;
-    const int hh = p.Hm == 1 ? 0 : h;
+  // The stages of every query head of the group form one flat sequence
+  // (head by head; per head its partial list, then its full list; a query
+  // block's 64-row stages in order), walked by one loop so that the dK / dV
+  // accumulators stay in place across heads.
+  auto head_lists = [&](int gi, int& np, int& nf, const const_i32*& pl, const const_i32*& fl) {
+    const int hh = p.Hm == 1 ? 0 : hk * group + gi;
     const int64_t col = (static_cast<int64_t>(bb) * p.Hm + hh) * nkvb + n;
-    const int np = min(max(bp.qnum[col], 0), nqb);
-    const int nf = bp.fqnum ? min(max(bp.fqnum[col], 0), nqb) : 0;
-    const const_i32* pl = (const const_i32*)(bp.qidx + col * nqb);
-    const const_i32* fl = (const const_i32*)(bp.fqidx ? bp.fqidx + col * nqb : bp.qidx);
-    const int nstages = (np + nf) * SPB;
-    const ScoreConsts sc = make_score_consts(p, h);
+    np = min(max(((const const_i32*)bp.qnum)[col], 0), nqb);
+    nf = bp.fqnum ? min(max(((const const_i32*)bp.fqnum)[col], 0), nqb) : 0;
+    pl = (const const_i32*)(bp.qidx + col * nqb);
+    fl = (const const_i32*)(bp.fqidx ? bp.fqidx + col * nqb : bp.qidx);
+  };
+  int total = 0;
+  for (int gi = 0; gi < group; ++gi) {
+    int np, nf;
+    const const_i32 *pl, *fl;
+    head_lists(gi, np, nf, pl, fl);
+    total += (np + nf) * SPB;
+  }
+
+  // cursor over the sequence: head cg, its lists, the next block visit
+  int cg = -1, c_np = 0, c_nf = 0, c_left = 0, c_it = 0, c_sub = 0, c_m = -1;
+  const const_i32* c_pl = nullptr;
+  const const_i32* c_fl = nullptr;
+  // the next stage: query block m (-1: an index outside [0, NQB), skipped),
+  // head h, 64-row stage sub of the block, and whether mask_mod applies.
+  // Called exactly `total` times, so a head with stages left always exists.
+  auto next_stage = [&](int& m, int& h, int& sub, bool& masked) {
+    while (c_left == 0) {
+      ++cg;
+      head_lists(cg, c_np, c_nf, c_pl, c_fl);
+      c_left = (c_np + c_nf) * SPB;
+      c_it = 0;
+      c_sub = 0;
+    }
+    if (c_sub == 0) {
+      const int mm = c_it < c_np ? c_pl[c_it] : c_fl[c_it - c_np];
+      c_m = static_cast<unsigned>(mm) < static_cast<unsigned>(nqb) ? mm : -1;
+    }
+    m = c_m;
+    h = hk * group + cg;
+    sub = c_sub;
+    masked = c_it < c_np || (c_m + 1) * BLK > q_len || (n + 1) * BLK > kv_len;
+    if (++c_sub == SPB) {
+      c_sub = 0;
+      ++c_it;
+    }
+    --c_left;
+  };
+
+  auto issue = [&](int m, int h, int sub, char* sQ, char* sO, float* sL, float* sE, int* sD) {
+    if (m < 0) return;
     const char* qbase = reinterpret_cast<const char*>(
         static_cast<const __bf16*>(p.q) + b * p.qs[0] + h * p.qs[1]);
     const int64_t rowbase = (static_cast<int64_t>(b) * p.H + h) * q_len;  // dO, LSE, delta
-    const char* obase = reinterpret_cast<const char*>(static_cast<const __bf16*>(bp.dout) + rowbase * D);
-
-    auto block_at = [&](int it) -> int { return it < np ? pl[it] : fl[it - np]; };
-    auto stage_block = [&](int st) -> int {
-      const int m = block_at(st / SPB);
-      return static_cast<unsigned>(m) < static_cast<unsigned>(nqb) ? m : -1;
-    };
-    auto masked_at = [&](int st, int m) -> bool {
-      return st / SPB < np || (m + 1) * BLK > q_len || (n + 1) * BLK > kv_len;
-    };
-    auto issue = [&](int st, int m, char* sQ, char* sO, float* sL, float* sE, int* sD) {
-      if (m < 0) return;
-      const int i0 = m * BLK + (st % SPB) * kStageKeys;
-      const int rows_left = q_len - i0;
-      const int qrec = rows_left >= kStageKeys ? 0x7fffffff
-                       : rows_left <= 0       ? 0
-                                              : (rows_left - 1) * static_cast<int>(qstride) + RB;
-      const int orec = rows_left >= kStageKeys ? 0x7fffffff
-                       : rows_left <= 0       ? 0
-                                              : (rows_left - 1) * static_cast<int>(ostride) + RB;
-      const hw::i32x4 qr = hw::make_rsrc(qbase + (rows_left > 0 ? i0 * qstride : 0), qrec);
-      const hw::i32x4 orr = hw::make_rsrc(obase + (rows_left > 0 ? i0 * ostride : 0), orec);
+    const char* obase =
+        reinterpret_cast<const char*>(static_cast<const __bf16*>(bp.dout) + rowbase * D);
+    const int i0 = m * BLK + sub * kStageKeys;
+    const int rows_left = q_len - i0;
+    const int qrec = rows_left >= kStageKeys ? 0x7fffffff
+                     : rows_left <= 0       ? 0
+                                            : (rows_left - 1) * static_cast<int>(qstride) + RB;
+    const int orec = rows_left >= kStageKeys ? 0x7fffffff
+                     : rows_left <= 0       ? 0
+                                            : (rows_left - 1) * static_cast<int>(ostride) + RB;
+    const hw::i32x4 qr = hw::make_rsrc(qbase + (rows_left > 0 ? i0 * qstride : 0), qrec);
+    const hw::i32x4 orr = hw::make_rsrc(obase + (rows_left > 0 ? i0 * ostride : 0), orec);
 #pragma unroll
-      for (int rd = 0; rd < ROUNDS; ++rd) {
-        const int seg = (rd * NW + wave) * 1024;
-        hw::dma_tile16(qr, hw::lds_addr(sQ + seg), dma_q[rd], 0);
-        hw::dma_tile16(orr, hw::lds_addr(sO + seg), dma_o[rd], 0);
-      }
-      if (wave == 0) {
-        const uint32_t r4 = static_cast<uint32_t>(min(i0 + lane, q_len - 1)) * 4;
-        hw::dma_dword(reinterpret_cast<const int*>(bp.lse + rowbase), hw::lds_addr(sL), r4);
-        hw::dma_dword(reinterpret_cast<const int*>(bp.delta + rowbase), hw::lds_addr(sE), r4);
-        if (doc_mask) hw::dma_dword(doc, hw::lds_addr(sD), r4);
-      }
-    };
+    for (int rd = 0; rd < ROUNDS; ++rd) {
+      const int seg = (rd * NW + wave) * 1024;
+      hw::dma_tile16(qr, hw::lds_addr(sQ + seg), dma_q[rd], 0);
+      hw::dma_tile16(orr, hw::lds_addr(sO + seg), dma_o[rd], 0);
+    }
+    if (wave == 0) {
+      const uint32_t r4 = static_cast<uint32_t>(min(i0 + lane, q_len - 1)) * 4;
+      hw::dma_dword(reinterpret_cast<const int*>(bp.lse + rowbase), hw::lds_addr(sL), r4);
+      hw::dma_dword(reinterpret_cast<const int*>(bp.delta + rowbase), hw::lds_addr(sE), r4);
+      if (doc_mask) hw::dma_dword(doc, hw::lds_addr(sD), r4);
+    }
+  };
 
-    auto compute = [&](int st, int m, const char* sQ, const char* sO, const float* sL,
-                       const float* sE, const int* sD) {
-      if (m < 0) return;
-      const bool masked = masked_at(st, m);
-      const int i0 = m * BLK + (st % SPB) * kStageKeys;
+  auto compute = [&](int m, int h, int sub, bool masked, const char* sQ, const char* sO,
+                     const float* sL, const float* sE, const int* sD) {
+    if (m < 0) return;
+    const ScoreConsts sc = make_score_consts(p, h);
+    const int i0 = m * BLK + sub * kStageKeys;
 
-      // S = Q K^T and dP = dO V^T for the stage's 64 query rows
-      f32x16 s[2], dpm[2];
+    // Two halves of 32 query rows each (it), one after the other: the
+    // live fp32 tiles per half are one S and one dP tile, which leaves the
+    // compiler registers to keep several LDS reads in flight.
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        s[it] = f32x16{};
-        dpm[it] = f32x16{};
+    for (int it = 0; it < 2; ++it) {
+      // S = Q K^T and dP = dO V^T for rows [32 it, 32 it + 32) of the stage
+      f32x16 s = f32x16{}, dpm = f32x16{};
+      u32x4 qa[DK], oa[DK];
+#pragma unroll
+      for (int dd = 0; dd < DK; ++dd) {
+        qa[dd] = *reinterpret_cast<const u32x4*>(sQ + k_rd[dd] + it * 32 * RB);
+        oa[dd] = *reinterpret_cast<const u32x4*>(sO + k_rd[dd] + it * 32 * RB);
       }
 #pragma unroll
       for (int dd = 0; dd < DK; ++dd) {
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(sQ + k_rd[dd] + it * 32 * RB);
-          s[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), kf[dd],
-                                                          s[it], 0, 0, 0);
-          const u32x4 o = *reinterpret_cast<const u32x4*>(sO + k_rd[dd] + it * 32 * RB);
-          dpm[it] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o), vf[dd],
-                                                            dpm[it], 0, 0, 0);
-        }
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, qa[dd]), kf[dd],
+                                                    s, 0, 0, 0);
+        dpm = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, oa[dd]), vf[dd],
+                                                      dpm, 0, 0, 0);
       }
 
-      // element (it, r): query row i0 + 32 it + 8 (r / 4) + 4 g + r % 4
-      bf16x8 pb[4], tb[4];
+      // element r: query row i0 + 32 it + 8 (r / 4) + 4 g + r % 4
 #pragma unroll
-      for (int it = 0; it < 2; ++it)
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int il = 32 * it + 8 * r4 + 4 * g;  // first of 4 consecutive rows
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(sL + il);
+        const f32x4 del4 = *reinterpret_cast<const f32x4*>(sE + il);
+        int4 d4 = {dj, dj, dj, dj};
+        if (doc_mask && masked) d4 = *reinterpret_cast<const int4*>(sD + il);
+        const int dqs[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int il = 32 * it + 8 * r4 + 4 * g;  // first of 4 consecutive rows
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(sL + il);
-          const f32x4 del4 = *reinterpret_cast<const f32x4*>(sE + il);
-          int4 d4 = {dj, dj, dj, dj};
-          if (doc_mask && masked) d4 = *reinterpret_cast<const int4*>(sD + il);
-          const int dqs[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const int r = 4 * r4 + c;
-            const int irow = i0 + il + c;
-            float x = s[it][r], fp = 1.0f;
-            if constexpr (SCORE == FA_SCORE_ALIBI) {
-              x = __builtin_fmaf(x, sc.c, sc.slope2 * static_cast<float>(j - irow));
-            } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
-              const float e = exp2_hw(x * (2.0f * sc.cap_in * kLog2e));
-              const float tt = __builtin_amdgcn_rcpf(e + 1.0f);
-              x = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out);
-              fp = 4.0f * tt * (1.0f - tt);
-            } else {
-              x *= sc.c;
-            }
-            bool ok = true;
-            if (masked)
-              ok = (static_cast<unsigned>(irow - ilo) < ispan) & (dqs[c] == dj) & (irow < q_len);
-            const float l2 = lse4[c] == FA_NEG_INF ? __builtin_inff() : lse4[c] * kLog2e;
-            const float pr = ok ? exp2_hw(x - l2) : 0.0f;
-            s[it][r] = pr;                                     // P
-            dpm[it][r] = pr * (dpm[it][r] - del4[c]) * fp;     // dT
+        for (int c = 0; c < 4; ++c) {
+          const int r = 4 * r4 + c;
+          const int irow = i0 + il + c;
+          float x = s[r], fp = 1.0f;
+          if constexpr (SCORE == FA_SCORE_ALIBI) {
+            x = __builtin_fmaf(x, sc.c, sc.slope2 * static_cast<float>(j - irow));
+          } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
+            const float e = exp2_hw(x * (2.0f * sc.cap_in * kLog2e));
+            const float tt = __builtin_amdgcn_rcpf(e + 1.0f);
+            x = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out);
+            fp = 4.0f * tt * (1.0f - tt);
+          } else {
+            x *= sc.c;
           }
+          bool ok = true;
+          if (masked)
+            ok = (static_cast<unsigned>(irow - ilo) < ispan) & (dqs[c] == dj) & (irow < q_len);
+          const float l2 = lse4[c] == FA_NEG_INF ? __builtin_inff() : lse4[c] * kLog2e;
+          const float pr = ok ? exp2_hw(x - l2) : 0.0f;
+          s[r] = pr;                                  // P
+          dpm[r] = pr * (dpm[r] - del4[c]) * fp;      // dT
         }
+      }
+      bf16x8 pb[2], tb[2];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int h2 = 0; h2 < 2; ++h2) {
         f32x8 pf, tf;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pf[e] = s[kk >> 1][(kk & 1) * 8 + e];
-          tf[e] = dpm[kk >> 1][(kk & 1) * 8 + e];
+          pf[e] = s[h2 * 8 + e];
+          tf[e] = dpm[h2 * 8 + e];
         }
-        pb[kk] = __builtin_convertvector(pf, bf16x8);
-        tb[kk] = __builtin_convertvector(tf, bf16x8);
+        pb[h2] = __builtin_convertvector(pf, bf16x8);
+        tb[h2] = __builtin_convertvector(tf, bf16x8);
       }
 
-      // dV^T += dO^T P and dK^T += Q^T dT (4 k-steps of 16 query rows)
+      // dV^T += dO^T P and dK^T += Q^T dT over these 32 rows (2 k-steps
+      // of 16)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int kk = 2 * it + h2;
+        i16x8 o8[DT], q8[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const i16x4 olo = lds_read_tr(sO + v_rd[0][dt] + kk * 16 * RB);
           const i16x4 ohi = lds_read_tr(sO + v_rd[1][dt] + kk * 16 * RB);
-          const i16x8 o8 = {olo[0], olo[1], olo[2], olo[3], ohi[0], ohi[1], ohi[2], ohi[3]};
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o8), pb[kk],
-                                                           dv[dt], 0, 0, 0);
+          o8[dt] = i16x8{olo[0], olo[1], olo[2], olo[3], ohi[0], ohi[1], ohi[2], ohi[3]};
           const i16x4 qlo = lds_read_tr(sQ + v_rd[0][dt] + kk * 16 * RB);
           const i16x4 qhi = lds_read_tr(sQ + v_rd[1][dt] + kk * 16 * RB);
-          const i16x8 q8 = {qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q8), tb[kk],
-                                                           dk[dt], 0, 0, 0);
+          q8[dt] = i16x8{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, o8[dt]),
+                                                           pb[h2], dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, q8[dt]),
+                                                           tb[h2], dk[dt], 0, 0, 0);
         }
       }
-    };
-
-    int m_cur = nstages > 0 ? stage_block(0) : -1;
-    if (nstages > 0) issue(0, m_cur, sQ0, sO0, sL0, sE0, sD0);
-    for (int st = 0; st < nstages; st += 2) {
-      __builtin_amdgcn_s_waitcnt(0x0f70);
-      __syncthreads();
-      int m_nxt = st + 1 >= nstages ? -1 : (st + 1) % SPB == 0 ? stage_block(st + 1) : m_cur;
-      if (st + 1 < nstages) issue(st + 1, m_nxt, sQ1, sO1, sL1, sE1, sD1);
-      compute(st, m_cur, sQ0, sO0, sL0, sE0, sD0);
-      if (st + 1 >= nstages) break;
-      m_cur = m_nxt;
-      __builtin_amdgcn_s_waitcnt(0x0f70);
-      __syncthreads();
-      m_nxt = st + 2 >= nstages ? -1 : (st + 2) % SPB == 0 ? stage_block(st + 2) : m_cur;
-      if (st + 2 < nstages) issue(st + 2, m_nxt, sQ0, sO0, sL0, sE0, sD0);
-      compute(st + 1, m_cur, sQ1, sO1, sL1, sE1, sD1);
-      m_cur = m_nxt;
     }
-    // the next head's first loads reuse buffer 0
+  };
+
+  int m_cur = -1, h_cur = 0, sub_cur = 0, m_nxt = -1, h_nxt = 0, sub_nxt = 0;
+  bool mk_cur = false, mk_nxt = false;
+  if (total > 0) {
+    next_stage(m_cur, h_cur, sub_cur, mk_cur);
+    issue(m_cur, h_cur, sub_cur, sQ0, sO0, sL0, sE0, sD0);
+  }
+  for (int st = 0; st < total; st += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's DMA landed
+    __syncthreads();                     // every lane's DMA landed; buffer 1 free
+    if (st + 1 < total) {
+      next_stage(m_nxt, h_nxt, sub_nxt, mk_nxt);
+      issue(m_nxt, h_nxt, sub_nxt, sQ1, sO1, sL1, sE1, sD1);
+    }
+    compute(m_cur, h_cur, sub_cur, mk_cur, sQ0, sO0, sL0, sE0, sD0);
+    if (st + 1 >= total) break;
+    m_cur = m_nxt;
+    h_cur = h_nxt;
+    sub_cur = sub_nxt;
+    mk_cur = mk_nxt;
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
+    if (st + 2 < total) {
+      next_stage(m_nxt, h_nxt, sub_nxt, mk_nxt);
+      issue(m_nxt, h_nxt, sub_nxt, sQ0, sO0, sL0, sE0, sD0);
+    }
+    compute(m_cur, h_cur, sub_cur, mk_cur, sQ1, sO1, sL1, sE1, sD1);
+    m_cur = m_nxt;
+    h_cur = h_nxt;
+    sub_cur = sub_nxt;
+    mk_cur = mk_nxt;
   }
 
   if (j_ok) {
