@@ -9,7 +9,8 @@ timed region starts. The JSON line reports live-block TFLOP/s:
 
 (partial blocks count their full area), its fraction of the bf16 MFMA peak,
 the speedup of the same kernel over a dense causal block mask at the same
-shape, and the oracle timed on the host cores as a baseline.
+shape, the oracle timed on the host cores as a baseline, and (outside the
+step) the backward's time and algorithmic rate.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
 """
@@ -164,6 +165,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-reference-masks", action="store_true",
                     help="skip the dense-causal and no-skip timings")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the timing of the backward (dQ, dK, dV)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB copy kernel (for counter "
                          "calibration under rocprofv3 --pmc)")
@@ -240,6 +243,43 @@ def main(argv=None) -> int:
     value = live_flops / (step_ms * 1e-3) / 1e12
     achieved = live_flops / (fwd_avg * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+
+    # backward of the same attention (not part of the step): one
+    # fa_flex_attention_bwd call per repetition, O and LSE from an unsplit
+    # forward, a seeded upstream gradient
+    bwd = None
+    if not a.no_backward and w.dtype == "bf16" and w.block_m == w.block_n:
+        gen = torch.Generator(device=dev).manual_seed(w.seed)
+        dout = torch.randn(qd.shape, generator=gen, device=dev).to(qd.dtype)
+        o1, l1 = fa.flex_attention(qd, kd, vd, bm, score_mod=score,
+                                   scale=w.scale, num_splits=1)
+
+        def bwd_call():
+            return fa.flex_attention_backward(qd, kd, vd, o1, l1, dout, bm,
+                                              score_mod=score, scale=w.scale)
+        for _ in range(2):
+            bwd_call()
+        reps = max(3, min(a.steps, 20))
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        b0.record(stream)
+        for _ in range(reps):
+            bwd_call()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = b0.elapsed_time(b1) / reps
+        # algorithmic work: five products per live tile (S recomputed, dP,
+        # dV, dK, dQ) = 2.5 x the forward's two
+        bwd_flops = 2.5 * live_flops
+        bwd = {"ms": round(bwd_ms, 5), "reps": reps,
+               "flops_per_call": bwd_flops,
+               "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
+               "frac_of_peak": round(bwd_flops / (bwd_ms * 1e-3) / 1e12 / peak, 4),
+               "ratio_to_fwd": round(bwd_ms / fwd_avg, 3)}
+        log(f"[bench] backward {bwd_ms:.4f} ms ({bwd['tflops']} TFLOP/s "
+            f"algorithmic)")
+        del o1, l1, dout
 
     extra = {}
     if not a.no_reference_masks:
@@ -333,6 +373,7 @@ def main(argv=None) -> int:
                      "kernel": FWD_KERNEL,
                      "per_launch_flops": live_flops},
         "cpu_baseline": cpu,
+        "backward": bwd,
     }
     print(json.dumps(line), flush=True)
     return 0

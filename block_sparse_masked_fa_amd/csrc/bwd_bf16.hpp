@@ -13,10 +13,11 @@
 // The forward's LSE makes P available per tile with no running maximum, so
 // every tile is independent and two kernels avoid atomics:
 //   * bwd_dq_kernel: one workgroup per (query block, head), the forward's
-//     work split and key-block lists. Per 64-key stage: S^T = K Q^T and
-//     dP^T = V dO^T (K and V rows as MFMA A operands from LDS, Q^T and dO^T
-//     resident as B operands), then dQ^T += K^T dT^T (K read transposed,
-//     ds_read_b64_tr_b16, exactly as the forward reads V).
+//     work split and key-block lists. It first forms delta_i from its rows
+//     of O and dO (and stores it for the next kernel). Per 64-key stage:
+//     S^T = K Q^T and dP^T = V dO^T (K and V rows as MFMA A operands from
+//     LDS, Q^T and dO^T resident as B operands), then dQ^T += K^T dT^T (K
+//     read transposed, ds_read_b64_tr_b16, exactly as the forward reads V).
 //   * bwd_dkdv_kernel: one workgroup per (key block, key head), wave w owns
 //     keys [32w, 32w + 32); it walks the transposed lists (the query blocks
 //     that name the key block) and, with grouped heads, every query head of
@@ -51,7 +52,7 @@ __device__ __forceinline__ bool xcd_kv_item(const FwdLaunch& p, int& b, int& hk,
 
 // ---------------------------------------------------------------- dQ
 template <int D, int BLK, int SCORE>
-__global__ __launch_bounds__(BLK * 2, 1) void bwd_dq_kernel(const BwdLaunch bp) {
+__global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLaunch bp) {
   const FwdLaunch& p = bp.f;
   constexpr int NW = BLK / 32;
   constexpr int NT = NW * 64;
@@ -114,7 +115,25 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dq_kernel(const BwdLaunch bp) 
   // log2-domain LSE (a row without keys: +inf, so that every P is 0)
   const float lse_i = i_ok ? bp.lse[orow] : FA_NEG_INF;
   const float lse2 = lse_i == FA_NEG_INF ? __builtin_inff() : lse_i * kLog2e;
-  const float delta_i = i_ok ? bp.delta[orow] : 0.0f;
+  // delta_i = dO_i . O_i (fp32), the row term of dS; written for the dK / dV
+  // kernel, which runs after this one. Each lane holds the row's d in
+  // [16 dk + 8 g, +8): a partial dot, then the sum with lane ^ 32.
+  float delta_i;
+  {
+    const __bf16* orow_p = static_cast<const __bf16*>(bp.o) + (i_ok ? orow : 0) * D;
+    float part = 0.0f;
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const bf16x8 ov = __builtin_bit_cast(
+          bf16x8, i_ok ? *reinterpret_cast<const u32x4*>(orow_p + dk * 16 + g * 8) : z);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        part = __builtin_fmaf(static_cast<float>(ov[e]), static_cast<float>(dof[dk][e]), part);
+    }
+    delta_i = row_pair_sum(part);
+    if (i_ok && g == 0) bp.delta[orow] = delta_i;
+  }
   const int di = doc_mask ? doc[i_ok ? i : 0] : 0;
 
   const int bb = p.Bm == 1 ? 0 : w.b;
@@ -209,50 +228,51 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dq_kernel(const BwdLaunch bp) 
     const bool masked = masked_at(it, n);
     const int j0 = n * BLK + (st % SPB) * kStageKeys;
 
-    // S^T = K Q^T and dP^T = V dO^T for the stage's 64 keys
-    f32x16 s[2], dp[2];
+    // Two halves of 32 keys each (jt), one after the other (one S and one
+    // dP tile live at a time); each half's LDS operands are read ahead of
+    // its MFMAs.
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
-      s[jt] = f32x16{};
-      dp[jt] = f32x16{};
-    }
+      // S^T = K Q^T and dP^T = V dO^T for keys [32 jt, 32 jt + 32)
+      f32x16 s = f32x16{}, dp = f32x16{};
+      u32x4 ka[DK], va[DK];
 #pragma unroll
-    for (int dk = 0; dk < DK; ++dk) {
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + k_rd[dk] + jt * 32 * RB);
-        s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[dk],
-                                                        s[jt], 0, 0, 0);
-        const u32x4 b = *reinterpret_cast<const u32x4*>(sV + k_rd[dk] + jt * 32 * RB);
-        dp[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, b), dof[dk],
-                                                         dp[jt], 0, 0, 0);
+      for (int dk = 0; dk < DK; ++dk) {
+        ka[dk] = *reinterpret_cast<const u32x4*>(sK + k_rd[dk] + jt * 32 * RB);
+        va[dk] = *reinterpret_cast<const u32x4*>(sV + k_rd[dk] + jt * 32 * RB);
       }
-    }
-
-    // score_mod into the log2 domain, and its derivative (soft-cap)
-    float fp[2][16];
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
+      for (int dk = 0; dk < DK; ++dk) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[dk]), qf[dk], s,
+                                                    0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[dk]), dof[dk],
+                                                     dp, 0, 0, 0);
+      }
+
+      // score_mod into the log2 domain and its derivative (soft-cap); key of
+      // element r: j0 + 32 jt + 8 (r / 4) + 4 g + r % 4
+      float fp[16];
+      // ALiBi bias slope2 (j - i) = bias0 + slope2 (8 (r / 4) + r % 4)
+      const float bias0 =
+          SCORE == FA_SCORE_ALIBI ? sc.slope2 * static_cast<float>(j0 + 4 * g + 32 * jt - i) : 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        fp[jt][r] = 1.0f;
+        fp[r] = 1.0f;
         if constexpr (SCORE == FA_SCORE_ALIBI) {
-          const float bj = sc.slope2 * static_cast<float>(j0 + 4 * g + 32 * jt + 8 * (r >> 2) + (r & 3) - i);
-          s[jt][r] = __builtin_fmaf(s[jt][r], sc.c, bj);
+          const float bj =
+              __builtin_fmaf(sc.slope2, static_cast<float>(8 * (r >> 2) + (r & 3)), bias0);
+          s[r] = __builtin_fmaf(s[r], sc.c, bj);
         } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
-          const float e = exp2_hw(s[jt][r] * (2.0f * sc.cap_in * kLog2e));
+          const float e = exp2_hw(s[r] * (2.0f * sc.cap_in * kLog2e));
           const float tt = __builtin_amdgcn_rcpf(e + 1.0f);  // tanh = 1 - 2 tt
-          s[jt][r] = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out);
-          fp[jt][r] = 4.0f * tt * (1.0f - tt);               // 1 - tanh^2
+          s[r] = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out);
+          fp[r] = 4.0f * tt * (1.0f - tt);                   // 1 - tanh^2
         } else {
-          s[jt][r] *= sc.c;
+          s[r] *= sc.c;
         }
       }
-    if (masked) {
-      const int lo = lo_abs - (j0 + 4 * g);
-      const unsigned sp = span;
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
+      if (masked) {
+        const int lo = lo_abs - (j0 + 4 * g);
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const int jl = 32 * jt + 8 * r4;
@@ -263,36 +283,42 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dq_kernel(const BwdLaunch bp) 
           }
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const bool ok = (static_cast<unsigned>(jl + c - lo) < sp) & (dj[c] == di);
-            s[jt][4 * r4 + c] = ok ? s[jt][4 * r4 + c] : FA_NEG_INF;
+            const bool ok = (static_cast<unsigned>(jl + c - lo) < span) & (dj[c] == di);
+            s[4 * r4 + c] = ok ? s[4 * r4 + c] : FA_NEG_INF;
           }
         }
-    }
-
-    // P, dS = P (dP - delta), dT = dS score_mod' -> bf16 B operands
-    bf16x8 tb[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      f32x8 tf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int jt = kk >> 1, r = (kk & 1) * 8 + e;
-        const float pr = exp2_hw(s[jt][r] - lse2);
-        tf[e] = pr * (dp[jt][r] - delta_i) * fp[jt][r];
       }
-      tb[kk] = __builtin_convertvector(tf, bf16x8);
-    }
 
-    // dQ^T += K^T dT^T (4 k-steps of 16 keys; K read transposed)
+      // P, dS = P (dP - delta), dT = dS score_mod' -> bf16 B operands
+      bf16x8 tb[2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+      for (int h2 = 0; h2 < 2; ++h2) {
+        f32x8 tf;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const i16x4 lo = lds_read_tr(sK + v_rd[0][dt] + kk * 16 * RB);
-        const i16x4 hi = lds_read_tr(sK + v_rd[1][dt] + kk * 16 * RB);
-        const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), tb[kk],
-                                                         dq[dt], 0, 0, 0);
+        for (int e = 0; e < 8; ++e) {
+          const int r = h2 * 8 + e;
+          const float pr = exp2_hw(s[r] - lse2);
+          tf[e] = pr * (dp[r] - delta_i) * fp[r];
+        }
+        tb[h2] = __builtin_convertvector(tf, bf16x8);
+      }
+
+      // dQ^T += K^T dT^T over these 32 keys (2 k-steps of 16; K read
+      // transposed)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int kk = 2 * jt + h2;
+        i16x8 a8[DT];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const i16x4 lo = lds_read_tr(sK + v_rd[0][dt] + kk * 16 * RB);
+          const i16x4 hi = lds_read_tr(sK + v_rd[1][dt] + kk * 16 * RB);
+          a8[dt] = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8[dt]),
+                                                           tb[h2], dq[dt], 0, 0, 0);
       }
     }
   };

@@ -1,7 +1,4 @@
 // Backward preparation, before the gradient kernels:
-//   * delta_i = sum_d dO[i, d] * O[i, d] (fp32): the row term of the softmax
-//     gradient, dS_ij = P_ij (dP_ij - delta_i), since sum_j P_ij dP_ij =
-//     dO_i . O_i;
 //   * the block lists transposed: for each key block n, the query blocks m
 //     whose row lists name n (partial and full apart), in ascending m. The
 //     dK / dV kernel walks them. Built from the forward's lists (whatever
@@ -17,24 +14,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-
-// one wavefront per row
-template <int D>
-__global__ __launch_bounds__(kThreads) void delta_kernel(const BwdLaunch p, int64_t rows) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int lane = threadIdx.x & 63;
-  constexpr int E = D / 64;
-  const __bf16* o = static_cast<const __bf16*>(p.o) + row * D + lane * E;
-  const __bf16* d = static_cast<const __bf16*>(p.dout) + row * D + lane * E;
-  float acc = 0.0f;
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    acc = __builtin_fmaf(static_cast<float>(o[e]), static_cast<float>(d[e]), acc);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-  if (lane == 0) p.delta[row] = acc;
-}
 
 __global__ __launch_bounds__(kThreads) void clear_kernel(unsigned char* s, int64_t n) {
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; t < n;
@@ -133,15 +112,7 @@ int launch_zero_fill(void* dst, uint64_t bytes, void* stream) {
 int launch_bwd_prepare(const BwdLaunch& p, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const FwdLaunch& f = p.f;
-  const int64_t rows = static_cast<int64_t>(f.B) * f.H * f.q_len;
   const dim3 blk(kThreads);
-  if (rows > 0) {
-    const dim3 grid(static_cast<unsigned>((rows + kWaves - 1) / kWaves));
-    if (f.D == 64)
-      hipLaunchKernelGGL((delta_kernel<64>), grid, blk, 0, s, p, rows);
-    else
-      hipLaunchKernelGGL((delta_kernel<128>), grid, blk, 0, s, p, rows);
-  }
   const int64_t lrows = static_cast<int64_t>(f.Bm) * f.Hm * f.nqb;
   const int64_t cells = lrows * f.nkvb;
   if (cells > 0) {

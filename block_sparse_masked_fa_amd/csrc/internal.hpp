@@ -76,7 +76,7 @@ struct BwdLaunch {
   const void* o;         // forward output, [B, H, q_len, D] contiguous
   const float* lse;      // forward LSE, [B, H, q_len]
   const void* dout;      // dO, [B, H, q_len, D] contiguous
-  float* delta;          // [B, H, q_len]: rowsum(dO * O), written first
+  float* delta;          // [B, H, q_len]: rowsum(dO * O), written by the dQ kernel
   // per key block, the query blocks that list it ([Bm, Hm, nkvb] and
   // [Bm, Hm, nkvb, nqb]); full_* NULL when the mask has no full lists
   int32_t* qnum;
@@ -98,7 +98,7 @@ int launch_fwd_bf16_d64(const FwdLaunch& p, void* stream);
 int launch_fwd_bf16_d128(const FwdLaunch& p, void* stream);
 int launch_fwd_fp32(const FwdLaunch& p, void* stream);
 int launch_split_combine(const CombineLaunch& p, void* stream);
-int launch_bwd_prepare(const BwdLaunch& p, void* stream);  // delta, transposed lists
+int launch_bwd_prepare(const BwdLaunch& p, void* stream);  // transposed lists
 int launch_zero_fill(void* dst, uint64_t bytes, void* stream);  // 16-byte aligned
 int launch_bwd_bf16_d64(const BwdLaunch& p, void* stream);
 int launch_bwd_bf16_d128(const BwdLaunch& p, void* stream);

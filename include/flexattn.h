@@ -288,9 +288,10 @@ fa_status fa_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
  *   dk, dv     device bf16 [B, H_kv, kv_len, D], contiguous, written (zero
  *              for keys that no allowed pair reaches).
  *   All device arrays 16-byte aligned; outputs must not overlap inputs.
- * Five kernel launches (delta = rowsum(dO * O), two that transpose the
- * block lists into per-key-block lists of query blocks, then dQ, then
- * dK / dV); asynchronous. */
+ * Five kernel launches: three that transpose the block lists into
+ * per-key-block lists of query blocks (clear, scatter, compact), the dQ
+ * kernel (which also forms delta = rowsum(dO * O)), then the dK / dV
+ * kernel; asynchronous. */
 fa_status fa_flex_attention_bwd(
     int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t q_len,
     int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
