@@ -199,7 +199,7 @@ def fa_flex_attention_bwd(dtype: int, B: int, H: int, H_kv: int, q_len: int,
                           kv_len: int, D: int, q: int, q_stride, k: int,
                           k_stride, v: int, v_stride, scale: float,
                           bm: C.fa_block_mask, score: Optional[C.fa_score_mod],
-                          o: int, lse: int, dout: int,
+                          dq_kv_order: int, o: int, lse: int, dout: int,
                           workspace: Optional[int], workspace_bytes: int,
                           dq: int, dk: int, dv: int,
                           stream: Optional[int]) -> int:
@@ -207,8 +207,8 @@ def fa_flex_attention_bwd(dtype: int, B: int, H: int, H_kv: int, q_len: int,
         dtype, B, H, H_kv, q_len, kv_len, D,
         q, C.Stride3(*q_stride), k, C.Stride3(*k_stride),
         v, C.Stride3(*v_stride), scale, ctypes.byref(bm),
-        ctypes.byref(score) if score is not None else None, o, lse, dout,
-        workspace, workspace_bytes, dq, dk, dv, stream)
+        ctypes.byref(score) if score is not None else None, dq_kv_order, o,
+        lse, dout, workspace, workspace_bytes, dq, dk, dv, stream)
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, q_len: int,
@@ -252,6 +252,10 @@ class BlockMask:
         self.full_kv_indices = full_kv_indices
         self.num_q_blocks = kv_num_blocks.shape[-1]
         self.num_kv_blocks = kv_indices.shape[-1]
+        # order of the backward's dQ accumulation over key blocks (tensorplay
+        # create_block_mask page, dq_kv_order): True descending, False
+        # ascending. Either is deterministic and needs no stored metadata.
+        self.dq_kv_order = True
 
     @property
     def separate_full_blocks(self) -> bool:
@@ -307,14 +311,22 @@ class BlockMask:
 def create_block_mask(mask_mod, B: Optional[int], H: Optional[int],
                       Q_LEN: int, KV_LEN: int, device="cuda",
                       BLOCK_SIZE: Union[int, Tuple[int, int]] = 128,
-                      separate_full_blocks: bool = True, *, window=None,
+                      separate_full_blocks: bool = True,
+                      compute_dq_write_order: bool = False,
+                      dq_kv_order: bool = True, *, window=None,
                       doc_id=None) -> BlockMask:
     """Build a block mask on the device (one call of fa_create_block_mask).
 
     ``mask_mod``: a :class:`MaskMod` or one of "causal", "sliding_window" /
     "local_window" (with ``window``), "document" (with ``doc_id``, ``[L]`` or
     per batch entry ``[B, L]``), "none". ``B``/``H`` None broadcast the mask
-    over every batch entry / head."""
+    over every batch entry / head.
+
+    ``dq_kv_order`` picks the order in which the backward sums each dQ row
+    over its key blocks (True: descending block index, False: ascending).
+    ``compute_dq_write_order`` is accepted for the page's signature: the
+    backward here accumulates every dQ row in one workgroup, so its order
+    needs no precomputed metadata and the flag changes nothing."""
     mask = _mask_from(mask_mod, window, doc_id)
     device = torch.device(device)
     if device.type != "cuda":
@@ -345,8 +357,10 @@ def create_block_mask(mask_mod, B: Optional[int], H: Optional[int],
                                      bn_, int(separate_full_blocks), cbm,
                                      _stream_handle(device)),
                 "fa_create_block_mask")
-    return BlockMask(mask, Bm, Hm, Q_LEN, KV_LEN, bm_, bn_, num, idx, fnum,
-                     fidx)
+    out = BlockMask(mask, Bm, Hm, Q_LEN, KV_LEN, bm_, bn_, num, idx, fnum,
+                    fidx)
+    out.dq_kv_order = bool(dq_kv_order)
+    return out
 
 
 _DTYPES = {torch.bfloat16: C.FA_BF16, torch.float32: C.FA_FP32}
@@ -425,14 +439,16 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             o: torch.Tensor, lse: torch.Tensor,
                             dout: torch.Tensor, block_mask: BlockMask,
-                            score_mod=None, scale: Optional[float] = None):
+                            score_mod=None, scale: Optional[float] = None,
+                            dq_kv_order: Optional[bool] = None):
     """Gradients ``(dQ, dK, dV)`` of ``O = flex_attention(q, k, v,
     block_mask, score_mod, scale)`` for the upstream gradient ``dout``.
 
     bf16 only; ``o`` and ``lse`` are what the forward returned for the same
     arguments; ``block_mask`` needs equal query and key block sizes (64 or
     128). One fa_flex_attention_bwd call with a workspace allocated here;
-    the results are deterministic."""
+    the results are deterministic. ``dq_kv_order`` (default: the block
+    mask's) is the order of dQ's sum over key blocks, True descending."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, H, S, D)")
     if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype
@@ -461,6 +477,8 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     dq = torch.empty((B, H, q_len, D), dtype=q.dtype, device=q.device)
     dk = torch.empty((B, H_kv, kv_len, D), dtype=q.dtype, device=q.device)
     dv = torch.empty_like(dk)
+    if dq_kv_order is None:
+        dq_kv_order = getattr(block_mask, "dq_kv_order", True)
     bm = block_mask.to_c()
     nbytes = fa_bwd_workspace_bytes(B, H, q_len, bm)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
@@ -469,7 +487,8 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             C.FA_BF16, B, H, H_kv, q_len, kv_len, D,
             q.data_ptr(), q.stride()[:3], k.data_ptr(), k.stride()[:3],
             v.data_ptr(), v.stride()[:3], float(scale), bm, score.to_c(),
-            o.data_ptr(), lse.data_ptr(), dout.data_ptr(), ws.data_ptr(),
+            int(bool(dq_kv_order)), o.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), ws.data_ptr(),
             nbytes, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
             _stream_handle(q.device))
     C.check(st, "fa_flex_attention_bwd")

@@ -152,16 +152,16 @@ fa_status fa_flex_attention_bwd(
     int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
     const void* k, const int64_t k_stride[3], const void* v,
     const int64_t v_stride[3], float scale, const fa_block_mask* bm,
-    const fa_score_mod* score, const void* o, const float* lse,
-    const void* dout, void* workspace, uint64_t workspace_bytes, void* dq,
-    void* dk, void* dv, void* stream) {
+    const fa_score_mod* score, int32_t dq_kv_order, const void* o,
+    const float* lse, const void* dout, void* workspace,
+    uint64_t workspace_bytes, void* dq, void* dk, void* dv, void* stream) {
   std::string msg;
   fa::BwdLaunch p{};
   bool nothing = false;
   int st = fa::check_flex_attention_bwd(
       dtype, B, H, H_kv, q_len, kv_len, D, q, q_stride, k, k_stride, v,
-      v_stride, scale, bm, score, o, lse, dout, workspace, workspace_bytes, dq,
-      dk, dv, &p, &nothing, &msg);
+      v_stride, scale, bm, score, dq_kv_order, o, lse, dout, workspace,
+      workspace_bytes, dq, dk, dv, &p, &nothing, &msg);
   if (st != FA_OK) return finish(st, msg);
   if (nothing) {
     if (p.zero_bytes == 0) return FA_OK;

@@ -187,16 +187,44 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLau
     dma_v[rd] = static_cast<uint32_t>(r * vstride) + col;
   }
 
-  auto block_at = [&](int it) -> int { return it < np ? pl[it] : fl[it - np]; };
-  auto masked_at = [&](int it, int n) -> bool { return it < np || (n + 1) * BLK > kv_len; };
-  auto stage_block = [&](int st) -> int {
-    const int b = block_at(st / SPB);
-    return static_cast<unsigned>(b) < static_cast<unsigned>(nkvb) ? b : -1;
+  // dQ accumulation order: the row's live key blocks, the partial and the
+  // full list merged by block index, in ascending (dq_kv_order 0) or
+  // descending (1) order; descending also takes a block's later 64 keys
+  // first. Each list is walked in its own order, which the builder sorts.
+  // Fixed for given inputs, so dQ is bitwise reproducible.
+  const bool desc = bp.dq_kv_order != 0;
+  int ip = desc ? np - 1 : 0;
+  int ifl = desc ? nf - 1 : 0;
+  int c_n = -1, c_sub = 0;
+  bool c_masked = false;
+  // the next stage: key block n (-1: an index outside [0, NKVB), skipped),
+  // its 64-key stage sub, and whether mask_mod applies. Called once per
+  // stage, in order, nstages times.
+  auto next_stage = [&](int& n, int& sub, bool& masked) {
+    if (c_sub == 0) {
+      const bool p_left = desc ? ip >= 0 : ip < np;
+      const bool f_left = desc ? ifl >= 0 : ifl < nf;
+      bool take_p = p_left;
+      if (p_left && f_left) {
+        const int a = pl[ip], bq = fl[ifl];
+        take_p = desc ? a > bq : a < bq;
+      }
+      const int bsel = take_p ? pl[ip] : fl[ifl];
+      if (take_p) ip += desc ? -1 : 1;
+      else ifl += desc ? -1 : 1;
+      c_n = static_cast<unsigned>(bsel) < static_cast<unsigned>(nkvb) ? bsel : -1;
+      c_masked = take_p || (c_n + 1) * BLK > kv_len;
+    }
+    n = c_n;
+    sub = desc ? SPB - 1 - c_sub : c_sub;
+    masked = c_masked;
+    if (++c_sub == SPB) c_sub = 0;
   };
-  auto issue = [&](int st, int n, char* sK, char* sV, int* sD) {
-    const int it = st / SPB;
+  auto issue = [&](int n, int sub, bool masked, char* sK, char* sV, int* sD) {
     if (n < 0) return;
-    const int j0 = n * BLK + (st % SPB) * kStageKeys;
+    const int j0 = n * BLK + sub * kStageKeys;
+    // a stage of a ragged last block may lie wholly past the end: then the
+    // buffers have size 0 and the tiles arrive as zeros
     const int rows_left = kv_len - j0;
     const int krec = rows_left >= kStageKeys ? 0x7fffffff
                      : rows_left <= 0       ? 0
@@ -212,7 +240,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLau
       hw::dma_tile16(kr, hw::lds_addr(sK + seg), dma_k[rd], 0);
       hw::dma_tile16(vr, hw::lds_addr(sV + seg), dma_v[rd], 0);
     }
-    if (doc_mask && masked_at(it, n) && wave == 0) {
+    if (doc_mask && masked && wave == 0) {
       const int j = min(j0 + lane, kv_len - 1);
       hw::dma_dword(doc, hw::lds_addr(sD), static_cast<uint32_t>(j * 4));
     }
@@ -222,11 +250,10 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLau
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
 
-  auto compute = [&](int st, int n, const char* sK, const char* sV, const int* sD) {
-    const int it = st / SPB;
+  auto compute = [&](int n, int sub, bool masked, const char* sK, const char* sV,
+                     const int* sD) {
     if (n < 0) return;
-    const bool masked = masked_at(it, n);
-    const int j0 = n * BLK + (st % SPB) * kStageKeys;
+    const int j0 = n * BLK + sub * kStageKeys;
 
     // Two halves of 32 keys each (jt), one after the other (one S and one
     // dP tile live at a time); each half's LDS operands are read ahead of
@@ -324,22 +351,34 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLau
   };
 
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): setup loads landed
-  int n_cur = nstages > 0 ? stage_block(0) : -1;
-  if (nstages > 0) issue(0, n_cur, sK0, sV0, sDoc0);
+  int n_cur = -1, sub_cur = 0, n_nxt = -1, sub_nxt = 0;
+  bool mk_cur = false, mk_nxt = false;
+  if (nstages > 0) {
+    next_stage(n_cur, sub_cur, mk_cur);
+    issue(n_cur, sub_cur, mk_cur, sK0, sV0, sDoc0);
+  }
   for (int st = 0; st < nstages; st += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-    int n_nxt = st + 1 >= nstages ? -1 : (st + 1) % SPB == 0 ? stage_block(st + 1) : n_cur;
-    if (st + 1 < nstages) issue(st + 1, n_nxt, sK1, sV1, sDoc1);
-    compute(st, n_cur, sK0, sV0, sDoc0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's DMA landed
+    __syncthreads();                     // every lane's DMA landed; buffer 1 free
+    if (st + 1 < nstages) {
+      next_stage(n_nxt, sub_nxt, mk_nxt);
+      issue(n_nxt, sub_nxt, mk_nxt, sK1, sV1, sDoc1);
+    }
+    compute(n_cur, sub_cur, mk_cur, sK0, sV0, sDoc0);
     if (st + 1 >= nstages) break;
     n_cur = n_nxt;
+    sub_cur = sub_nxt;
+    mk_cur = mk_nxt;
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
-    n_nxt = st + 2 >= nstages ? -1 : (st + 2) % SPB == 0 ? stage_block(st + 2) : n_cur;
-    if (st + 2 < nstages) issue(st + 2, n_nxt, sK0, sV0, sDoc0);
-    compute(st + 1, n_cur, sK1, sV1, sDoc1);
+    if (st + 2 < nstages) {
+      next_stage(n_nxt, sub_nxt, mk_nxt);
+      issue(n_nxt, sub_nxt, mk_nxt, sK0, sV0, sDoc0);
+    }
+    compute(n_cur, sub_cur, mk_cur, sK1, sV1, sDoc1);
     n_cur = n_nxt;
+    sub_cur = sub_nxt;
+    mk_cur = mk_nxt;
   }
 
   if (i_ok) {

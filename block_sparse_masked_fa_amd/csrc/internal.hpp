@@ -87,6 +87,7 @@ struct BwdLaunch {
   void* dq;              // [B, H, q_len, D] contiguous, bf16
   void* dk;              // [B, H_kv, kv_len, D] contiguous, bf16
   void* dv;
+  int32_t dq_kv_order;   // dQ accumulation over key blocks: 0 ascending, 1 descending
   // no query rows (q_len == 0) but keys: bytes of dk and of dv to clear,
   // nothing else runs
   uint64_t zero_bytes;

@@ -373,12 +373,15 @@ int check_flex_attention_bwd(
     int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
     const void* k, const int64_t k_stride[3], const void* v,
     const int64_t v_stride[3], float scale, const fa_block_mask* bm,
-    const fa_score_mod* score, const void* o, const float* lse,
-    const void* dout, void* workspace, uint64_t workspace_bytes, void* dq,
-    void* dk, void* dv, BwdLaunch* out, bool* nothing_to_do, std::string* msg) {
+    const fa_score_mod* score, int32_t dq_kv_order, const void* o,
+    const float* lse, const void* dout, void* workspace,
+    uint64_t workspace_bytes, void* dq, void* dk, void* dv, BwdLaunch* out,
+    bool* nothing_to_do, std::string* msg) {
   *nothing_to_do = false;
   if (dtype != FA_BF16)
     return fail(msg, FA_ERR_UNSUPPORTED, "the backward is built for bf16 only");
+  if (dq_kv_order != 0 && dq_kv_order != 1)
+    return fail(msg, FA_ERR_INVALID_VALUE, "dq_kv_order must be 0 or 1");
   // the forward's checks (o is only read here; the descriptor field is unused)
   int st = check_flex_attention_fwd(dtype, B, H, H_kv, q_len, kv_len, D, q,
                                     q_stride, k, k_stride, v, v_stride, scale,
@@ -441,6 +444,7 @@ int check_flex_attention_bwd(
   out->dq = dq;
   out->dk = dk;
   out->dv = dv;
+  out->dq_kv_order = dq_kv_order;
   return FA_OK;
 }
 

@@ -68,8 +68,9 @@ int check_flex_attention_bwd(
     int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
     const void* k, const int64_t k_stride[3], const void* v,
     const int64_t v_stride[3], float scale, const fa_block_mask* bm,
-    const fa_score_mod* score, const void* o, const float* lse,
-    const void* dout, void* workspace, uint64_t workspace_bytes, void* dq,
-    void* dk, void* dv, BwdLaunch* out, bool* nothing_to_do, std::string* msg);
+    const fa_score_mod* score, int32_t dq_kv_order, const void* o,
+    const float* lse, const void* dout, void* workspace,
+    uint64_t workspace_bytes, void* dq, void* dk, void* dv, BwdLaunch* out,
+    bool* nothing_to_do, std::string* msg);
 
 }  // namespace fa

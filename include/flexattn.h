@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -268,12 +268,19 @@ fa_status fa_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
  *   dQ = scale dT K,  dK = scale dT^T Q,
  * and with H_kv < H the gradients of a key head sum over its query heads.
  * Deterministic: no atomics; every output row is accumulated by one
- * workgroup in a fixed order, so repeated calls give identical bits.
+ * workgroup in a fixed order, so repeated calls give identical bits. The
+ * order of dQ's accumulation over key blocks is selectable, as with the
+ * create_block_mask page's dq_kv_order (ascending or descending n-block
+ * order); it changes only the rounding.
  *
  *   dtype      FA_BF16 only (FA_ERR_UNSUPPORTED otherwise).
  *   B ... score  as for fa_flex_attention_fwd, with the block mask's
  *              block_m == block_n in {64, 128}; bm and score must be the
  *              ones the forward ran with.
+ *   dq_kv_order  0: each dQ row sums its live key blocks (partial and full
+ *              lists merged by block index) in ascending block order; 1:
+ *              descending, a block's later keys first. Other values:
+ *              FA_ERR_INVALID_VALUE.
  *   o          device bf16 [B, H, q_len, D], contiguous: the forward's output.
  *   lse        device fp32 [B, H, q_len], contiguous: the forward's lse.
  *              Gradients are only meaningful for the o and lse that the
@@ -297,9 +304,9 @@ fa_status fa_flex_attention_bwd(
     int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
     const void* k, const int64_t k_stride[3], const void* v,
     const int64_t v_stride[3], float scale, const fa_block_mask* bm,
-    const fa_score_mod* score, const void* o, const float* lse,
-    const void* dout, void* workspace, uint64_t workspace_bytes, void* dq,
-    void* dk, void* dv, void* stream);
+    const fa_score_mod* score, int32_t dq_kv_order, const void* o,
+    const float* lse, const void* dout, void* workspace,
+    uint64_t workspace_bytes, void* dq, void* dk, void* dv, void* stream);
 
 /* Workspace size of fa_flex_attention_bwd for a block mask: B * H * q_len
  * fp32 (delta), then bm->B * bm->H * NQB * NKVB bytes of tile states and the

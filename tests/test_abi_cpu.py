@@ -388,7 +388,7 @@ def _bwd(**over):
              k_stride=(2 * 256 * 128, 256 * 128, 128), v=FAKE,
              v_stride=(2 * 256 * 128, 256 * 128, 128), scale=0.088,
              bm=bm, score=C.fa_score_mod(kind=C.FA_SCORE_NONE),
-             o=FAKE, lse=FAKE, dout=FAKE, workspace=FAKE,
+             dq_kv_order=1, o=FAKE, lse=FAKE, dout=FAKE, workspace=FAKE,
              workspace_bytes=_bwd_ws_bytes(2, 4, 256, 2, 2), dq=FAKE, dk=FAKE,
              dv=FAKE, stream=None)
     a.update(over)
@@ -398,6 +398,8 @@ def _bwd(**over):
 @needs_lib
 @pytest.mark.parametrize("over,status", [
     (dict(dtype=C.FA_FP32), C.FA_ERR_UNSUPPORTED),
+    (dict(dq_kv_order=2), C.FA_ERR_INVALID_VALUE),
+    (dict(dq_kv_order=-1), C.FA_ERR_INVALID_VALUE),
     (dict(bm=_bm(**{**{f: getattr(_good_bm(), f) for f, _ in
                        C.fa_block_mask._fields_}, "block_n": 64,
                     "num_kv_blocks": 4})), C.FA_ERR_UNSUPPORTED),

@@ -39,7 +39,7 @@ def _doc_t(doc):
     return torch.from_numpy(np.ascontiguousarray(doc)).to(DEV) if doc is not None else None
 
 
-def gpu_fwd_bwd(w, q, k, v, do, doc=None, sep=True, bm=None):
+def gpu_fwd_bwd(w, q, k, v, do, doc=None, sep=True, bm=None, order=None):
     if bm is None:
         bm = fa.create_block_mask(w.mask, None, None, w.q_len, w.kv_len,
                                   device=DEV, BLOCK_SIZE=w.block_m,
@@ -50,7 +50,8 @@ def gpu_fwd_bwd(w, q, k, v, do, doc=None, sep=True, bm=None):
     o, lse = fa.flex_attention(qd, kd, vd, bm, score_mod=sm, scale=w.scale,
                                num_splits=1)
     dq, dk, dv = fa.flex_attention_backward(qd, kd, vd, o, lse, dod, bm,
-                                            score_mod=sm, scale=w.scale)
+                                            score_mod=sm, scale=w.scale,
+                                            dq_kv_order=order)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -91,7 +92,8 @@ for D, blk in ((128, 128), (64, 128), (128, 64), (64, 64)):
 @pytest.mark.parametrize("D,blk,mask,score", SMALL)
 def test_small_backward(D, blk, mask, score):
     # several tiles and ragged tails on both axes, q_len != kv_len, grouped
-    # heads (dK / dV sum over two query heads), both list layouts
+    # heads (dK / dV sum over two query heads), both list layouts (with the
+    # descending and the ascending dQ order)
     ql, kl = 3 * blk + 37, 2 * blk + 101
     w = WL.Workload("small", "bf16", 2, 4, 2, ql, kl, D, mask, blk, blk,
                     seed=0, window=blk + 13 if "window" in mask else None,
@@ -103,7 +105,7 @@ def test_small_backward(D, blk, mask, score):
     ref = oracle_bwd(w, q, k, v, do, doc)
     for sep in (True, False):
         print(f"[bwd small] D={D} blk={blk} {mask} {score} sep={sep}", flush=True)
-        got = gpu_fwd_bwd(w, q, k, v, do, doc, sep=sep)
+        got = gpu_fwd_bwd(w, q, k, v, do, doc, sep=sep, order=sep)
         for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
             assert_grad_close(g, r, f"{name} D={D} blk={blk} {mask} {score} sep={sep}")
 
@@ -177,7 +179,7 @@ def test_backward_zero_lengths():
     st = fa.fa_flex_attention_bwd(
         0, 1, 2, 1, 0, 200, 128, q0.data_ptr(), q0.stride()[:3], k.data_ptr(),
         k.stride()[:3], k.data_ptr(), k.stride()[:3], 128 ** -0.5, bm.to_c(),
-        None, q0.data_ptr(), lse0.data_ptr(), q0.data_ptr(), ws.data_ptr(),
+        None, 1, q0.data_ptr(), lse0.data_ptr(), q0.data_ptr(), ws.data_ptr(),
         nbytes, q0.data_ptr(), dk.data_ptr(), dv.data_ptr(), None)
     torch.cuda.synchronize()
     assert st == 0
@@ -223,6 +225,33 @@ def test_backward_deterministic():
         again = gpu_fwd_bwd(w, q, k, v, do, doc)
         for a, b in zip(first, again):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("mask", ["causal", "document", "none"])
+def test_backward_dq_order(mask):
+    # dq_kv_order: ascending and descending key-block order give dQ within
+    # the bar of the oracle and of each other, each bit-reproducible; dK and
+    # dV do not depend on it
+    blk = 64
+    w = WL.Workload("order", "bf16", 1, 2, 2, 5 * blk + 11, 5 * blk + 11, 128,
+                    mask, blk, blk, seed=0, score="softcap", softcap=5.0)
+    doc = WL.doc_ids([100, 150, 81]) if mask == "document" else None
+    q, k, v, do = _inputs(w, 77)
+    ref = oracle_bwd(w, q, k, v, do, doc)
+    res = {}
+    for order in (False, True):
+        print(f"[bwd dq order] {mask} descending={order}", flush=True)
+        a = gpu_fwd_bwd(w, q, k, v, do, doc, order=order)
+        b = gpu_fwd_bwd(w, q, k, v, do, doc, order=order)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+        for name, g, r in zip(("dQ", "dK", "dV"), a, ref):
+            assert_grad_close(g, r, f"{name} {mask} descending={order}")
+        res[order] = a
+    assert torch.equal(res[False][1], res[True][1])
+    assert torch.equal(res[False][2], res[True][2])
+    assert (res[False][0].float() - res[True][0].float()).abs().max().item() <= \
+        TOL_BWD * max(1.0, float(np.abs(ref[0]).max()))
 
 
 def test_backward_errors():
