@@ -64,6 +64,14 @@ What is computed, and where the pages fix it
   ``0..NKVB-1`` (the pages fix no order or padding; this stable partition is
   the plain reading).
 
+* Decode over a paged cache (``decode_paged``): one new query token per
+  sequence at the end of its cached keys, the key/value cache kept as pages
+  with a per-sequence page table (frontiernews "What Attention Patterns
+  Does FlexAttention Support?": PagedAttention, causal masking for
+  language-model decoding, sliding-window decoders). Pinned in
+  ``tests/test_oracle_decode.py`` against ``attention`` on the gathered
+  rows, page-order invariance and closed forms.
+
 Every function here is pinned by ``tests/test_oracle_pins.py`` against
 what the pages print or what mathematics fixes (the T=6, W=3 mask printed
 on the crackedaicode page, W=1 and W>=T special cases, block-diagonal
@@ -284,6 +292,77 @@ def attention(q, k, v, mask="none", score="none", scale=None, window=None,
                     live[:, None], (w @ vb) / safe[:, None], 0.0)
                 lse[b, h, r0:r0 + len(ri)] = np.where(
                     live, mx + np.log(safe), -np.inf)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
+# decode over a paged key/value cache
+# --------------------------------------------------------------------------
+def paged_rows(pages, table_b, length):
+    """The first ``length`` token rows of one sequence from a paged cache.
+
+    ``pages [P, page_size, H_kv, D]``: a pool of physical pages of
+    ``page_size`` consecutive token rows (the key/value cache treated as
+    pages, frontiernews "What Attention Patterns Does FlexAttention
+    Support?", PagedAttention); ``table_b``: the sequence's page table,
+    logical page p (tokens ``[p * page_size, (p + 1) * page_size)``) held in
+    physical page ``table_b[p]``. Returns ``[H_kv, length, D]``."""
+    pages = _as_f64(pages)
+    page_size = pages.shape[1]
+    n = -(-int(length) // page_size)
+    rows = np.concatenate([pages[int(table_b[p])] for p in range(n)], axis=0) \
+        if n else np.zeros((0,) + pages.shape[2:])
+    return rows[:length].transpose(1, 0, 2)
+
+
+def decode_paged(q, k_pages, v_pages, page_table, seq_lens, mask="causal",
+                 score="none", scale=None, window=None, doc_id=None,
+                 softcap=None):
+    """One decode step over a paged cache, fp64.
+
+    ``q [B, H, D]`` holds each sequence's newest token, already appended to
+    the cache: sequence b has ``L_b = seq_lens[b]`` cached tokens (rows of
+    ``k_pages`` / ``v_pages [P, page_size, H_kv, D]`` reached through
+    ``page_table [B, max_pages]``) and its query sits at position
+    ``q_idx = L_b - 1``. The attention is the plain definition above for
+    that one row over keys ``kv_idx in [0, L_b)``: ``mask_mod(q_idx,
+    kv_idx)``, ``score_mod`` with that q_idx and the query head h, the
+    softmax over the allowed keys. ``doc_id``: ``[L]`` shared or ``[B, L]``
+    per sequence, indexed by token position. Returns ``O [B, H, D]`` and
+    ``LSE [B, H]``; a sequence with no allowed key (``L_b = 0``) gives 0 and
+    -inf."""
+    q = _as_f64(q)
+    B, H, D = q.shape
+    H_kv = k_pages.shape[2]
+    group = H // H_kv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    table = np.asarray(page_table)
+    lens = np.asarray(seq_lens)
+    out = np.zeros((B, H, v_pages.shape[3]))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        L = int(lens[b])
+        if L <= 0:
+            continue
+        kb = paged_rows(k_pages, table[b], L)
+        vb = paged_rows(v_pages, table[b], L)
+        doc_b = (np.asarray(doc_id)[b]
+                 if doc_id is not None and np.ndim(doc_id) == 2 else doc_id)
+        i = L - 1
+        cols = np.arange(L)
+        allowed = mask_mod(mask, i, cols, window=window, doc_id=doc_b)
+        if not allowed.any():
+            continue
+        for h in range(H):
+            t = scale * (kb[h // group] @ q[b, h])
+            s = score_mod(score, t, h, H, i, cols, softcap=softcap)
+            z = np.where(allowed, s, -np.inf)
+            mx = z.max()
+            w = np.exp(z - mx)
+            den = w.sum()
+            out[b, h] = (w @ vb[h // group]) / den
+            lse[b, h] = mx + np.log(den)
     return out, lse
 
 
