@@ -40,7 +40,7 @@ FA_SCORE_ALIBI = 2
 # largest num_splits of fa_flex_attention_fwd_split
 FA_MAX_SPLITS = 64
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class fa_mask_mod(ctypes.Structure):
@@ -74,6 +74,7 @@ class fa_block_mask(ctypes.Structure):
 
 
 Stride3 = ctypes.c_int64 * 3
+Stride2 = ctypes.c_int64 * 2
 
 # name -> (restype, argtypes); every function include/flexattn.h declares
 SIGNATURES = {
@@ -118,6 +119,15 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (ctypes.c_int, [
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.POINTER(fa_block_mask), ctypes.POINTER(ctypes.c_uint64)]),
+    "fa_flex_attention_decode_paged": (ctypes.c_int, [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_float, ctypes.POINTER(fa_mask_mod),
+        ctypes.POINTER(fa_score_mod), ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_abi_version": (ctypes.c_int32, []),

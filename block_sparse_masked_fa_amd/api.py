@@ -7,12 +7,15 @@ kernels. Two layers:
 * the raw entry points with the C names (``fa_block_mask_dims``,
   ``fa_create_block_mask``, ``fa_flex_attention_fwd``,
   ``fa_flex_attention_fwd_split``, ``fa_split_workspace_bytes``,
-  ``fa_flex_attention_bwd``, ``fa_bwd_workspace_bytes``), taking
+  ``fa_flex_attention_bwd``, ``fa_bwd_workspace_bytes``,
+  ``fa_flex_attention_decode_paged``), taking
   ctypes structs and integer device addresses;
 * a FlexAttention-style convenience layer: ``create_block_mask(...)`` returns
   a :class:`BlockMask` holding its index tensors, and
   ``flex_attention(q, k, v, block_mask, score_mod)`` returns ``(O, LSE)``
-  and ``flex_attention_backward(...)`` returns ``(dQ, dK, dV)``.
+  and ``flex_attention_backward(...)`` returns ``(dQ, dK, dV)``;
+  ``flex_attention_decode_paged(...)`` runs one decode step per sequence
+  over a paged key/value cache.
   The shapes follow scaled_dot_product_attention: (B, H, S, D).
 """
 from __future__ import annotations
@@ -34,7 +37,8 @@ __all__ = [
     "fa_flex_attention_fwd", "fa_flex_attention_fwd_split",
     "fa_split_workspace_bytes", "auto_num_splits", "FlexAttnError",
     "flex_attention_backward", "fa_flex_attention_bwd",
-    "fa_bwd_workspace_bytes",
+    "fa_bwd_workspace_bytes", "flex_attention_decode_paged",
+    "fa_flex_attention_decode_paged", "auto_decode_splits",
 ]
 
 FlexAttnError = C.FlexAttnError
@@ -218,6 +222,38 @@ def fa_bwd_workspace_bytes(B: int, H: int, q_len: int,
                                            ctypes.byref(n)),
             "fa_bwd_workspace_bytes")
     return n.value
+
+
+def fa_flex_attention_decode_paged(B: int, H: int, H_kv: int, D: int, q: int,
+                                   q_stride, k_pages: int, k_stride,
+                                   v_pages: int, v_stride, num_pages: int,
+                                   page_size: int, page_table: int,
+                                   max_pages: int, seq_lens: int,
+                                   scale: float, mask: C.fa_mask_mod,
+                                   score: Optional[C.fa_score_mod],
+                                   num_splits: int, workspace: Optional[int],
+                                   workspace_bytes: int, o: int,
+                                   lse: Optional[int],
+                                   stream: Optional[int]) -> int:
+    return C.lib().fa_flex_attention_decode_paged(
+        B, H, H_kv, D, q, C.Stride2(*q_stride), k_pages, C.Stride3(*k_stride),
+        v_pages, C.Stride3(*v_stride), num_pages, page_size, page_table,
+        max_pages, seq_lens, scale, ctypes.byref(mask),
+        ctypes.byref(score) if score is not None else None, num_splits,
+        workspace, workspace_bytes, o, lse, stream)
+
+
+def auto_decode_splits(B: int, H_kv: int, max_tokens: int,
+                       num_cus: int) -> int:
+    """Parts per (sequence, key head) for the paged decode: about eight
+    single-wavefront workgroups per compute unit (two are resident at a
+    time; the rest even out ragged lengths), at most one part per 64-key
+    stage of the longest possible sequence, at most 64."""
+    wgs = B * H_kv
+    if wgs == 0:
+        return 1
+    stages = max(1, -(-max_tokens // 64))
+    return max(1, min(C.FA_MAX_SPLITS, stages, -(-8 * num_cus // wgs)))
 
 
 def auto_num_splits(dtype: torch.dtype, B: int, H: int, num_q_blocks: int,
@@ -493,3 +529,73 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             _stream_handle(q.device))
     C.check(st, "fa_flex_attention_bwd")
     return dq, dk, dv
+
+
+def flex_attention_decode_paged(q: torch.Tensor, k_pages: torch.Tensor,
+                                v_pages: torch.Tensor,
+                                page_table: torch.Tensor,
+                                seq_lens: torch.Tensor, mask_mod="causal",
+                                score_mod=None, scale: Optional[float] = None,
+                                num_splits: Optional[int] = None, *,
+                                window=None, doc_id=None,
+                                return_lse: bool = True):
+    """One decode step per sequence over a paged key/value cache.
+
+    ``q``: bf16 ``(B, H, D)``, each sequence's newest token (already in the
+    cache). ``k_pages`` / ``v_pages``: bf16 ``(num_pages, page_size, H_kv,
+    D)`` pools (any strides with D contiguous). ``page_table``: int32
+    ``(B, max_pages)``; ``seq_lens``: int32 ``(B,)`` cached tokens per
+    sequence. ``mask_mod``: "causal", "none", "sliding_window" /
+    "local_window" (``window``), "document" (``doc_id`` by token position)
+    or a :class:`MaskMod`. Returns ``(O (B, H, D), LSE (B, H))``.
+    ``num_splits`` None picks :func:`auto_decode_splits`."""
+    if q.dim() != 3 or k_pages.dim() != 4 or v_pages.dim() != 4:
+        raise ValueError("q must be (B, H, D) and the pools (P, page, H_kv, D)")
+    if not (q.dtype == k_pages.dtype == v_pages.dtype == torch.bfloat16):
+        raise ValueError("the paged decode takes bf16 q and pools")
+    if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("page_table and seq_lens must be int32")
+    for t in (q, k_pages, v_pages, page_table, seq_lens):
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("all tensors must be on q's HIP device")
+    B, H, D = q.shape
+    P, page_size, H_kv, Dk = k_pages.shape
+    if v_pages.shape != k_pages.shape or Dk != D:
+        raise ValueError("k_pages and v_pages must be (P, page_size, H_kv, D)")
+    if page_table.dim() != 2 or page_table.shape[0] != B or \
+            not page_table.is_contiguous():
+        raise ValueError("page_table must be a contiguous (B, max_pages) tensor")
+    if seq_lens.shape != (B,) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous (B,) tensor")
+    for t in (q, k_pages, v_pages):
+        if t.numel() and t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    max_pages = page_table.shape[1]
+    mask = _mask_from(mask_mod, window, doc_id)
+    if mask.kind == C.FA_MASK_DOCUMENT and mask.per_batch and \
+            mask.doc_id.shape[0] != B:
+        raise ValueError("per-sequence doc_id must be (B, L)")
+    score = _score_from(score_mod)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if num_splits is None:
+        num_splits = auto_decode_splits(
+            B, H_kv, max_pages * page_size,
+            torch.cuda.get_device_properties(q.device).multi_processor_count)
+    out = torch.empty((B, H, D), dtype=q.dtype, device=q.device)
+    lse = (torch.empty((B, H), dtype=torch.float32, device=q.device)
+           if return_lse else None)
+    nbytes = fa_split_workspace_bytes(B, H, 1, D, num_splits)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        st = fa_flex_attention_decode_paged(
+            B, H, H_kv, D, q.data_ptr(), q.stride()[:2], k_pages.data_ptr(),
+            k_pages.stride()[:3], v_pages.data_ptr(), v_pages.stride()[:3], P,
+            page_size, page_table.data_ptr(), max_pages, seq_lens.data_ptr(),
+            float(scale), mask.to_c(), score.to_c(), num_splits,
+            ws.data_ptr(), nbytes, out.data_ptr(),
+            lse.data_ptr() if lse is not None else None,
+            _stream_handle(q.device))
+    C.check(st, "fa_flex_attention_decode_paged")
+    return out, lse
+

@@ -32,6 +32,7 @@ SOURCES = [
     "bwd_prepare.hip",
     "bwd_bf16_d64.hip",
     "bwd_bf16_d128.hip",
+    "decode_bf16.hip",
 ]
 
 # Per-source extra flags. The backward kernels keep two fp32 tiles, two

@@ -175,4 +175,28 @@ fa_status fa_flex_attention_bwd(
   return hip_status(err, "attention backward launch");
 }
 
+fa_status fa_flex_attention_decode_paged(
+    int32_t B, int32_t H, int32_t H_kv, int32_t D, const void* q,
+    const int64_t q_stride[2], const void* k_pages, const int64_t k_stride[3],
+    const void* v_pages, const int64_t v_stride[3], int32_t num_pages,
+    int32_t page_size, const int32_t* page_table, int32_t max_pages,
+    const int32_t* seq_lens, float scale, const fa_mask_mod* mask,
+    const fa_score_mod* score, int32_t num_splits, void* workspace,
+    uint64_t workspace_bytes, void* o, float* lse, void* stream) {
+  std::string msg;
+  fa::DecodeLaunch p{};
+  fa::CombineLaunch cl{};
+  bool nothing = false;
+  int st = fa::check_decode_paged(B, H, H_kv, D, q, q_stride, k_pages, k_stride,
+                                  v_pages, v_stride, num_pages, page_size,
+                                  page_table, max_pages, seq_lens, scale, mask,
+                                  score, num_splits, workspace, workspace_bytes,
+                                  o, lse, &p, &cl, &nothing, &msg);
+  if (st != FA_OK) return finish(st, msg);
+  if (nothing) return FA_OK;
+  int err = fa::launch_decode_paged(p, stream);
+  if (err != 0 || p.nsplit == 1) return hip_status(err, "decode kernel launch");
+  return hip_status(fa::launch_split_combine(cl, stream), "split-KV merge launch");
+}
+
 }  // extern "C"

@@ -93,6 +93,31 @@ struct BwdLaunch {
   uint64_t zero_bytes;
 };
 
+// Decode step over a paged key/value cache: one query token per sequence
+// at position seq_lens[b] - 1, keys [0, seq_lens[b]) read through the
+// sequence's page table. Split into nsplit parts merged like the split-KV
+// forward (part_o / part_ml layout of FwdLaunch with q_len = 1).
+struct DecodeLaunch {
+  int32_t B, H, H_kv, D;
+  const void* q;                 // [B, H, D] bf16, strides qs (batch, head)
+  int64_t qs[2];
+  const void* k_pages;           // pool of pages, strides (page, row, head)
+  const void* v_pages;
+  int64_t ks[3], vs[3];
+  int32_t num_pages, page_size, max_pages;
+  const int32_t* page_table;     // [B, max_pages]
+  const int32_t* seq_lens;       // [B]
+  float scale;
+  MaskParams mask;
+  int32_t score_kind;
+  float softcap;
+  int32_t nsplit;
+  void* o;                       // [B, H, D] bf16 contiguous
+  float* lse;                    // [B, H] or NULL
+  float* part_o;
+  float* part_ml;
+};
+
 // Kernel launchers: return a hipError_t value (0 = success).
 int launch_block_mask(const BlockMaskLaunch& p, void* stream);
 int launch_fwd_bf16_d64(const FwdLaunch& p, void* stream);
@@ -101,6 +126,7 @@ int launch_fwd_fp32(const FwdLaunch& p, void* stream);
 int launch_split_combine(const CombineLaunch& p, void* stream);
 int launch_bwd_prepare(const BwdLaunch& p, void* stream);  // transposed lists
 int launch_zero_fill(void* dst, uint64_t bytes, void* stream);  // 16-byte aligned
+int launch_decode_paged(const DecodeLaunch& p, void* stream);
 int launch_bwd_bf16_d64(const BwdLaunch& p, void* stream);
 int launch_bwd_bf16_d128(const BwdLaunch& p, void* stream);
 

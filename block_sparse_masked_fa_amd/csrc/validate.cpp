@@ -448,4 +448,127 @@ int check_flex_attention_bwd(
   return FA_OK;
 }
 
+int check_decode_paged(int32_t B, int32_t H, int32_t H_kv, int32_t D,
+                       const void* q, const int64_t q_stride[2],
+                       const void* k_pages, const int64_t k_stride[3],
+                       const void* v_pages, const int64_t v_stride[3],
+                       int32_t num_pages, int32_t page_size,
+                       const int32_t* page_table, int32_t max_pages,
+                       const int32_t* seq_lens, float scale,
+                       const fa_mask_mod* mask, const fa_score_mod* score,
+                       int32_t num_splits, void* workspace,
+                       uint64_t workspace_bytes, void* o, float* lse,
+                       DecodeLaunch* out, CombineLaunch* cl,
+                       bool* nothing_to_do, std::string* msg) {
+  *nothing_to_do = false;
+  if (B < 0 || H < 0) return fail(msg, FA_ERR_INVALID_VALUE, "negative size");
+  if (H_kv < 1 || H % H_kv != 0)
+    return fail(msg, FA_ERR_INVALID_VALUE, "H_kv must be >= 1 and divide H");
+  if (H / H_kv > 32)
+    return fail(msg, FA_ERR_UNSUPPORTED,
+                "decode packs a key head's query heads into 32 MFMA columns: "
+                "H / H_kv must be <= 32");
+  if (D != 64 && D != 128)
+    return fail(msg, FA_ERR_UNSUPPORTED,
+                "head dimension " + std::to_string(D) + " (built: 64, 128)");
+  if (!std::isfinite(scale) || !(scale > 0.0f))
+    return fail(msg, FA_ERR_INVALID_VALUE, "scale must be finite and > 0");
+  if (page_size < 64 || page_size % 64 != 0 || page_size > (1 << 20))
+    return fail(msg, FA_ERR_UNSUPPORTED,
+                "page_size must be a multiple of 64 in [64, 2^20]");
+  if (max_pages < 0 || num_pages < 0)
+    return fail(msg, FA_ERR_INVALID_VALUE, "negative page count");
+  const int64_t cap = static_cast<int64_t>(max_pages) * page_size;
+  if (cap > (int64_t(1) << 30))
+    return fail(msg, FA_ERR_UNSUPPORTED, "max_pages * page_size above 2^30 tokens");
+  if (!mask) return fail(msg, FA_ERR_NULL_POINTER, "mask is NULL");
+  int st = check_mask_mod(mask, 0, static_cast<int32_t>(cap), msg);
+  if (st != FA_OK) return st;
+  int32_t skind = score ? score->kind : FA_SCORE_NONE;
+  float softcap = score ? score->softcap : 0.0f;
+  if (skind != FA_SCORE_NONE && skind != FA_SCORE_SOFTCAP && skind != FA_SCORE_ALIBI)
+    return fail(msg, FA_ERR_INVALID_VALUE, "unknown score kind " + std::to_string(skind));
+  if (skind == FA_SCORE_SOFTCAP && (!std::isfinite(softcap) || !(softcap > 0.0f)))
+    return fail(msg, FA_ERR_INVALID_VALUE, "softcap must be finite and > 0");
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(msg, FA_ERR_INVALID_VALUE,
+                "num_splits must be in [1, " + std::to_string(kMaxSplits) + "]");
+  const int64_t wgs = static_cast<int64_t>(B) * H_kv * num_splits;
+  if (wgs > INT32_MAX) return fail(msg, FA_ERR_UNSUPPORTED, "too many workgroups");
+  if (static_cast<int64_t>(B) * H == 0) {
+    *nothing_to_do = true;
+    return FA_OK;
+  }
+  if (!q || !o) return fail(msg, FA_ERR_NULL_POINTER, "q or o is NULL");
+  if (!seq_lens) return fail(msg, FA_ERR_NULL_POINTER, "seq_lens is NULL");
+  if (max_pages > 0 && (!page_table || !k_pages || !v_pages))
+    return fail(msg, FA_ERR_NULL_POINTER, "page_table, k_pages or v_pages is NULL");
+  if (max_pages > 0 && num_pages < 1)
+    return fail(msg, FA_ERR_INVALID_VALUE, "num_pages must be >= 1");
+  if (!q_stride || !k_stride || !v_stride)
+    return fail(msg, FA_ERR_NULL_POINTER, "a stride array is NULL");
+  for (int d = 0; d < 2; ++d)
+    if (q_stride[d] < 0 || (q_stride[d] * 2) % 16 != 0)
+      return fail(msg, FA_ERR_UNSUPPORTED, "q strides must be >= 0 and multiples of 16 bytes");
+  for (int d = 0; d < 3; ++d)
+    if (k_stride[d] < 0 || v_stride[d] < 0 || (k_stride[d] * 2) % 16 != 0 ||
+        (v_stride[d] * 2) % 16 != 0)
+      return fail(msg, FA_ERR_UNSUPPORTED,
+                  "k / v page strides must be >= 0 and multiples of 16 bytes");
+  // a 64-row stage is addressed with 32-bit byte offsets
+  if (k_stride[1] * 2 * 64 >= (int64_t(1) << 31) || v_stride[1] * 2 * 64 >= (int64_t(1) << 31))
+    return fail(msg, FA_ERR_UNSUPPORTED, "k / v row stride too large");
+  if (!aligned16(q) || !aligned16(o) || (max_pages > 0 && (!aligned16(k_pages) || !aligned16(v_pages))))
+    return fail(msg, FA_ERR_UNSUPPORTED, "q, o, k_pages and v_pages must be 16-byte aligned");
+  uint64_t need = 0;
+  if ((st = check_split_workspace_bytes(B, H, 1, D, num_splits, &need, msg)) != FA_OK) return st;
+  if (num_splits > 1) {
+    if (!workspace) return fail(msg, FA_ERR_NULL_POINTER, "workspace is NULL");
+    if (!aligned16(workspace))
+      return fail(msg, FA_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(msg, FA_ERR_INVALID_VALUE,
+                  "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                      std::to_string(need));
+  }
+  out->B = B;
+  out->H = H;
+  out->H_kv = H_kv;
+  out->D = D;
+  out->q = q;
+  out->qs[0] = q_stride[0];
+  out->qs[1] = q_stride[1];
+  out->k_pages = k_pages;
+  out->v_pages = v_pages;
+  for (int d = 0; d < 3; ++d) {
+    out->ks[d] = k_stride[d];
+    out->vs[d] = v_stride[d];
+  }
+  out->num_pages = num_pages;
+  out->page_size = page_size;
+  out->max_pages = max_pages;
+  out->page_table = page_table;
+  out->seq_lens = seq_lens;
+  out->scale = scale;
+  out->mask = MaskParams{mask->kind, mask->window, mask->doc_id,
+                         mask->kind == FA_MASK_DOCUMENT ? mask->doc_stride : 0};
+  out->score_kind = skind;
+  out->softcap = softcap;
+  out->nsplit = num_splits;
+  out->o = o;
+  out->lse = lse;
+  const int64_t rows = static_cast<int64_t>(B) * H;
+  float* ws = static_cast<float*>(workspace);
+  out->part_o = num_splits > 1 ? ws : nullptr;
+  out->part_ml = num_splits > 1 ? ws + static_cast<int64_t>(num_splits) * rows * D : nullptr;
+  cl->nsplit = num_splits;
+  cl->rows = rows;
+  cl->D = D;
+  cl->part_o = out->part_o;
+  cl->part_ml = out->part_ml;
+  cl->o = o;
+  cl->lse = lse;
+  return FA_OK;
+}
+
 }  // namespace fa

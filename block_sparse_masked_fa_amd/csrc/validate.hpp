@@ -73,4 +73,19 @@ int check_flex_attention_bwd(
     uint64_t workspace_bytes, void* dq, void* dk, void* dv, BwdLaunch* out,
     bool* nothing_to_do, std::string* msg);
 
+// Fills *out for launch_decode_paged (and *cl for the merge when
+// num_splits > 1) on success; *nothing_to_do when B * H == 0.
+int check_decode_paged(int32_t B, int32_t H, int32_t H_kv, int32_t D,
+                       const void* q, const int64_t q_stride[2],
+                       const void* k_pages, const int64_t k_stride[3],
+                       const void* v_pages, const int64_t v_stride[3],
+                       int32_t num_pages, int32_t page_size,
+                       const int32_t* page_table, int32_t max_pages,
+                       const int32_t* seq_lens, float scale,
+                       const fa_mask_mod* mask, const fa_score_mod* score,
+                       int32_t num_splits, void* workspace,
+                       uint64_t workspace_bytes, void* o, float* lse,
+                       DecodeLaunch* out, CombineLaunch* cl,
+                       bool* nothing_to_do, std::string* msg);
+
 }  // namespace fa

@@ -21,6 +21,8 @@
  *                          FlexAttention and Why Does It Matter").
  *   fa_flex_attention_bwd  its gradients dQ, dK, dV over the same block
  *                          mask (deterministic).
+ *   fa_flex_attention_decode_paged  one decode step per sequence over a
+ *                          paged key/value cache.
  *
  * Conventions shared by every entry point
  *   - Every pointer argument named "device" is HIP device memory owned by
@@ -45,7 +47,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -315,6 +317,59 @@ fa_status fa_flex_attention_bwd(
  * Host only (bm's dims are read, not its arrays); nothing is launched. */
 fa_status fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
                                  const fa_block_mask* bm, uint64_t* bytes);
+
+/* Decode step over a paged key/value cache (bf16). PagedAttention keeps the
+ * key/value cache as pages, like virtual memory (frontiernews, "What
+ * Attention Patterns Does FlexAttention Support?"); decoding runs one new
+ * token per sequence under a causal or sliding-window mask (same section
+ * and "What Are the Limitations of FlexAttention on Apple Silicon?").
+ * Sequence b holds L_b = seq_lens[b] cached tokens, its newest token (whose
+ * query is q[b]) included; token t of the sequence is row t % page_size of
+ * physical page page_table[b * max_pages + t / page_size]. The query sits
+ * at position q_idx = L_b - 1 and attends to keys kv_idx in [0, L_b) with
+ * mask_mod(q_idx, kv_idx) and score_mod exactly as in fa_flex_attention_fwd
+ * for that one row (ALiBi uses the query head h and these positions).
+ *
+ *   B, H, H_kv  sequences, query heads, key heads; H % H_kv == 0 and
+ *              H / H_kv <= 32 (a key head's query heads share its tiles).
+ *   D          64 or 128.
+ *   q          device bf16 [B, H, D], element strides q_stride = {batch,
+ *              head}; D contiguous; rows 16-byte aligned.
+ *   k_pages, v_pages  device bf16 page pools: element (page, row, head, d)
+ *              at page * stride[0] + row * stride[1] + head * stride[2] + d
+ *              (e.g. [num_pages, page_size, H_kv, D] contiguous); strides
+ *              multiples of 16 bytes.
+ *   num_pages  pages in each pool (>= 1 when max_pages > 0).
+ *   page_size  token rows per page: a multiple of 64 (no 64-key stage
+ *              crosses a page).
+ *   page_table device int32 [B, max_pages]. Entries for pages past L_b are
+ *              never read; an entry outside [0, num_pages) is not read
+ *              through either: its tokens are left out of the softmax.
+ *   seq_lens   device int32 [B]; values are clamped to [0, max_pages *
+ *              page_size]. L_b = 0 gives o = 0 and lse = -inf.
+ *   scale      as for the forward.
+ *   mask       host pointer: NONE, CAUSAL (both: every cached key),
+ *              SLIDING_WINDOW or LOCAL_WINDOW (the last W keys) or
+ *              DOCUMENT (keys of the query's document; doc_id indexed by
+ *              token position, doc_len >= max_pages * page_size, doc_stride
+ *              per sequence or 0).
+ *   score      host pointer or NULL, as for the forward.
+ *   num_splits 1 ... 64: each sequence's key range is cut into that many
+ *              consecutive parts run as separate workgroups and merged
+ *              exactly as in fa_flex_attention_fwd_split (workspace: at
+ *              least fa_split_workspace_bytes(B, H, 1, D, num_splits)
+ *              bytes, 16-byte aligned; NULL allowed for 1).
+ *   o          device bf16 [B, H, D] contiguous; lse device fp32 [B, H] or
+ *              NULL.
+ * One or two kernel launches; asynchronous. */
+fa_status fa_flex_attention_decode_paged(
+    int32_t B, int32_t H, int32_t H_kv, int32_t D, const void* q,
+    const int64_t q_stride[2], const void* k_pages, const int64_t k_stride[3],
+    const void* v_pages, const int64_t v_stride[3], int32_t num_pages,
+    int32_t page_size, const int32_t* page_table, int32_t max_pages,
+    const int32_t* seq_lens, float scale, const fa_mask_mod* mask,
+    const fa_score_mod* score, int32_t num_splits, void* workspace,
+    uint64_t workspace_bytes, void* o, float* lse, void* stream);
 
 /* Static description of a status code. */
 const char* fa_status_string(int32_t status);

@@ -307,11 +307,10 @@ def paged_rows(pages, table_b, length):
     Support?", PagedAttention); ``table_b``: the sequence's page table,
     logical page p (tokens ``[p * page_size, (p + 1) * page_size)``) held in
     physical page ``table_b[p]``. Returns ``[H_kv, length, D]``."""
-    pages = _as_f64(pages)
     page_size = pages.shape[1]
     n = -(-int(length) // page_size)
-    rows = np.concatenate([pages[int(table_b[p])] for p in range(n)], axis=0) \
-        if n else np.zeros((0,) + pages.shape[2:])
+    rows = np.concatenate([_as_f64(pages[int(table_b[p])]) for p in range(n)],
+                          axis=0) if n else np.zeros((0,) + tuple(pages.shape[2:]))
     return rows[:length].transpose(1, 0, 2)
 
 

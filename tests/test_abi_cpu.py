@@ -445,3 +445,78 @@ def test_bwd_empty_problem_is_a_noop():
     bm.num_q_blocks = 0
     assert _bwd(q_len=0, bm=bm, q=None, o=None, lse=None, dout=None,
                 dq=None, dk=None) == C.FA_ERR_NULL_POINTER
+
+
+def _decode(**over):
+    a = dict(B=2, H=8, H_kv=2, D=128, q=FAKE, q_stride=(8 * 128, 128),
+             k_pages=FAKE, k_stride=(128 * 2 * 128, 2 * 128, 128),
+             v_pages=FAKE, v_stride=(128 * 2 * 128, 2 * 128, 128),
+             num_pages=10, page_size=128, page_table=FAKE, max_pages=5,
+             seq_lens=FAKE, scale=0.088,
+             mask=C.fa_mask_mod(kind=C.FA_MASK_CAUSAL),
+             score=C.fa_score_mod(kind=C.FA_SCORE_NONE), num_splits=1,
+             workspace=None, workspace_bytes=0, o=FAKE, lse=FAKE, stream=None)
+    a.update(over)
+    return api.fa_flex_attention_decode_paged(**a)
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status", [
+    (dict(D=96), C.FA_ERR_UNSUPPORTED),
+    (dict(H_kv=3), C.FA_ERR_INVALID_VALUE),
+    (dict(H=66, H_kv=2), C.FA_ERR_UNSUPPORTED),          # 33 heads per key head
+    (dict(page_size=96), C.FA_ERR_UNSUPPORTED),
+    (dict(page_size=32), C.FA_ERR_UNSUPPORTED),
+    (dict(num_pages=0), C.FA_ERR_INVALID_VALUE),
+    (dict(max_pages=-1), C.FA_ERR_INVALID_VALUE),
+    (dict(scale=0.0), C.FA_ERR_INVALID_VALUE),
+    (dict(mask=C.fa_mask_mod(kind=C.FA_MASK_SLIDING_WINDOW, window=0)),
+     C.FA_ERR_INVALID_VALUE),
+    (dict(mask=C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT, doc_id=FAKE,
+                             doc_len=639)), C.FA_ERR_SHAPE_MISMATCH),
+    (dict(mask=None), C.FA_ERR_NULL_POINTER),
+    (dict(score=C.fa_score_mod(kind=C.FA_SCORE_SOFTCAP, softcap=0.0)),
+     C.FA_ERR_INVALID_VALUE),
+    (dict(num_splits=0), C.FA_ERR_INVALID_VALUE),
+    (dict(num_splits=65), C.FA_ERR_INVALID_VALUE),
+    (dict(num_splits=4), C.FA_ERR_NULL_POINTER),         # no workspace
+    (dict(num_splits=4, workspace=FAKE, workspace_bytes=4 * 16 * 130 * 4 - 1),
+     C.FA_ERR_INVALID_VALUE),
+    (dict(q=None), C.FA_ERR_NULL_POINTER),
+    (dict(o=None), C.FA_ERR_NULL_POINTER),
+    (dict(seq_lens=None), C.FA_ERR_NULL_POINTER),
+    (dict(page_table=None), C.FA_ERR_NULL_POINTER),
+    (dict(k_pages=None), C.FA_ERR_NULL_POINTER),
+    (dict(q=FAKE + 8), C.FA_ERR_UNSUPPORTED),
+    (dict(k_stride=(128 * 2 * 128, 2 * 128, 100)), C.FA_ERR_UNSUPPORTED),
+    (dict(v_stride=(-1, 2 * 128, 128)), C.FA_ERR_UNSUPPORTED),
+])
+def test_decode_refuses(over, status):
+    if "mask" in over and over["mask"] is None:
+        a = dict(over)
+        a.pop("mask")
+        st = C.lib().fa_flex_attention_decode_paged(
+            1, 1, 1, 128, FAKE, C.Stride2(128, 128), FAKE,
+            C.Stride3(128 * 128, 128, 128), FAKE, C.Stride3(128 * 128, 128, 128),
+            1, 128, FAKE, 1, FAKE, 0.1, None, None, 1, None, 0, FAKE, FAKE,
+            None)
+        assert st == status
+        return
+    st = _decode(**over)
+    assert st == status, C.lib().fa_last_error()
+
+
+@needs_lib
+def test_decode_empty_problem_is_a_noop():
+    assert _decode(B=0, q=None, o=None, seq_lens=None, page_table=None,
+                   k_pages=None, v_pages=None) == C.FA_OK
+
+
+def test_auto_decode_splits():
+    # about eight single-wavefront workgroups per compute unit, never more
+    # parts than 64-key stages, at most 64
+    assert api.auto_decode_splits(16, 8, 32768, 256) == 16
+    assert api.auto_decode_splits(1, 1, 32768, 256) == 64
+    assert api.auto_decode_splits(1, 1, 128, 256) == 2
+    assert api.auto_decode_splits(256, 8, 32768, 256) == 1
+    assert api.auto_decode_splits(0, 8, 32768, 256) == 1

@@ -18,6 +18,14 @@ The five workloads follow the shapes the pages use:
   section at cap 50.
 * ``c5``: causal attention with an ALiBi distance bias over 16384 tokens.
 
+A sixth workload, ``decode_paged``, is one decode step per sequence over a
+paged key/value cache (PagedAttention and language-model decoding in the
+frontiernews article's list of supported patterns): 16 sequences with
+seeded context lengths between 1024 and 32768 tokens, 32 query heads over 8
+key heads, head dim 128, pages of 128 token rows scattered over the pool in
+a seeded order, causal. See :class:`DecodeWorkload` and
+:func:`make_paged_inputs`.
+
 Values are N(0, 1) from ``numpy.random.default_rng(seed)``, drawn as float32
 in (B, H, S, D) order: the document lengths first (``c4`` only), then Q, K
 and V. bf16 workloads are rounded to bf16 with round-to-nearest-even, and
@@ -31,7 +39,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "CONFIGS", "get", "doc_lengths", "doc_ids",
-           "draw_qkv", "make_inputs"]
+           "draw_qkv", "make_inputs", "DecodeWorkload", "DECODE",
+           "make_paged_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -125,3 +134,79 @@ def make_inputs(w: Workload):
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     qt, kt, vt = (torch.from_numpy(x).to(tdt) for x in (q, k, v))
     return qt, kt, vt, doc
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int                  # sequences
+    H: int                  # query heads
+    H_kv: int               # key / value heads
+    D: int
+    page_size: int
+    min_len: int            # context lengths drawn uniformly in
+    max_len: int            # [min_len, max_len]
+    seed: int
+    mask: str = "causal"
+    window: Optional[int] = None
+    score: str = "none"
+    softcap: Optional[float] = None
+    spare_pages: int = 7    # unused pages in the pool (poisoned)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / float(np.sqrt(self.D))
+
+
+DECODE = DecodeWorkload("decode_paged", B=16, H=32, H_kv=8, D=128,
+                        page_size=128, min_len=1024, max_len=32768, seed=5)
+
+
+def make_paged_inputs(w: DecodeWorkload, lens=None, poison=True):
+    """Seeded paged cache for ``w``.
+
+    Draws, in order: the context lengths (unless ``lens`` is given), each
+    sequence's K and V token rows ``[L_b, H_kv, D]`` and its query
+    ``[H, D]`` (float32 N(0, 1), then bf16 RNE), and a random permutation of
+    the physical pages. Pages are filled in the order of the sequences and
+    their logical pages; rows of a sequence's last page past its length,
+    the spare pages and the unused page-table slots hold poison (NaN rows,
+    index -1), which a correct reader never touches.
+
+    Returns CPU tensors ``q [B, H, D]``, ``k_pages``, ``v_pages
+    [P, page_size, H_kv, D]`` (bf16), ``page_table [B, max_pages]`` and
+    ``seq_lens [B]`` (int32)."""
+    import torch
+
+    rng = np.random.default_rng(w.seed)
+    if lens is None:
+        lens = rng.integers(w.min_len, w.max_len + 1, size=w.B)
+    lens = np.asarray(lens, dtype=np.int64)
+    ps = w.page_size
+    n_pages = [-(-int(L) // ps) for L in lens]
+    P = sum(n_pages) + w.spare_pages
+    max_pages = max(max(n_pages), 1)
+    fill = np.nan if poison else 0.0
+    kp = np.full((P, ps, w.H_kv, w.D), fill, dtype=np.float32)
+    vp = np.full((P, ps, w.H_kv, w.D), fill, dtype=np.float32)
+    q = np.empty((w.B, w.H, w.D), dtype=np.float32)
+    perm = rng.permutation(P)
+    table = np.full((w.B, max_pages), -1, dtype=np.int32)
+    at = 0
+    for b, L in enumerate(lens):
+        L = int(L)
+        k = rng.standard_normal((L, w.H_kv, w.D), dtype=np.float32)
+        v = rng.standard_normal((L, w.H_kv, w.D), dtype=np.float32)
+        q[b] = rng.standard_normal((w.H, w.D), dtype=np.float32)
+        for lp in range(n_pages[b]):
+            phys = int(perm[at])
+            at += 1
+            table[b, lp] = phys
+            rows = slice(lp * ps, min(L, (lp + 1) * ps))
+            n = rows.stop - rows.start
+            kp[phys, :n] = k[rows]
+            vp[phys, :n] = v[rows]
+    to = lambda x: torch.from_numpy(x).to(torch.bfloat16)  # noqa: E731
+    return (to(q), to(kp), to(vp), torch.from_numpy(table),
+            torch.from_numpy(lens.astype(np.int32)))
+
