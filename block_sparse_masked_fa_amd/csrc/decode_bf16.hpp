@@ -15,10 +15,13 @@
 // interval [lo, L_b) (every built-in mask allows only keys at or before the
 // query, and the window masks only the last W of them); its 64-key stages
 // are cut into `nsplit` consecutive parts, and the parts are merged by the
-// split-KV combine kernel. Per stage, as in the forward (fwd_bf16.hpp):
-// the K and V tiles arrive in LDS by buffer DMA (double-buffered), the
-// stage's physical address comes from the page table (page_size is a
-// multiple of 64, so no stage crosses a page), S^T = K Q^T and
+// split-KV combine kernel. Per stage: the stage's physical address comes
+// from the page table (page_size is a multiple of 64, so no stage crosses a
+// page); the V tile arrives in LDS by buffer DMA (double-buffered, read
+// transposed as in the forward, fwd_bf16.hpp) and K goes straight into
+// registers in the MFMA operand layout, which halves the LDS per workgroup
+// so that four workgroups (and their loads in flight) fit a compute unit;
+// S^T = K Q^T and
 // O^T += V^T P^T on MFMA, and an online softmax per query column. mask_mod
 // runs on the interval's first and last stage (and on every stage of a
 // document mask). A page-table entry outside [0, num_pages) skips its
@@ -41,9 +44,7 @@ __global__ __launch_bounds__(64) void decode_paged_kernel(const DecodeLaunch p) 
   constexpr int DK = D / 16;
   constexpr int DT = D / 32;
 
-  __shared__ __attribute__((aligned(1024))) char sK0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sV0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char sV1[STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int sDoc0[kStageKeys];
   __shared__ __attribute__((aligned(16))) int sDoc1[kStageKeys];
@@ -112,12 +113,6 @@ __global__ __launch_bounds__(64) void decode_paged_kernel(const DecodeLaunch p) 
   const int64_t vrow = p.vs[1] * 2;
   const int32_t* table = p.page_table + static_cast<int64_t>(b) * p.max_pages;
 
-  int k_rd[DK];  // K operand: row lq (+32 jt), chunk 2dk + g
-  {
-    const int s = kv_swizzle<D>(lq);
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk) k_rd[dk] = lq * RB + (((2 * dk + g) ^ s) << 4);
-  }
   int v_rd[2][DT];  // V^T operand: row 8*t2 + 4g + (lane%16)/4 (+16 kk)
 #pragma unroll
   for (int t2 = 0; t2 < 2; ++t2) {
@@ -138,32 +133,48 @@ __global__ __launch_bounds__(64) void decode_paged_kernel(const DecodeLaunch p) 
     return static_cast<unsigned>(phys) < static_cast<unsigned>(p.num_pages) ? phys : -1;
   };
   auto masked_at = [&](int j0) -> bool { return doc_mask || j0 < lo || j0 + kStageKeys > L; };
-  auto issue = [&](int k, int phys, char* sK, char* sV, int* sD) {
+  auto stage_base = [&](const char* pool, const int64_t* st, int phys, int j0) -> const char* {
+    return pool + (static_cast<int64_t>(phys) * st[0] + hk * st[2] +
+                   static_cast<int64_t>(j0 % p.page_size) * st[1]) * 2;
+  };
+  // V tile of stage k into LDS by DMA (rows past the sequence end as zeros)
+  auto issue_v = [&](int k, int phys, char* sV, int* sD) {
     if (phys < 0) return;
     const int j0 = stage_j0(k);
-    const int r0 = j0 % p.page_size;
-    // rows of the stage inside the sequence; the rest read as zeros
     const int rows_left = L - j0;
-    const int krec = rows_left >= kStageKeys ? 0x7fffffff
-                     : (rows_left - 1) * static_cast<int>(krow) + RB;
     const int vrec = rows_left >= kStageKeys ? 0x7fffffff
                      : (rows_left - 1) * static_cast<int>(vrow) + RB;
-    const char* kb = kpool + (static_cast<int64_t>(phys) * p.ks[0] + hk * p.ks[2] +
-                              static_cast<int64_t>(r0) * p.ks[1]) * 2;
-    const char* vb = vpool + (static_cast<int64_t>(phys) * p.vs[0] + hk * p.vs[2] +
-                              static_cast<int64_t>(r0) * p.vs[1]) * 2;
-    const hw::i32x4 kr = hw::make_rsrc(kb, krec);
-    const hw::i32x4 vr = hw::make_rsrc(vb, vrec);
+    const hw::i32x4 vr = hw::make_rsrc(stage_base(vpool, p.vs, phys, j0), vrec);
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
       const int r = rd * RPK + lane / CPR;
       const uint32_t col = static_cast<uint32_t>(((lane % CPR) ^ kv_swizzle<D>(r)) * 16);
-      hw::dma_tile16(kr, hw::lds_addr(sK + rd * 1024), static_cast<uint32_t>(r * krow) + col, 0);
       hw::dma_tile16(vr, hw::lds_addr(sV + rd * 1024), static_cast<uint32_t>(r * vrow) + col, 0);
     }
     if (doc_mask) {
       const int j = min(j0 + lane, L - 1);
       hw::dma_dword(doc, hw::lds_addr(sD), static_cast<uint32_t>(j * 4));
+    }
+  };
+  // K of stage k straight into registers, already in the MFMA A-operand
+  // layout (row lq + 32 jt, chunk 2 dk + g), by buffer loads whose range
+  // ends at the sequence end (rows past it read as zeros)
+  u32x4 kreg[DK][2];
+  auto load_k = [&](int k, int phys) {
+    if (phys < 0) return;
+    const int j0 = stage_j0(k);
+    const int rows_left = L - j0;
+    const int krec = rows_left >= kStageKeys ? 0x7fffffff
+                     : (rows_left - 1) * static_cast<int>(krow) + RB;
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(stage_base(kpool, p.ks, phys, j0)), 0, krec, hw::kRawBufferFlags);
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      const int vo = (lq + 32 * jt) * static_cast<int>(krow) + g * 16;
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk)
+        kreg[dk][jt] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, vo + dk * 32, 0, 0));
     }
   };
 
@@ -175,24 +186,22 @@ __global__ __launch_bounds__(64) void decode_paged_kernel(const DecodeLaunch p) 
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  auto compute = [&](int k, int phys, const char* sK, const char* sV, const int* sD) {
-    if (phys < 0) return;
-    const int j0 = stage_j0(k);
-    const bool masked = masked_at(j0);
-
-    // S^T = K Q^T for the stage's 64 keys
-    f32x16 s[2];
+  // S^T = K Q^T for the stage's 64 keys (K from registers)
+  auto scores = [&](f32x16* s) {
     s[0] = f32x16{};
     s[1] = f32x16{};
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + k_rd[dk] + jt * 32 * RB);
-        s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[dk],
-                                                        s[jt], 0, 0, 0);
-      }
+      for (int jt = 0; jt < 2; ++jt)
+        s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kreg[dk][jt]),
+                                                        qf[dk], s[jt], 0, 0, 0);
     }
+  };
+  auto compute = [&](int k, int phys, f32x16* s, const char* sV, const int* sD) {
+    if (phys < 0) return;
+    const int j0 = stage_j0(k);
+    const bool masked = masked_at(j0);
 
     // score_mod into the log2 domain; key of (jt, r): j0 + 4g + 32jt +
     // 8(r/4) + r%4
@@ -286,23 +295,33 @@ __global__ __launch_bounds__(64) void decode_paged_kernel(const DecodeLaunch p) 
     }
   };
 
-  // main loop: the DMA of stage k + 1 overlaps the compute of stage k
+  // main loop: stage k + 1's V tile (DMA) and K registers (loaded once
+  // stage k's scores have consumed the previous ones) arrive while stage k
+  // finishes
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): setup loads landed
   int ph_cur = nst > 0 ? stage_page(0) : -1;
-  if (nst > 0) issue(0, ph_cur, sK0, sV0, sDoc0);
+  if (nst > 0) {
+    issue_v(0, ph_cur, sV0, sDoc0);
+    load_k(0, ph_cur);
+  }
   for (int k = 0; k < nst; k += 2) {
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
     int ph_nxt = k + 1 < nst ? stage_page(k + 1) : -1;
-    if (k + 1 < nst) issue(k + 1, ph_nxt, sK1, sV1, sDoc1);
-    compute(k, ph_cur, sK0, sV0, sDoc0);
+    if (k + 1 < nst) issue_v(k + 1, ph_nxt, sV1, sDoc1);
+    f32x16 s[2];
+    if (ph_cur >= 0) scores(s);
+    if (k + 1 < nst) load_k(k + 1, ph_nxt);
+    compute(k, ph_cur, s, sV0, sDoc0);
     if (k + 1 >= nst) break;
     ph_cur = ph_nxt;
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
     ph_nxt = k + 2 < nst ? stage_page(k + 2) : -1;
-    if (k + 2 < nst) issue(k + 2, ph_nxt, sK0, sV0, sDoc0);
-    compute(k + 1, ph_cur, sK1, sV1, sDoc1);
+    if (k + 2 < nst) issue_v(k + 2, ph_nxt, sV0, sDoc0);
+    if (ph_cur >= 0) scores(s);
+    if (k + 2 < nst) load_k(k + 2, ph_nxt);
+    compute(k + 1, ph_cur, s, sV1, sDoc1);
     ph_cur = ph_nxt;
   }
 
