@@ -10,7 +10,8 @@ timed region starts. The JSON line reports live-block TFLOP/s:
 (partial blocks count their full area), its fraction of the bf16 MFMA peak,
 the speedup of the same kernel over a dense causal block mask at the same
 shape, the oracle timed on the host cores as a baseline, and (outside the
-step) the backward's time and algorithmic rate.
+step) the backward's time and algorithmic rate and the paged decode
+workload's time and HBM rate.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
 """
@@ -33,6 +34,7 @@ import workloads as WL  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
 PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 (published)
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E (published)
 FWD_KERNEL = "fwd_bf16_kernel"
 KERNEL_SOURCES = ["fwd_common.hpp", "fwd_asm.hpp", "fwd_bf16.hpp", "fwd_bf16_d64.hip",
                   "fwd_bf16_d128.hip", "fwd_fp32.hpp", "fwd_fp32.hip"]
@@ -167,6 +169,8 @@ def main(argv=None) -> int:
                     help="skip the dense-causal and no-skip timings")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the timing of the backward (dQ, dK, dV)")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the timing of the paged decode workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB copy kernel (for counter "
                          "calibration under rocprofv3 --pmc)")
@@ -281,6 +285,48 @@ def main(argv=None) -> int:
             f"algorithmic)")
         del o1, l1, dout
 
+    # paged decode workload (not part of the step): one
+    # fa_flex_attention_decode_paged call per repetition over a seeded
+    # paged cache; HBM-bound, rated on the key/value bytes it must read
+    dec = None
+    if not a.no_decode:
+        dw = WL.DECODE
+        log(f"[bench] generating the paged decode inputs ({dw.name})")
+        dq_, dkp, dvp, dtab, dlens = (t.to(dev) for t in WL.make_paged_inputs(dw))
+        dsplits = fa.auto_decode_splits(
+            dw.B, dw.H_kv, dtab.shape[1] * dw.page_size,
+            torch.cuda.get_device_properties(dev).multi_processor_count)
+
+        def dec_call():
+            return fa.flex_attention_decode_paged(dq_, dkp, dvp, dtab, dlens,
+                                                  scale=dw.scale,
+                                                  num_splits=dsplits)
+        for _ in range(3):
+            dec_call()
+        reps = 50
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        d0.record(stream)
+        for _ in range(reps):
+            dec_call()
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = d0.elapsed_time(d1) / reps
+        tokens = int(dlens.sum().item())
+        kv_bytes = tokens * dw.H_kv * dw.D * 2 * 2
+        io_bytes = kv_bytes + 2 * dw.B * dw.H * dw.D * 2 + dw.B * dw.H * 4
+        dec = {"workload": f"{dw.name}: bf16 B={dw.B} H={dw.H} H_kv={dw.H_kv} "
+                           f"D={dw.D} page={dw.page_size} lens {dw.min_len}-"
+                           f"{dw.max_len} (total {tokens} tokens), causal",
+               "us": round(dec_ms * 1e3, 2), "reps": reps,
+               "num_splits": dsplits, "algorithmic_bytes": io_bytes,
+               "achieved_GBps": round(io_bytes / (dec_ms * 1e-3) / 1e9, 1),
+               "peak_GBps": PEAK_HBM_GBPS,
+               "frac": round(io_bytes / (dec_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        log(f"[bench] decode {dec_ms * 1e3:.1f} us, {dec['achieved_GBps']} GB/s")
+        del dq_, dkp, dvp, dtab, dlens
+
     extra = {}
     if not a.no_reference_masks:
         def time_fwd(bm_x, reps=20):
@@ -374,6 +420,7 @@ def main(argv=None) -> int:
                      "per_launch_flops": live_flops},
         "cpu_baseline": cpu,
         "backward": bwd,
+        "decode": dec,
     }
     print(json.dumps(line), flush=True)
     return 0
