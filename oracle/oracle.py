@@ -64,6 +64,11 @@ What is computed, and where the pages fix it
   ``0..NKVB-1`` (the pages fix no order or padding; this stable partition is
   the plain reading).
 
+* Masked softmax over materialised scores (``masked_softmax``): the
+  materialising fallback's compare / select / softmax chain as one
+  operation (MLX pull request "Fuse the causal mask into the SDPA fallback
+  softmax"). Pinned in ``tests/test_oracle_masked_softmax.py``.
+
 * Decode over a paged cache (``decode_paged``): one new query token per
   sequence at the end of its cached keys, the key/value cache kept as pages
   with a per-sequence page table (frontiernews "What Attention Patterns
@@ -293,6 +298,35 @@ def attention(q, k, v, mask="none", score="none", scale=None, window=None,
                 lse[b, h, r0:r0 + len(ri)] = np.where(
                     live, mx + np.log(safe), -np.inf)
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# masked softmax over materialised scores
+# --------------------------------------------------------------------------
+def masked_softmax(scores, mask="causal", q_offset=0, window=None,
+                   doc_id=None):
+    """Softmax over the last axis of materialised scores with a built-in
+    mask_mod folded in, fp64 (the fallback chain "compare, select the
+    minimum, softmax" of the MLX pull request "Fuse the causal mask into the
+    SDPA fallback softmax", as one operation).
+
+    ``scores [..., Q, K]``: row i is query position ``q_idx = i + q_offset``
+    (a prefill chunk that starts after ``q_offset`` earlier tokens), column j
+    is ``kv_idx = j``. Allowed entries get ``exp(s - max) / sum exp(s - max)``
+    over the row's allowed entries; masked entries are exactly 0 (the pull
+    request's point: the masked minimum's exponential underflows to exact
+    zero). A row with no allowed entry is all zeros."""
+    s = _as_f64(scores)
+    Q, K = s.shape[-2], s.shape[-1]
+    rows = np.arange(Q)[:, None] + int(q_offset)
+    cols = np.arange(K)[None, :]
+    allowed = mask_mod(mask, rows, cols, window=window, doc_id=doc_id)
+    z = np.where(allowed, s, -np.inf)
+    live = allowed.any(axis=1)
+    mx = np.where(live, z.max(axis=-1, initial=-np.inf), 0.0)
+    w = np.exp(z - mx[..., None])
+    den = w.sum(axis=-1, keepdims=True)
+    return np.where(live[:, None], w / np.where(den > 0, den, 1.0), 0.0)
 
 
 # --------------------------------------------------------------------------
