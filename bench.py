@@ -10,8 +10,8 @@ timed region starts. The JSON line reports live-block TFLOP/s:
 (partial blocks count their full area), its fraction of the bf16 MFMA peak,
 the speedup of the same kernel over a dense causal block mask at the same
 shape, the oracle timed on the host cores as a baseline, and (outside the
-step) the backward's time and algorithmic rate and the paged decode
-workload's time and HBM rate.
+step) the backward's time and algorithmic rate, and the HBM rates of the
+paged decode workload and of the masked-softmax fallback workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c3]
 """
@@ -171,6 +171,8 @@ def main(argv=None) -> int:
                     help="skip the timing of the backward (dQ, dK, dV)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the timing of the paged decode workload")
+    ap.add_argument("--no-softmax", action="store_true",
+                    help="skip the timing of the masked softmax workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB copy kernel (for counter "
                          "calibration under rocprofv3 --pmc)")
@@ -327,6 +329,42 @@ def main(argv=None) -> int:
         log(f"[bench] decode {dec_ms * 1e3:.1f} us, {dec['achieved_GBps']} GB/s")
         del dq_, dkp, dvp, dtab, dlens
 
+    # masked softmax over materialised scores (the fallback workload; not
+    # part of the step), HBM-bound: allowed scores read once, every
+    # probability written once
+    smx = None
+    if not a.no_softmax:
+        sw = WL.SOFTMAX
+        log(f"[bench] generating the masked-softmax scores ({sw.name})")
+        sc = WL.make_scores(sw).to(dev)
+        sp = torch.empty_like(sc)
+
+        def sm_call():
+            fa.masked_softmax(sc, sw.mask, q_offset=sw.q_offset, out=sp)
+        for _ in range(3):
+            sm_call()
+        reps = 20
+        t0e = torch.cuda.Event(enable_timing=True)
+        t1e = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0e.record(stream)
+        for _ in range(reps):
+            sm_call()
+        t1e.record(stream)
+        torch.cuda.synchronize()
+        sm_ms = t0e.elapsed_time(t1e) / reps
+        allowed = sum(min(sw.kv_len, sw.q_offset + r + 1) for r in range(sw.q_len))
+        sm_bytes = sw.BH * (allowed * 2 + sw.q_len * sw.kv_len * 2)
+        smx = {"workload": f"{sw.name}: bf16 scores {sw.BH}x{sw.q_len}x{sw.kv_len}, "
+                           f"causal, query offset {sw.q_offset}",
+               "us": round(sm_ms * 1e3, 2), "reps": reps,
+               "algorithmic_bytes": sm_bytes,
+               "achieved_GBps": round(sm_bytes / (sm_ms * 1e-3) / 1e9, 1),
+               "peak_GBps": PEAK_HBM_GBPS,
+               "frac": round(sm_bytes / (sm_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)}
+        log(f"[bench] masked softmax {sm_ms * 1e3:.1f} us, {smx['achieved_GBps']} GB/s")
+        del sc, sp
+
     extra = {}
     if not a.no_reference_masks:
         def time_fwd(bm_x, reps=20):
@@ -421,6 +459,7 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "backward": bwd,
         "decode": dec,
+        "masked_softmax": smx,
     }
     print(json.dumps(line), flush=True)
     return 0

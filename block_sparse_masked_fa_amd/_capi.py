@@ -40,7 +40,7 @@ FA_SCORE_ALIBI = 2
 # largest num_splits of fa_flex_attention_fwd_split
 FA_MAX_SPLITS = 64
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class fa_mask_mod(ctypes.Structure):
@@ -128,6 +128,10 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.c_float, ctypes.POINTER(fa_mask_mod),
         ctypes.POINTER(fa_score_mod), ctypes.c_int32, ctypes.c_void_p,
         ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "fa_masked_softmax": (ctypes.c_int, [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+        ctypes.POINTER(fa_mask_mod), ctypes.c_void_p, ctypes.c_void_p]),
     "fa_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "fa_last_error": (ctypes.c_char_p, []),
     "fa_abi_version": (ctypes.c_int32, []),

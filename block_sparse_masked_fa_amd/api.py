@@ -8,7 +8,7 @@ kernels. Two layers:
   ``fa_create_block_mask``, ``fa_flex_attention_fwd``,
   ``fa_flex_attention_fwd_split``, ``fa_split_workspace_bytes``,
   ``fa_flex_attention_bwd``, ``fa_bwd_workspace_bytes``,
-  ``fa_flex_attention_decode_paged``), taking
+  ``fa_flex_attention_decode_paged``, ``fa_masked_softmax``), taking
   ctypes structs and integer device addresses;
 * a FlexAttention-style convenience layer: ``create_block_mask(...)`` returns
   a :class:`BlockMask` holding its index tensors, and
@@ -39,6 +39,7 @@ __all__ = [
     "flex_attention_backward", "fa_flex_attention_bwd",
     "fa_bwd_workspace_bytes", "flex_attention_decode_paged",
     "fa_flex_attention_decode_paged", "auto_decode_splits",
+    "masked_softmax", "fa_masked_softmax",
 ]
 
 FlexAttnError = C.FlexAttnError
@@ -241,6 +242,14 @@ def fa_flex_attention_decode_paged(B: int, H: int, H_kv: int, D: int, q: int,
         max_pages, seq_lens, scale, ctypes.byref(mask),
         ctypes.byref(score) if score is not None else None, num_splits,
         workspace, workspace_bytes, o, lse, stream)
+
+
+def fa_masked_softmax(BH: int, q_len: int, kv_len: int, q_offset: int,
+                      scores: int, score_stride, mask: C.fa_mask_mod,
+                      probs: int, stream: Optional[int]) -> int:
+    return C.lib().fa_masked_softmax(BH, q_len, kv_len, q_offset, scores,
+                                     C.Stride2(*score_stride),
+                                     ctypes.byref(mask), probs, stream)
 
 
 def auto_decode_splits(B: int, H_kv: int, max_tokens: int,
@@ -598,4 +607,34 @@ def flex_attention_decode_paged(q: torch.Tensor, k_pages: torch.Tensor,
             _stream_handle(q.device))
     C.check(st, "fa_flex_attention_decode_paged")
     return out, lse
+
+
+def masked_softmax(scores: torch.Tensor, mask_mod="causal", q_offset: int = 0,
+                   *, window=None, doc_id=None,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Softmax over the last axis of bf16 scores ``(..., Q, K)`` with a
+    built-in mask_mod folded in (row i is query position ``i + q_offset``):
+    masked entries are exactly 0, a row with no allowed key is all zeros.
+    One fa_masked_softmax call; returns bf16 probabilities of the same
+    shape (contiguous)."""
+    if scores.dtype != torch.bfloat16 or not scores.is_cuda:
+        raise ValueError("scores must be a bf16 HIP device tensor")
+    if scores.dim() < 2:
+        raise ValueError("scores must be (..., Q, K)")
+    Q, K = scores.shape[-2], scores.shape[-1]
+    x = scores.reshape(-1, Q, K) if scores.dim() != 3 else scores
+    if x.numel() and x.stride(-1) != 1:
+        x = x.contiguous()
+    BH = x.shape[0]
+    mask = _mask_from(mask_mod, window, doc_id)
+    if mask.kind == C.FA_MASK_DOCUMENT and mask.per_batch:
+        raise ValueError("the masked softmax takes one shared doc_id array")
+    if out is None:
+        out = torch.empty(scores.shape, dtype=torch.bfloat16, device=scores.device)
+    with torch.cuda.device(scores.device):
+        st = fa_masked_softmax(BH, Q, K, int(q_offset), x.data_ptr(),
+                               (x.stride(0), x.stride(1)), mask.to_c(),
+                               out.data_ptr(), _stream_handle(scores.device))
+    C.check(st, "fa_masked_softmax")
+    return out
 

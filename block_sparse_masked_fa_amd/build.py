@@ -33,6 +33,7 @@ SOURCES = [
     "bwd_bf16_d64.hip",
     "bwd_bf16_d128.hip",
     "decode_bf16.hip",
+    "masked_softmax.hip",
 ]
 
 # Per-source extra flags. The backward kernels keep two fp32 tiles, two

@@ -199,4 +199,20 @@ fa_status fa_flex_attention_decode_paged(
   return hip_status(fa::launch_split_combine(cl, stream), "split-KV merge launch");
 }
 
+fa_status fa_masked_softmax(int32_t BH, int32_t q_len, int32_t kv_len,
+                            int64_t q_offset, const void* scores,
+                            const int64_t score_stride[2],
+                            const fa_mask_mod* mask, void* probs,
+                            void* stream) {
+  std::string msg;
+  fa::SoftmaxLaunch p{};
+  bool nothing = false;
+  int st = fa::check_masked_softmax(BH, q_len, kv_len, q_offset, scores,
+                                    score_stride, mask, probs, &p, &nothing,
+                                    &msg);
+  if (st != FA_OK) return finish(st, msg);
+  if (nothing) return FA_OK;
+  return hip_status(fa::launch_masked_softmax(p, stream), "masked softmax launch");
+}
+
 }  // extern "C"

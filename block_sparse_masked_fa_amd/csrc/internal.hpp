@@ -118,6 +118,18 @@ struct DecodeLaunch {
   float* part_ml;
 };
 
+// Masked softmax over materialised scores: rows = (batch * head) * q_len
+// rows of kv_len scores; row i of a head is query position i + q_offset.
+struct SoftmaxLaunch {
+  int64_t rows;
+  int32_t q_len, kv_len;
+  int64_t q_offset;
+  const void* scores;   // bf16, element strides ss = (batch * head, row)
+  int64_t ss[2];
+  MaskParams mask;      // doc ids shared by every row (doc_stride 0)
+  void* probs;          // bf16 [rows, kv_len] contiguous
+};
+
 // Kernel launchers: return a hipError_t value (0 = success).
 int launch_block_mask(const BlockMaskLaunch& p, void* stream);
 int launch_fwd_bf16_d64(const FwdLaunch& p, void* stream);
@@ -127,6 +139,7 @@ int launch_split_combine(const CombineLaunch& p, void* stream);
 int launch_bwd_prepare(const BwdLaunch& p, void* stream);  // transposed lists
 int launch_zero_fill(void* dst, uint64_t bytes, void* stream);  // 16-byte aligned
 int launch_decode_paged(const DecodeLaunch& p, void* stream);
+int launch_masked_softmax(const SoftmaxLaunch& p, void* stream);
 int launch_bwd_bf16_d64(const BwdLaunch& p, void* stream);
 int launch_bwd_bf16_d128(const BwdLaunch& p, void* stream);
 

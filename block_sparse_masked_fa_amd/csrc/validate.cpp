@@ -571,4 +571,52 @@ int check_decode_paged(int32_t B, int32_t H, int32_t H_kv, int32_t D,
   return FA_OK;
 }
 
+int check_masked_softmax(int32_t BH, int32_t q_len, int32_t kv_len,
+                         int64_t q_offset, const void* scores,
+                         const int64_t score_stride[2],
+                         const fa_mask_mod* mask, void* probs,
+                         SoftmaxLaunch* out, bool* nothing_to_do,
+                         std::string* msg) {
+  *nothing_to_do = false;
+  if (BH < 0 || q_len < 0 || kv_len < 0)
+    return fail(msg, FA_ERR_INVALID_VALUE, "negative size");
+  if (q_offset < 0 || q_offset > (int64_t(1) << 30))
+    return fail(msg, FA_ERR_INVALID_VALUE, "q_offset must be in [0, 2^30]");
+  if (kv_len % 8 != 0)
+    return fail(msg, FA_ERR_UNSUPPORTED, "kv_len must be a multiple of 8 (16-byte rows)");
+  if (!mask) return fail(msg, FA_ERR_NULL_POINTER, "mask is NULL");
+  const int64_t qmax = q_offset + q_len;
+  int st = check_mask_mod(mask, static_cast<int32_t>(qmax > INT32_MAX ? INT32_MAX : qmax),
+                          kv_len, msg);
+  if (st != FA_OK) return st;
+  if (mask->kind == FA_MASK_DOCUMENT && mask->doc_stride != 0)
+    return fail(msg, FA_ERR_UNSUPPORTED, "the masked softmax takes one shared doc_id array");
+  if (mask->kind == FA_MASK_DOCUMENT && !aligned16(mask->doc_id))
+    return fail(msg, FA_ERR_UNSUPPORTED, "doc_id must be 16-byte aligned");
+  const int64_t rows = static_cast<int64_t>(BH) * q_len;
+  if (rows == 0 || kv_len == 0) {
+    *nothing_to_do = true;
+    return FA_OK;
+  }
+  if (rows / 4 + 1 > INT32_MAX) return fail(msg, FA_ERR_UNSUPPORTED, "too many rows");
+  if (!scores || !probs) return fail(msg, FA_ERR_NULL_POINTER, "scores or probs is NULL");
+  if (!score_stride) return fail(msg, FA_ERR_NULL_POINTER, "score_stride is NULL");
+  for (int d = 0; d < 2; ++d)
+    if (score_stride[d] < 0 || (score_stride[d] * 2) % 16 != 0)
+      return fail(msg, FA_ERR_UNSUPPORTED,
+                  "score strides must be >= 0 and multiples of 16 bytes");
+  if (!aligned16(scores) || !aligned16(probs))
+    return fail(msg, FA_ERR_UNSUPPORTED, "scores and probs must be 16-byte aligned");
+  out->rows = rows;
+  out->q_len = q_len;
+  out->kv_len = kv_len;
+  out->q_offset = q_offset;
+  out->scores = scores;
+  out->ss[0] = score_stride[0];
+  out->ss[1] = score_stride[1];
+  out->mask = MaskParams{mask->kind, mask->window, mask->doc_id, 0};
+  out->probs = probs;
+  return FA_OK;
+}
+
 }  // namespace fa

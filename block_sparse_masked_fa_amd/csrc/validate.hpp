@@ -88,4 +88,13 @@ int check_decode_paged(int32_t B, int32_t H, int32_t H_kv, int32_t D,
                        DecodeLaunch* out, CombineLaunch* cl,
                        bool* nothing_to_do, std::string* msg);
 
+// Fills *out for launch_masked_softmax on success; *nothing_to_do when
+// there is no row or no column.
+int check_masked_softmax(int32_t BH, int32_t q_len, int32_t kv_len,
+                         int64_t q_offset, const void* scores,
+                         const int64_t score_stride[2],
+                         const fa_mask_mod* mask, void* probs,
+                         SoftmaxLaunch* out, bool* nothing_to_do,
+                         std::string* msg);
+
 }  // namespace fa

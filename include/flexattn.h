@@ -23,6 +23,8 @@
  *                          mask (deterministic).
  *   fa_flex_attention_decode_paged  one decode step per sequence over a
  *                          paged key/value cache.
+ *   fa_masked_softmax      the masked softmax of a materialising fallback,
+ *                          mask folded into the score reads.
  *
  * Conventions shared by every entry point
  *   - Every pointer argument named "device" is HIP device memory owned by
@@ -47,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -370,6 +372,32 @@ fa_status fa_flex_attention_decode_paged(
     const int32_t* seq_lens, float scale, const fa_mask_mod* mask,
     const fa_score_mod* score, int32_t num_splits, void* workspace,
     uint64_t workspace_bytes, void* o, float* lse, void* stream);
+
+/* Masked softmax over materialised scores (bf16 in and out, fp32 inside):
+ * the compare / select-minimum / softmax chain of a materialising attention
+ * fallback as one kernel (MLX pull request "Fuse the causal mask into the
+ * SDPA fallback softmax"). For each of the BH * q_len rows, row i of a head
+ * being query position q_idx = i + q_offset, and column j key position j:
+ *   probs[row, j] = exp(s_j - m) / sum_{allowed} exp(s - m)  if
+ *                   mask_mod(q_idx, j) allows the pair, else exactly 0,
+ * m the maximum over the row's allowed scores; a row with no allowed key is
+ * all zeros. Scores outside a row's allowed key interval are not read; no
+ * mask or masked copy of the scores is written.
+ *
+ *   BH, q_len, kv_len  rows = BH * q_len; kv_len a multiple of 8.
+ *   q_offset   >= 0: earlier tokens before the first row (a prefill chunk).
+ *   scores     device bf16; row i of head slice b at b * score_stride[0] +
+ *              i * score_stride[1] (elements, multiples of 8), columns
+ *              contiguous; 16-byte aligned.
+ *   mask       host pointer, any built-in kind (doc_id: one shared array,
+ *              16-byte aligned, doc_len >= max(q_offset + q_len, kv_len)).
+ *   probs      device bf16 [BH, q_len, kv_len] contiguous, 16-byte aligned.
+ * One kernel launch; asynchronous. */
+fa_status fa_masked_softmax(int32_t BH, int32_t q_len, int32_t kv_len,
+                            int64_t q_offset, const void* scores,
+                            const int64_t score_stride[2],
+                            const fa_mask_mod* mask, void* probs,
+                            void* stream);
 
 /* Static description of a status code. */
 const char* fa_status_string(int32_t status);

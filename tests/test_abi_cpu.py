@@ -520,3 +520,43 @@ def test_auto_decode_splits():
     assert api.auto_decode_splits(1, 1, 128, 256) == 2
     assert api.auto_decode_splits(256, 8, 32768, 256) == 1
     assert api.auto_decode_splits(0, 8, 32768, 256) == 1
+
+
+def _softmax(**over):
+    a = dict(BH=2, q_len=64, kv_len=256, q_offset=0, scores=FAKE,
+             score_stride=(64 * 256, 256),
+             mask=C.fa_mask_mod(kind=C.FA_MASK_CAUSAL), probs=FAKE,
+             stream=None)
+    a.update(over)
+    return api.fa_masked_softmax(**a)
+
+
+@needs_lib
+@pytest.mark.parametrize("over,status", [
+    (dict(kv_len=250), C.FA_ERR_UNSUPPORTED),
+    (dict(q_offset=-1), C.FA_ERR_INVALID_VALUE),
+    (dict(BH=-1), C.FA_ERR_INVALID_VALUE),
+    (dict(scores=None), C.FA_ERR_NULL_POINTER),
+    (dict(probs=None), C.FA_ERR_NULL_POINTER),
+    (dict(scores=FAKE + 2), C.FA_ERR_UNSUPPORTED),
+    (dict(score_stride=(64 * 256, 250)), C.FA_ERR_UNSUPPORTED),
+    (dict(mask=C.fa_mask_mod(kind=C.FA_MASK_SLIDING_WINDOW, window=0)),
+     C.FA_ERR_INVALID_VALUE),
+    (dict(mask=C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT, doc_id=FAKE,
+                             doc_len=255)), C.FA_ERR_SHAPE_MISMATCH),
+    (dict(q_offset=300, mask=C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT, doc_id=FAKE,
+                                           doc_len=300)), C.FA_ERR_SHAPE_MISMATCH),
+    (dict(mask=C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT, doc_id=FAKE,
+                             doc_len=256, doc_stride=256)), C.FA_ERR_UNSUPPORTED),
+    (dict(mask=C.fa_mask_mod(kind=C.FA_MASK_DOCUMENT, doc_id=FAKE + 4,
+                             doc_len=256)), C.FA_ERR_UNSUPPORTED),
+])
+def test_masked_softmax_refuses(over, status):
+    st = _softmax(**over)
+    assert st == status, C.lib().fa_last_error()
+
+
+@needs_lib
+def test_masked_softmax_empty_is_a_noop():
+    assert _softmax(BH=0, scores=None, probs=None) == C.FA_OK
+    assert _softmax(kv_len=0, scores=None, probs=None) == C.FA_OK

@@ -26,6 +26,11 @@ key heads, head dim 128, pages of 128 token rows scattered over the pool in
 a seeded order, causal. See :class:`DecodeWorkload` and
 :func:`make_paged_inputs`.
 
+A seventh, ``softmax_fallback``, is the masked softmax of a materialising
+attention fallback at the size the MLX pull request quotes (one chunk of
+8192 query rows over 32768 keys, bf16 scores: 512 MiB), the last chunk of a
+causal prefill (query offset 24576); see :func:`make_scores`.
+
 Values are N(0, 1) from ``numpy.random.default_rng(seed)``, drawn as float32
 in (B, H, S, D) order: the document lengths first (``c4`` only), then Q, K
 and V. bf16 workloads are rounded to bf16 with round-to-nearest-even, and
@@ -40,7 +45,7 @@ import numpy as np
 
 __all__ = ["Workload", "CONFIGS", "get", "doc_lengths", "doc_ids",
            "draw_qkv", "make_inputs", "DecodeWorkload", "DECODE",
-           "make_paged_inputs"]
+           "make_paged_inputs", "SoftmaxWorkload", "SOFTMAX", "make_scores"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -209,4 +214,32 @@ def make_paged_inputs(w: DecodeWorkload, lens=None, poison=True):
     to = lambda x: torch.from_numpy(x).to(torch.bfloat16)  # noqa: E731
     return (to(q), to(kp), to(vp), torch.from_numpy(table),
             torch.from_numpy(lens.astype(np.int32)))
+
+
+@dataclasses.dataclass(frozen=True)
+class SoftmaxWorkload:
+    name: str
+    BH: int                 # batch * heads
+    q_len: int
+    kv_len: int
+    q_offset: int
+    seed: int
+    mask: str = "causal"
+    window: Optional[int] = None
+    spread: float = 2.0     # scores ~ N(0, spread^2)
+
+
+SOFTMAX = SoftmaxWorkload("softmax_fallback", BH=1, q_len=8192, kv_len=32768,
+                          q_offset=24576, seed=6)
+
+
+def make_scores(w: SoftmaxWorkload):
+    """Seeded bf16 scores ``[BH, q_len, kv_len]`` (CPU tensor), N(0,
+    spread^2) drawn as float32 and rounded to bf16 (RNE)."""
+    import torch
+
+    rng = np.random.default_rng(w.seed)
+    x = rng.standard_normal((w.BH, w.q_len, w.kv_len), dtype=np.float32)
+    x *= np.float32(w.spread)
+    return torch.from_numpy(x).to(torch.bfloat16)
 
