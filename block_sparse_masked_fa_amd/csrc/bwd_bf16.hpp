@@ -21,14 +21,15 @@
 //   * bwd_dkdv_kernel: one workgroup per (key block, key head), wave w owns
 //     keys [32w, 32w + 32); it walks the transposed lists (the query blocks
 //     that name the key block) and, with grouped heads, every query head of
-//     the group. Per 64-row stage of Q and dO in LDS: S = Q K^T and
+//     the group. Per 64-row stage of Q and dO in LDS (with each row's
+//     delta and exponent offset, which the dQ kernel stores): S = Q K^T and
 //     dP = dO V^T (K^T and V^T resident as B operands), then
 //     dV^T += dO^T P and dK^T += Q^T dT (dO and Q read transposed).
 // The layouts, swizzles and loads are the forward's (fwd_bf16.hpp). With
 // the roles of queries and keys exchanged in bwd_dkdv_kernel, a lane's
 // accumulator values share one key and span 16 query rows, so the per-row
-// terms (LSE, delta, document id) come from LDS and mask_mod is an interval
-// of query rows per key.
+// terms (exponent offset, delta, document id) come from LDS and mask_mod is
+// an interval of query rows per key.
 #pragma once
 
 #include "fwd_bf16.hpp"
@@ -132,7 +133,14 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLau
         part = __builtin_fmaf(static_cast<float>(ov[e]), static_cast<float>(dof[dk][e]), part);
     }
     delta_i = row_pair_sum(part);
-    if (i_ok && g == 0) bp.delta[orow] = delta_i;
+    if (i_ok && g == 0) {
+      bp.delta[orow] = delta_i;
+      // the row's exponent offset for the dK / dV kernel
+      float rt = lse_i == FA_NEG_INF ? FA_NEG_INF : -lse_i * kLog2e;
+      if (SCORE == FA_SCORE_ALIBI && lse_i != FA_NEG_INF)
+        rt -= make_score_consts(p, w.h).slope2 * static_cast<float>(i);
+      bp.rowterm[orow] = rt;
+    }
   }
   const int di = doc_mask ? doc[i_ok ? i : 0] : 0;
 
@@ -580,7 +588,7 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp
     }
     if (wave == 0) {
       const uint32_t r4 = static_cast<uint32_t>(min(i0 + lane, q_len - 1)) * 4;
-      hw::dma_dword(reinterpret_cast<const int*>(bp.lse + rowbase), hw::lds_addr(sL), r4);
+      hw::dma_dword(reinterpret_cast<const int*>(bp.rowterm + rowbase), hw::lds_addr(sL), r4);
       hw::dma_dword(reinterpret_cast<const int*>(bp.delta + rowbase), hw::lds_addr(sE), r4);
       if (doc_mask) hw::dma_dword(doc, hw::lds_addr(sD), r4);
     }
@@ -613,11 +621,14 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp
                                                       dpm, 0, 0, 0);
       }
 
-      // element r: query row i0 + 32 it + 8 (r / 4) + 4 g + r % 4
+      // element r: query row i0 + 32 it + 8 (r / 4) + 4 g + r % 4. The
+      // row's exponent offset (rowterm, from the dQ kernel) folds in -LSE
+      // and ALiBi's row part; the key part of ALiBi is tj.
+      const float tj = SCORE == FA_SCORE_ALIBI ? sc.slope2 * static_cast<float>(j) : 0.0f;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int il = 32 * it + 8 * r4 + 4 * g;  // first of 4 consecutive rows
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(sL + il);
+        const f32x4 rt4 = *reinterpret_cast<const f32x4*>(sL + il);
         const f32x4 del4 = *reinterpret_cast<const f32x4*>(sE + il);
         int4 d4 = {dj, dj, dj, dj};
         if (doc_mask && masked) d4 = *reinterpret_cast<const int4*>(sD + il);
@@ -625,23 +636,24 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int r = 4 * r4 + c;
-          const int irow = i0 + il + c;
-          float x = s[r], fp = 1.0f;
+          float arg, fp = 1.0f;
           if constexpr (SCORE == FA_SCORE_ALIBI) {
-            x = __builtin_fmaf(x, sc.c, sc.slope2 * static_cast<float>(j - irow));
+            arg = __builtin_fmaf(s[r], sc.c, rt4[c] + tj);
           } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
-            const float e = exp2_hw(x * (2.0f * sc.cap_in * kLog2e));
+            const float e = exp2_hw(s[r] * (2.0f * sc.cap_in * kLog2e));
             const float tt = __builtin_amdgcn_rcpf(e + 1.0f);
-            x = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out);
+            arg = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out + rt4[c]);
             fp = 4.0f * tt * (1.0f - tt);
           } else {
-            x *= sc.c;
+            arg = __builtin_fmaf(s[r], sc.c, rt4[c]);
           }
-          bool ok = true;
-          if (masked)
-            ok = (static_cast<unsigned>(irow - ilo) < ispan) & (dqs[c] == dj) & (irow < q_len);
-          const float l2 = lse4[c] == FA_NEG_INF ? __builtin_inff() : lse4[c] * kLog2e;
-          const float pr = ok ? exp2_hw(x - l2) : 0.0f;
+          float pr = exp2_hw(arg);
+          if (masked) {
+            const int irow = i0 + il + c;
+            const bool ok =
+                (static_cast<unsigned>(irow - ilo) < ispan) & (dqs[c] == dj) & (irow < q_len);
+            pr = ok ? pr : 0.0f;
+          }
           s[r] = pr;                                  // P
           dpm[r] = pr * (dpm[r] - del4[c]) * fp;      // dT
         }

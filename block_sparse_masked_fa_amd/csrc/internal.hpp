@@ -77,6 +77,11 @@ struct BwdLaunch {
   const float* lse;      // forward LSE, [B, H, q_len]
   const void* dout;      // dO, [B, H, q_len, D] contiguous
   float* delta;          // [B, H, q_len]: rowsum(dO * O), written by the dQ kernel
+  // [B, H, q_len]: each row's exponent offset, -LSE log2(e) (minus the
+  // ALiBi term slope_h log2(e) i), -inf for a row without keys; written by
+  // the dQ kernel so that P = exp2(scale log2(e) q.k [+ slope log2(e) j] +
+  // rowterm) in the dK / dV kernel
+  float* rowterm;
   // per key block, the query blocks that list it ([Bm, Hm, nkvb] and
   // [Bm, Hm, nkvb, nqb]); full_* NULL when the mask has no full lists
   int32_t* qnum;

@@ -354,6 +354,8 @@ int bwd_workspace_layout(int32_t B, int32_t H, int32_t q_len,
   uint64_t at = 0;
   ws->delta = at;
   at = align256(at + rows * 4u);
+  ws->rowterm = at;
+  at = align256(at + rows * 4u);
   ws->states = at;
   at = align256(at + bh * nqb * nkvb);
   ws->qnum = at;
@@ -436,6 +438,7 @@ int check_flex_attention_bwd(
   out->lse = lse;
   out->dout = dout;
   out->delta = reinterpret_cast<float*>(w + ws.delta);
+  out->rowterm = reinterpret_cast<float*>(w + ws.rowterm);
   out->states = reinterpret_cast<unsigned char*>(w + ws.states);
   out->qnum = reinterpret_cast<int32_t*>(w + ws.qnum);
   out->qidx = reinterpret_cast<int32_t*>(w + ws.qidx);

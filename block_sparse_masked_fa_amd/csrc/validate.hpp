@@ -51,10 +51,11 @@ int check_split(int32_t dtype, int32_t num_splits, void* workspace,
                 uint64_t workspace_bytes, FwdLaunch* p, CombineLaunch* cl,
                 std::string* msg);
 
-// Backward workspace: delta (fp32 per query row), the tile-state matrix and
-// the transposed block lists, each section 256-byte aligned.
+// Backward workspace: delta and the exponent offsets (fp32 per query row),
+// the tile-state matrix and the transposed block lists, each section
+// 256-byte aligned.
 struct BwdWorkspace {
-  uint64_t delta, states, qnum, qidx, fqnum, fqidx;  // byte offsets
+  uint64_t delta, rowterm, states, qnum, qidx, fqnum, fqidx;  // byte offsets
   uint64_t total;
 };
 int bwd_workspace_layout(int32_t B, int32_t H, int32_t q_len,

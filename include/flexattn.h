@@ -313,7 +313,8 @@ fa_status fa_flex_attention_bwd(
     uint64_t workspace_bytes, void* dq, void* dk, void* dv, void* stream);
 
 /* Workspace size of fa_flex_attention_bwd for a block mask: B * H * q_len
- * fp32 (delta), then bm->B * bm->H * NQB * NKVB bytes of tile states and the
+ * fp32 twice (delta and each row's exponent offset), then
+ * bm->B * bm->H * NQB * NKVB bytes of tile states and the
  * transposed lists (per key block a count and NQB indices, int32, twice
  * when bm->separate_full_blocks), each part rounded up to 256 bytes.
  * Host only (bm's dims are read, not its arrays); nothing is launched. */

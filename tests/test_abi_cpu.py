@@ -354,10 +354,11 @@ def test_auto_num_splits():
 
 
 def _bwd_ws_bytes(B, H, q_len, nq, nk, Bm=1, Hm=1, full=True):
-    # the documented layout: delta, tile states, then per key block a count
-    # and NQB indices (twice with full lists), each part rounded to 256
+    # the documented layout: delta and the row exponent offsets, tile
+    # states, then per key block a count and NQB indices (twice with full
+    # lists), each part rounded to 256
     r = lambda x: -(-x // 256) * 256  # noqa: E731
-    n = r(B * H * q_len * 4) + r(Bm * Hm * nq * nk)
+    n = 2 * r(B * H * q_len * 4) + r(Bm * Hm * nq * nk)
     n += r(Bm * Hm * nk * 4) + r(Bm * Hm * nk * nq * 4)
     if full:
         n += r(Bm * Hm * nk * 4) + r(Bm * Hm * nk * nq * 4)
