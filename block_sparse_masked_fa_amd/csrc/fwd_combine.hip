@@ -13,27 +13,53 @@
 namespace fa {
 namespace {
 
-// One wavefront per row; lane L holds elements [L * E, L * E + E) of D.
+// One wavefront per row. Lane r < nsplit (at most 64) fetches part r's
+// (m_r, l_r), so the maximum and the weights w_r = 2^(m_r - m) come from
+// wave reductions; then lane L accumulates elements [L * E, L * E + E) of D
+// over the parts, with the parts' loads issued four at a time.
 template <int D>
-__global__ __launch_bounds__(256) void split_combine_kernel(const CombineLaunch p) {
+__global__ __launch_bounds__(64) void split_combine_kernel(const CombineLaunch p) {
   constexpr int E = D / 64;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= p.rows) return;
-  const int lane = threadIdx.x & 63;
-  float m = FA_NEG_INF;
-  for (int r = 0; r < p.nsplit; ++r) m = __builtin_fmaxf(m, p.part_ml[2 * (r * p.rows + row)]);
-  float l = 0.0f;
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int ns = p.nsplit;
+  float mr = FA_NEG_INF, lr = 0.0f;
+  if (lane < ns) {
+    const int64_t pr = lane * p.rows + row;
+    mr = p.part_ml[2 * pr];
+    lr = p.part_ml[2 * pr + 1];
+  }
+  float m = mr;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  const float wr = mr == FA_NEG_INF ? 0.0f : exp2_hw(mr - m);
+  float l = wr * lr;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-  for (int r = 0; r < p.nsplit; ++r) {
-    const int64_t pr = r * p.rows + row;
-    const float mr = p.part_ml[2 * pr];
-    const float wr = mr == FA_NEG_INF ? 0.0f : exp2_hw(mr - m);
-    l = __builtin_fmaf(wr, p.part_ml[2 * pr + 1], l);
-    const float* po = p.part_o + pr * D + lane * E;
+  const float* base = p.part_o + row * D + lane * E;
+  const int64_t step = p.rows * D;  // between parts
+  int r = 0;
+  for (; r + 4 <= ns; r += 4) {
+    float v[4][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(wr, po[e], acc[e]);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[u][e] = base[(r + u) * step + e];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = __shfl(wr, r + u);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(w, v[u][e], acc[e]);
+    }
+  }
+  for (; r < ns; ++r) {
+    const float w = __shfl(wr, r);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(w, base[r * step + e], acc[e]);
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   __bf16* op = static_cast<__bf16*>(p.o) + row * D + lane * E;
@@ -47,11 +73,11 @@ __global__ __launch_bounds__(256) void split_combine_kernel(const CombineLaunch 
 
 int launch_split_combine(const CombineLaunch& p, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const dim3 grid(static_cast<unsigned>((p.rows + 3) / 4));
+  const dim3 grid(static_cast<unsigned>(p.rows));
   if (p.D == 64)
-    hipLaunchKernelGGL((split_combine_kernel<64>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((split_combine_kernel<64>), grid, dim3(64), 0, s, p);
   else if (p.D == 128)
-    hipLaunchKernelGGL((split_combine_kernel<128>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((split_combine_kernel<128>), grid, dim3(64), 0, s, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -319,6 +319,8 @@ int check_split(int32_t dtype, int32_t num_splits, void* workspace,
   const int64_t rows = static_cast<int64_t>(p->B) * p->H * p->q_len;
   if (static_cast<int64_t>(p->B) * p->H * p->nqb * num_splits > INT32_MAX)
     return fail(msg, FA_ERR_UNSUPPORTED, "too many split-KV workgroups");
+  if (rows > INT32_MAX)  // the merge runs one workgroup per row
+    return fail(msg, FA_ERR_UNSUPPORTED, "B * H * q_len too large for the split-KV merge");
   float* ws = static_cast<float*>(workspace);
   p->nsplit = num_splits;
   p->part_o = ws;
@@ -497,7 +499,8 @@ int check_decode_paged(int32_t B, int32_t H, int32_t H_kv, int32_t D,
     return fail(msg, FA_ERR_INVALID_VALUE,
                 "num_splits must be in [1, " + std::to_string(kMaxSplits) + "]");
   const int64_t wgs = static_cast<int64_t>(B) * H_kv * num_splits;
-  if (wgs > INT32_MAX) return fail(msg, FA_ERR_UNSUPPORTED, "too many workgroups");
+  if (wgs > INT32_MAX || static_cast<int64_t>(B) * H > INT32_MAX)
+    return fail(msg, FA_ERR_UNSUPPORTED, "too many workgroups");
   if (static_cast<int64_t>(B) * H == 0) {
     *nothing_to_do = true;
     return FA_OK;
