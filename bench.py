@@ -254,7 +254,7 @@ def main(argv=None) -> int:
     # fa_flex_attention_bwd call per repetition, O and LSE from an unsplit
     # forward, a seeded upstream gradient
     bwd = None
-    if not a.no_backward and w.dtype == "bf16" and w.block_m == w.block_n:
+    if not a.no_backward and w.dtype == "bf16":
         gen = torch.Generator(device=dev).manual_seed(w.seed)
         dout = torch.randn(qd.shape, generator=gen, device=dev).to(qd.dtype)
         o1, l1 = fa.flex_attention(qd, kd, vd, bm, score_mod=score,

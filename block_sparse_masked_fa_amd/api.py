@@ -490,8 +490,8 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     block_mask, score_mod, scale)`` for the upstream gradient ``dout``.
 
     bf16 only; ``o`` and ``lse`` are what the forward returned for the same
-    arguments; ``block_mask`` needs equal query and key block sizes (64 or
-    128). One fa_flex_attention_bwd call with a workspace allocated here;
+    arguments; ``block_mask`` block sizes in {64, 128} (an int or a pair).
+    One fa_flex_attention_bwd call with a workspace allocated here;
     the results are deterministic. ``dq_kv_order`` (default: the block
     mask's) is the order of dQ's sum over key blocks, True descending."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:

@@ -52,12 +52,12 @@ __device__ __forceinline__ bool xcd_kv_item(const FwdLaunch& p, int& b, int& hk,
 }
 
 // ---------------------------------------------------------------- dQ
-template <int D, int BLK, int SCORE>
-__global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLaunch bp) {
+template <int D, int BQ, int BK, int SCORE>
+__global__ __launch_bounds__(BQ * 2, 256 / BQ) void bwd_dq_kernel(const BwdLaunch bp) {
   const FwdLaunch& p = bp.f;
-  constexpr int NW = BLK / 32;
+  constexpr int NW = BQ / 32;
   constexpr int NT = NW * 64;
-  constexpr int SPB = BLK / kStageKeys;
+  constexpr int SPB = BK / kStageKeys;
   constexpr int RB = D * 2;
   constexpr int CPR = D / 8;
   constexpr int RPK = 1024 / RB;
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLau
   const int g = lane >> 5;
 
   const int hk = w.h / (p.H / p.H_kv);
-  const int i = w.m * BLK + wave * 32 + lq;
+  const int i = w.m * BQ + wave * 32 + lq;
   const bool i_ok = i < p.q_len;
   const int kv_len = p.kv_len;
   const int mkind = p.mask.kind;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLau
       if (take_p) ip += desc ? -1 : 1;
       else ifl += desc ? -1 : 1;
       c_n = static_cast<unsigned>(bsel) < static_cast<unsigned>(nkvb) ? bsel : -1;
-      c_masked = take_p || (c_n + 1) * BLK > kv_len;
+      c_masked = take_p || (c_n + 1) * BK > kv_len;
     }
     n = c_n;
     sub = desc ? SPB - 1 - c_sub : c_sub;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLau
   };
   auto issue = [&](int n, int sub, bool masked, char* sK, char* sV, int* sD) {
     if (n < 0) return;
-    const int j0 = n * BLK + sub * kStageKeys;
+    const int j0 = n * BK + sub * kStageKeys;
     // a stage of a ragged last block may lie wholly past the end: then the
     // buffers have size 0 and the tiles arrive as zeros
     const int rows_left = kv_len - j0;
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLau
   auto compute = [&](int n, int sub, bool masked, const char* sK, const char* sV,
                      const int* sD) {
     if (n < 0) return;
-    const int j0 = n * BLK + sub * kStageKeys;
+    const int j0 = n * BK + sub * kStageKeys;
 
     // Two halves of 32 keys each (jt), one after the other (one S and one
     // dP tile live at a time); each half's LDS operands are read ahead of
@@ -403,12 +403,12 @@ __global__ __launch_bounds__(BLK * 2, 256 / BLK) void bwd_dq_kernel(const BwdLau
 }
 
 // ------------------------------------------------------------- dK, dV
-template <int D, int BLK, int SCORE>
-__global__ __launch_bounds__(BLK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp) {
+template <int D, int BQ, int BK, int SCORE>
+__global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp) {
   const FwdLaunch& p = bp.f;
-  constexpr int NW = BLK / 32;
+  constexpr int NW = BK / 32;
   constexpr int NT = NW * 64;
-  constexpr int SPB = BLK / kStageKeys;  // 64-row query stages per query block
+  constexpr int SPB = BQ / kStageKeys;  // 64-row query stages per query block
   constexpr int RB = D * 2;
   constexpr int CPR = D / 8;
   constexpr int RPK = 1024 / RB;
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp
 
   const int q_len = p.q_len;
   const int kv_len = p.kv_len;
-  const int j = n * BLK + wave * 32 + lq;  // this lane's key
+  const int j = n * BK + wave * 32 + lq;  // this lane's key
   const bool j_ok = j < kv_len;
   const int mkind = p.mask.kind;
   const int window = p.mask.window;
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp
     m = c_m;
     h = hk * group + cg;
     sub = c_sub;
-    masked = c_it < c_np || (c_m + 1) * BLK > q_len || (n + 1) * BLK > kv_len;
+    masked = c_it < c_np || (c_m + 1) * BQ > q_len || (n + 1) * BK > kv_len;
     if (++c_sub == SPB) {
       c_sub = 0;
       ++c_it;
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp
     const int64_t rowbase = (static_cast<int64_t>(b) * p.H + h) * q_len;  // dO, LSE, delta
     const char* obase =
         reinterpret_cast<const char*>(static_cast<const __bf16*>(bp.dout) + rowbase * D);
-    const int i0 = m * BLK + sub * kStageKeys;
+    const int i0 = m * BQ + sub * kStageKeys;
     const int rows_left = q_len - i0;
     const int qrec = rows_left >= kStageKeys ? 0x7fffffff
                      : rows_left <= 0       ? 0
@@ -598,7 +598,7 @@ __global__ __launch_bounds__(BLK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp
                      const float* sL, const float* sE, const int* sD) {
     if (m < 0) return;
     const ScoreConsts sc = make_score_consts(p, h);
-    const int i0 = m * BLK + sub * kStageKeys;
+    const int i0 = m * BQ + sub * kStageKeys;
 
     // Two halves of 32 query rows each (it), one after the other: the
     // live fp32 tiles per half are one S and one dP tile, which leaves the

@@ -11,19 +11,23 @@ int launch_bwd_bf16_d128(const BwdLaunch& p, void* stream) {
   const int kv_items = f.B * f.H_kv * f.nkvb;
   const dim3 qgrid(static_cast<unsigned>((q_items + 7) / 8 * 8));  // whole XCD rounds
   const dim3 kgrid(static_cast<unsigned>((kv_items + 7) / 8 * 8));
-  switch (f.block_m * 4 + f.score_kind) {
-#define FA_CASE(BLK, SC)                                                                     \
-  case BLK * 4 + SC:                                                                         \
-    if (q_items > 0) hipLaunchKernelGGL((bwd_dq_kernel<128, BLK, SC>), qgrid, dim3(BLK * 2), 0, s, p); \
+  switch ((f.block_m * 1000 + f.block_n) * 4 + f.score_kind) {
+#define FA_CASE(BQ, BK, SC)                                                                  \
+  case (BQ * 1000 + BK) * 4 + SC:                                                            \
+    if (q_items > 0)                                                                         \
+      hipLaunchKernelGGL((bwd_dq_kernel<128, BQ, BK, SC>), qgrid, dim3(BQ * 2), 0, s, p);     \
     if (kv_items > 0)                                                                        \
-      hipLaunchKernelGGL((bwd_dkdv_kernel<128, BLK, SC>), kgrid, dim3(BLK * 2), 0, s, p);      \
+      hipLaunchKernelGGL((bwd_dkdv_kernel<128, BQ, BK, SC>), kgrid, dim3(BK * 2), 0, s, p);   \
     break;
-    FA_CASE(64, FA_SCORE_NONE)
-    FA_CASE(64, FA_SCORE_SOFTCAP)
-    FA_CASE(64, FA_SCORE_ALIBI)
-    FA_CASE(128, FA_SCORE_NONE)
-    FA_CASE(128, FA_SCORE_SOFTCAP)
-    FA_CASE(128, FA_SCORE_ALIBI)
+#define FA_CASES(BQ, BK)           \
+  FA_CASE(BQ, BK, FA_SCORE_NONE)    \
+  FA_CASE(BQ, BK, FA_SCORE_SOFTCAP) \
+  FA_CASE(BQ, BK, FA_SCORE_ALIBI)
+    FA_CASES(64, 64)
+    FA_CASES(64, 128)
+    FA_CASES(128, 64)
+    FA_CASES(128, 128)
+#undef FA_CASES
 #undef FA_CASE
     default:
       return hipErrorInvalidValue;

@@ -406,9 +406,6 @@ int check_flex_attention_bwd(
     out->dv = dv;
     return FA_OK;
   }
-  if (bm->block_m != bm->block_n)
-    return fail(msg, FA_ERR_UNSUPPORTED,
-                "the backward needs block_m == block_n (64 or 128)");
   const int64_t kv_items = static_cast<int64_t>(B) * H_kv * bm->num_kv_blocks;
   if (kv_items > INT32_MAX)
     return fail(msg, FA_ERR_UNSUPPORTED, "B * H_kv * num_kv_blocks too large");

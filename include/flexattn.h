@@ -278,9 +278,9 @@ fa_status fa_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
  * order); it changes only the rounding.
  *
  *   dtype      FA_BF16 only (FA_ERR_UNSUPPORTED otherwise).
- *   B ... score  as for fa_flex_attention_fwd, with the block mask's
- *              block_m == block_n in {64, 128}; bm and score must be the
- *              ones the forward ran with.
+ *   B ... score  as for fa_flex_attention_fwd (block_m, block_n in
+ *              {64, 128}); bm and score must be the ones the forward ran
+ *              with.
  *   dq_kv_order  0: each dQ row sums its live key blocks (partial and full
  *              lists merged by block index) in ascending block order; 1:
  *              descending, a block's later keys first. Other values:

@@ -402,8 +402,8 @@ def _bwd(**over):
     (dict(dq_kv_order=2), C.FA_ERR_INVALID_VALUE),
     (dict(dq_kv_order=-1), C.FA_ERR_INVALID_VALUE),
     (dict(bm=_bm(**{**{f: getattr(_good_bm(), f) for f, _ in
-                       C.fa_block_mask._fields_}, "block_n": 64,
-                    "num_kv_blocks": 4})), C.FA_ERR_UNSUPPORTED),
+                       C.fa_block_mask._fields_}, "block_n": 32,
+                    "num_kv_blocks": 8})), C.FA_ERR_UNSUPPORTED),
     (dict(workspace_bytes=_bwd_ws_bytes(2, 4, 256, 2, 2) - 1),
      C.FA_ERR_INVALID_VALUE),
     (dict(workspace=None), C.FA_ERR_NULL_POINTER),

@@ -254,9 +254,38 @@ def test_backward_dq_order(mask):
         TOL_BWD * max(1.0, float(np.abs(ref[0]).max()))
 
 
+PAIRS = []
+for D in (128, 64):
+    for bq, bk in ((128, 64), (64, 128)):
+        for mask in ("causal", "sliding_window", "document", "none", "local_window"):
+            for score in ("none", "softcap", "alibi"):
+                PAIRS.append((D, bq, bk, mask, score))
+
+
+@pytest.mark.parametrize("D,bq,bk,mask,score", PAIRS)
+def test_backward_block_size_pairs(D, bq, bk, mask, score):
+    # BLOCK_SIZE as a (q, kv) pair: query and key blocks of different sizes,
+    # ragged tails on both axes, grouped heads
+    ql, kl = 3 * bq + 29, 3 * bk + 77
+    w = WL.Workload("pair", "bf16", 2, 4, 2, ql, kl, D, mask, bq, bk, seed=0,
+                    window=bk + 21 if "window" in mask else None, score=score,
+                    softcap=3.0 if score == "softcap" else None)
+    rng = np.random.default_rng(zlib.crc32(f"bwdpair{D}{bq}{bk}{mask}{score}".encode()))
+    doc = (np.sort(rng.integers(0, 3, max(ql, kl))).astype(np.int32)
+           if mask == "document" else None)
+    q, k, v, do = _inputs(w, 37)
+    ref = oracle_bwd(w, q, k, v, do, doc)
+    bm = fa.create_block_mask(mask, None, None, ql, kl, device=DEV,
+                              BLOCK_SIZE=(bq, bk), window=w.window, doc_id=_doc_t(doc))
+    print(f"[bwd block pair] D={D} ({bq},{bk}) {mask} {score}", flush=True)
+    got = gpu_fwd_bwd(w, q, k, v, do, doc, bm=bm)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        assert_grad_close(g, r, f"{name} pair ({bq},{bk}) D={D} {mask} {score}")
+
+
 def test_backward_errors():
     bm = fa.create_block_mask("causal", None, None, 256, 256, device=DEV,
-                              BLOCK_SIZE=(128, 64))
+                              BLOCK_SIZE=(128, 32))
     q = torch.randn(1, 1, 256, 128, device=DEV).to(torch.bfloat16)
     lse = torch.zeros(1, 1, 256, device=DEV)
     with pytest.raises(fa.FlexAttnError, match="UNSUPPORTED"):
