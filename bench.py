@@ -260,9 +260,14 @@ def main(argv=None) -> int:
         o1, l1 = fa.flex_attention(qd, kd, vd, bm, score_mod=score,
                                    scale=w.scale, num_splits=1)
 
+        bwd_splits = fa.auto_bwd_splits(
+            w.B, w.H_kv, bm.num_kv_blocks,
+            torch.cuda.get_device_properties(dev).multi_processor_count)
+
         def bwd_call():
             return fa.flex_attention_backward(qd, kd, vd, o1, l1, dout, bm,
-                                              score_mod=score, scale=w.scale)
+                                              score_mod=score, scale=w.scale,
+                                              num_splits=bwd_splits)
         for _ in range(2):
             bwd_call()
         reps = max(3, min(a.steps, 20))
@@ -278,7 +283,7 @@ def main(argv=None) -> int:
         # algorithmic work: five products per live tile (S recomputed, dP,
         # dV, dK, dQ) = 2.5 x the forward's two
         bwd_flops = 2.5 * live_flops
-        bwd = {"ms": round(bwd_ms, 5), "reps": reps,
+        bwd = {"ms": round(bwd_ms, 5), "reps": reps, "num_splits": bwd_splits,
                "flops_per_call": bwd_flops,
                "tflops": round(bwd_flops / (bwd_ms * 1e-3) / 1e12, 2),
                "frac_of_peak": round(bwd_flops / (bwd_ms * 1e-3) / 1e12 / peak, 4),

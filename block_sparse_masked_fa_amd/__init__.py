@@ -12,7 +12,7 @@ from .api import (  # noqa: F401
     fa_bwd_workspace_bytes, fa_create_block_mask, fa_flex_attention_bwd,
     fa_flex_attention_fwd, fa_flex_attention_fwd_split,
     fa_split_workspace_bytes, flex_attention, flex_attention_backward,
-    auto_decode_splits, fa_flex_attention_decode_paged,
+    auto_bwd_splits, auto_decode_splits, fa_flex_attention_decode_paged,
     flex_attention_decode_paged, local_window, no_mask, masked_softmax,
     fa_masked_softmax,
     sliding_window,

@@ -40,7 +40,7 @@ FA_SCORE_ALIBI = 2
 # largest num_splits of fa_flex_attention_fwd_split
 FA_MAX_SPLITS = 64
 
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 
 class fa_mask_mod(ctypes.Structure):
@@ -113,12 +113,14 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
         ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
         ctypes.c_float, ctypes.POINTER(fa_block_mask),
-        ctypes.POINTER(fa_score_mod), ctypes.c_int32, ctypes.c_void_p,
-        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
-        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+        ctypes.POINTER(fa_score_mod), ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p]),
     "fa_bwd_workspace_bytes": (ctypes.c_int, [
-        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-        ctypes.POINTER(fa_block_mask), ctypes.POINTER(ctypes.c_uint64)]),
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(fa_block_mask),
+        ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]),
     "fa_flex_attention_decode_paged": (ctypes.c_int, [
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),

@@ -37,7 +37,7 @@ __all__ = [
     "fa_flex_attention_fwd", "fa_flex_attention_fwd_split",
     "fa_split_workspace_bytes", "auto_num_splits", "FlexAttnError",
     "flex_attention_backward", "fa_flex_attention_bwd",
-    "fa_bwd_workspace_bytes", "flex_attention_decode_paged",
+    "fa_bwd_workspace_bytes", "auto_bwd_splits", "flex_attention_decode_paged",
     "fa_flex_attention_decode_paged", "auto_decode_splits",
     "masked_softmax", "fa_masked_softmax",
 ]
@@ -204,22 +204,25 @@ def fa_flex_attention_bwd(dtype: int, B: int, H: int, H_kv: int, q_len: int,
                           kv_len: int, D: int, q: int, q_stride, k: int,
                           k_stride, v: int, v_stride, scale: float,
                           bm: C.fa_block_mask, score: Optional[C.fa_score_mod],
-                          dq_kv_order: int, o: int, lse: int, dout: int,
-                          workspace: Optional[int], workspace_bytes: int,
-                          dq: int, dk: int, dv: int,
+                          dq_kv_order: int, num_splits: int, o: int,
+                          lse: int, dout: int, workspace: Optional[int],
+                          workspace_bytes: int, dq: int, dk: int, dv: int,
                           stream: Optional[int]) -> int:
     return C.lib().fa_flex_attention_bwd(
         dtype, B, H, H_kv, q_len, kv_len, D,
         q, C.Stride3(*q_stride), k, C.Stride3(*k_stride),
         v, C.Stride3(*v_stride), scale, ctypes.byref(bm),
-        ctypes.byref(score) if score is not None else None, dq_kv_order, o,
-        lse, dout, workspace, workspace_bytes, dq, dk, dv, stream)
+        ctypes.byref(score) if score is not None else None, dq_kv_order,
+        num_splits, o, lse, dout, workspace, workspace_bytes, dq, dk, dv,
+        stream)
 
 
-def fa_bwd_workspace_bytes(B: int, H: int, q_len: int,
-                           bm: C.fa_block_mask) -> int:
+def fa_bwd_workspace_bytes(B: int, H: int, H_kv: int, q_len: int,
+                           kv_len: int, D: int, bm: C.fa_block_mask,
+                           num_splits: int = 1) -> int:
     n = ctypes.c_uint64()
-    C.check(C.lib().fa_bwd_workspace_bytes(B, H, q_len, ctypes.byref(bm),
+    C.check(C.lib().fa_bwd_workspace_bytes(B, H, H_kv, q_len, kv_len, D,
+                                           ctypes.byref(bm), num_splits,
                                            ctypes.byref(n)),
             "fa_bwd_workspace_bytes")
     return n.value
@@ -263,6 +266,19 @@ def auto_decode_splits(B: int, H_kv: int, max_tokens: int,
         return 1
     stages = max(1, -(-max_tokens // 64))
     return max(1, min(C.FA_MAX_SPLITS, stages, -(-8 * num_cus // wgs)))
+
+
+def auto_bwd_splits(B: int, H_kv: int, num_kv_blocks: int,
+                    num_cus: int) -> int:
+    """Parts per gradient row for the backward: 1 when the dK / dV kernel's
+    B * H_kv * NKVB workgroups (one resident per compute unit) already
+    cover the compute units, else enough parts for about two workgroups per
+    unit (the second wave of workgroups evens out rows of unequal length),
+    at most 16 and at most NKVB."""
+    wgs = B * H_kv * num_kv_blocks
+    if wgs == 0 or wgs >= num_cus:
+        return 1
+    return max(1, min(16, num_kv_blocks, -(-2 * num_cus // wgs)))
 
 
 def auto_num_splits(dtype: torch.dtype, B: int, H: int, num_q_blocks: int,
@@ -485,7 +501,8 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             o: torch.Tensor, lse: torch.Tensor,
                             dout: torch.Tensor, block_mask: BlockMask,
                             score_mod=None, scale: Optional[float] = None,
-                            dq_kv_order: Optional[bool] = None):
+                            dq_kv_order: Optional[bool] = None,
+                            num_splits: Optional[int] = None):
     """Gradients ``(dQ, dK, dV)`` of ``O = flex_attention(q, k, v,
     block_mask, score_mod, scale)`` for the upstream gradient ``dout``.
 
@@ -493,7 +510,9 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     arguments; ``block_mask`` block sizes in {64, 128} (an int or a pair).
     One fa_flex_attention_bwd call with a workspace allocated here;
     the results are deterministic. ``dq_kv_order`` (default: the block
-    mask's) is the order of dQ's sum over key blocks, True descending."""
+    mask's) is the order of dQ's sum over key blocks, True descending.
+    ``num_splits``: parts per gradient row (1 ... 64), added by one more
+    kernel; None picks :func:`auto_bwd_splits` for the device."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, H, S, D)")
     if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype
@@ -525,14 +544,20 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     if dq_kv_order is None:
         dq_kv_order = getattr(block_mask, "dq_kv_order", True)
     bm = block_mask.to_c()
-    nbytes = fa_bwd_workspace_bytes(B, H, q_len, bm)
+    if num_splits is None:
+        num_splits = auto_bwd_splits(
+            B, H_kv, block_mask.num_kv_blocks,
+            torch.cuda.get_device_properties(q.device).multi_processor_count)
+    nbytes = fa_bwd_workspace_bytes(B, H, H_kv, q_len, kv_len, D, bm,
+                                    num_splits)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
         st = fa_flex_attention_bwd(
             C.FA_BF16, B, H, H_kv, q_len, kv_len, D,
             q.data_ptr(), q.stride()[:3], k.data_ptr(), k.stride()[:3],
             v.data_ptr(), v.stride()[:3], float(scale), bm, score.to_c(),
-            int(bool(dq_kv_order)), o.data_ptr(), lse.data_ptr(),
+            int(bool(dq_kv_order)), int(num_splits), o.data_ptr(),
+            lse.data_ptr(),
             dout.data_ptr(), ws.data_ptr(),
             nbytes, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
             _stream_handle(q.device))

@@ -136,12 +136,14 @@ fa_status fa_flex_attention_fwd_split(
   return hip_status(fa::launch_split_combine(cl, stream), "split-KV merge launch");
 }
 
-fa_status fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
-                                 const fa_block_mask* bm, uint64_t* bytes) {
+fa_status fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t H_kv,
+                                 int32_t q_len, int32_t kv_len, int32_t D,
+                                 const fa_block_mask* bm, int32_t num_splits,
+                                 uint64_t* bytes) {
   std::string msg;
   if (!bytes) return finish(FA_ERR_NULL_POINTER, "bytes is NULL");
   fa::BwdWorkspace ws{};
-  int st = fa::bwd_workspace_layout(B, H, q_len, bm, &ws, &msg);
+  int st = fa::bwd_workspace_layout(B, H, H_kv, q_len, kv_len, D, bm, num_splits, &ws, &msg);
   if (st != FA_OK) return finish(st, msg);
   *bytes = ws.total;
   return FA_OK;
@@ -152,15 +154,15 @@ fa_status fa_flex_attention_bwd(
     int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
     const void* k, const int64_t k_stride[3], const void* v,
     const int64_t v_stride[3], float scale, const fa_block_mask* bm,
-    const fa_score_mod* score, int32_t dq_kv_order, const void* o,
-    const float* lse, const void* dout, void* workspace,
+    const fa_score_mod* score, int32_t dq_kv_order, int32_t num_splits,
+    const void* o, const float* lse, const void* dout, void* workspace,
     uint64_t workspace_bytes, void* dq, void* dk, void* dv, void* stream) {
   std::string msg;
   fa::BwdLaunch p{};
   bool nothing = false;
   int st = fa::check_flex_attention_bwd(
       dtype, B, H, H_kv, q_len, kv_len, D, q, q_stride, k, k_stride, v,
-      v_stride, scale, bm, score, dq_kv_order, o, lse, dout, workspace,
+      v_stride, scale, bm, score, dq_kv_order, num_splits, o, lse, dout, workspace,
       workspace_bytes, dq, dk, dv, &p, &nothing, &msg);
   if (st != FA_OK) return finish(st, msg);
   if (nothing) {
@@ -172,7 +174,16 @@ fa_status fa_flex_attention_bwd(
   int err = fa::launch_bwd_prepare(p, stream);
   if (err != 0) return hip_status(err, "backward preparation launch");
   err = D == 64 ? fa::launch_bwd_bf16_d64(p, stream) : fa::launch_bwd_bf16_d128(p, stream);
-  return hip_status(err, "attention backward launch");
+  if (err != 0 || p.kv_splits == 1) return hip_status(err, "attention backward launch");
+  // split mode: the parts' sums, in part order
+  const uint64_t q_elems = static_cast<uint64_t>(B) * H * q_len * D;
+  const uint64_t kv_elems = static_cast<uint64_t>(B) * H_kv * kv_len * D;
+  err = fa::launch_reduce_parts(p.part_dq, dq, p.f.scale, nullptr, nullptr, 0.0f, q_elems,
+                                p.kv_splits, stream);
+  if (err == 0)
+    err = fa::launch_reduce_parts(p.part_dk, dk, p.f.scale, p.part_dv, dv, 1.0f, kv_elems,
+                                  p.kv_splits, stream);
+  return hip_status(err, "split backward merge launch");
 }
 
 fa_status fa_flex_attention_decode_paged(

@@ -38,14 +38,17 @@ namespace fa {
 
 // Workgroup -> (batch, key head, key block) for the dK / dV kernel: dealt to
 // the 8 XCDs in contiguous ranges (one head's blocks share an L2).
-__device__ __forceinline__ bool xcd_kv_item(const FwdLaunch& p, int& b, int& hk, int& n) {
-  const int total = p.B * p.H_kv * p.nkvb;
+__device__ __forceinline__ bool xcd_kv_item(const FwdLaunch& p, int nsplit, int& b, int& hk,
+                                            int& n, int& c) {
+  const int total = p.B * p.H_kv * p.nkvb * nsplit;
   const int per_xcd = (total + 7) >> 3;
   const int wg = blockIdx.x;
   const int logical = (wg & 7) * per_xcd + (wg >> 3);
   if (logical >= total) return false;
-  n = logical % p.nkvb;
-  const int bh = logical / p.nkvb;
+  c = logical % nsplit;  // the parts of one key block run side by side
+  const int item = logical / nsplit;
+  n = item % p.nkvb;
+  const int bh = item / p.nkvb;
   hk = bh % p.H_kv;
   b = bh / p.H_kv;
   return true;
@@ -133,7 +136,7 @@ __global__ __launch_bounds__(BQ * 2, 256 / BQ) void bwd_dq_kernel(const BwdLaunc
         part = __builtin_fmaf(static_cast<float>(ov[e]), static_cast<float>(dof[dk][e]), part);
     }
     delta_i = row_pair_sum(part);
-    if (i_ok && g == 0) {
+    if (i_ok && g == 0 && w.c == 0) {
       bp.delta[orow] = delta_i;
       // the row's exponent offset for the dK / dV kernel
       float rt = lse_i == FA_NEG_INF ? FA_NEG_INF : -lse_i * kLog2e;
@@ -153,7 +156,11 @@ __global__ __launch_bounds__(BQ * 2, 256 / BQ) void bwd_dq_kernel(const BwdLaunc
   const const_i32* fl = (const const_i32*)(p.fidx ? p.fidx + lrow * nkvb : p.idx);
   const const_i32* pl = (const const_i32*)(p.idx + lrow * nkvb);
   const int nblocks = nf + np;
-  const int nstages = nblocks * SPB;
+  // part w.c of p.nsplit: block visits [v0, v0 + nvis) of the merged order
+  const int per_part = (nblocks + p.nsplit - 1) / p.nsplit;
+  const int v0 = min(w.c * per_part, nblocks);
+  const int nvis = min(per_part, nblocks - v0);
+  const int nstages = nvis * SPB;
 
   const ScoreConsts sc = make_score_consts(p, w.h);
   const int hi_abs =
@@ -205,6 +212,15 @@ __global__ __launch_bounds__(BQ * 2, 256 / BQ) void bwd_dq_kernel(const BwdLaunc
   int ifl = desc ? nf - 1 : 0;
   int c_n = -1, c_sub = 0;
   bool c_masked = false;
+  // this part's first visit: skip v0 blocks of the merged order
+  for (int v = 0; v < v0; ++v) {
+    const bool p_left = desc ? ip >= 0 : ip < np;
+    const bool f_left = desc ? ifl >= 0 : ifl < nf;
+    bool take_p = p_left;
+    if (p_left && f_left) take_p = desc ? pl[ip] > fl[ifl] : pl[ip] < fl[ifl];
+    if (take_p) ip += desc ? -1 : 1;
+    else ifl += desc ? -1 : 1;
+  }
   // the next stage: key block n (-1: an index outside [0, NKVB), skipped),
   // its 64-key stage sub, and whether mask_mod applies. Called once per
   // stage, in order, nstages times.
@@ -389,7 +405,16 @@ __global__ __launch_bounds__(BQ * 2, 256 / BQ) void bwd_dq_kernel(const BwdLaunc
     mk_cur = mk_nxt;
   }
 
-  if (i_ok) {
+  if (i_ok && p.nsplit > 1) {
+    // this part's unscaled sum; the parts are added in order afterwards
+    float* po = bp.part_dq + (static_cast<int64_t>(w.c) * p.B * p.H * p.q_len + orow) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4*>(po + dt * 32 + 8 * q4 + 4 * g) =
+            f32x4{dq[dt][4 * q4 + 0], dq[dt][4 * q4 + 1], dq[dt][4 * q4 + 2], dq[dt][4 * q4 + 3]};
+  } else if (i_ok) {
     __bf16* out = static_cast<__bf16*>(bp.dq) + orow * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -426,8 +451,9 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
   __shared__ __attribute__((aligned(16))) float sE0[kStageKeys], sE1[kStageKeys];
   __shared__ __attribute__((aligned(16))) int sD0[kStageKeys], sD1[kStageKeys];
 
-  int b, hk, n;
-  if (!xcd_kv_item(p, b, hk, n)) return;
+  int b, hk, n, c;
+  const int nsplit = bp.kv_splits;
+  if (!xcd_kv_item(p, nsplit, b, hk, n, c)) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -525,18 +551,39 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
     pl = (const const_i32*)(bp.qidx + col * nqb);
     fl = (const const_i32*)(bp.fqidx ? bp.fqidx + col * nqb : bp.qidx);
   };
-  int total = 0;
+  int all_blocks = 0;
   for (int gi = 0; gi < group; ++gi) {
     int np, nf;
     const const_i32 *pl, *fl;
     head_lists(gi, np, nf, pl, fl);
-    total += (np + nf) * SPB;
+    all_blocks += np + nf;
   }
+  // part c of nsplit: block visits [v0, v0 + nvis) of the sequence
+  const int per_part = (all_blocks + nsplit - 1) / nsplit;
+  const int v0 = min(c * per_part, all_blocks);
+  const int total = min(per_part, all_blocks - v0) * SPB;
 
   // cursor over the sequence: head cg, its lists, the next block visit
   int cg = -1, c_np = 0, c_nf = 0, c_left = 0, c_it = 0, c_sub = 0, c_m = -1;
   const const_i32* c_pl = nullptr;
   const const_i32* c_fl = nullptr;
+  // skip the visits of the earlier parts (whole blocks: c_sub stays 0)
+  {
+    int skip = v0 * SPB;
+    while (skip > 0) {
+      if (c_left == 0) {
+        ++cg;
+        head_lists(cg, c_np, c_nf, c_pl, c_fl);
+        c_left = (c_np + c_nf) * SPB;
+        c_it = 0;
+        continue;
+      }
+      const int t = min(skip, c_left);
+      skip -= t;
+      c_left -= t;
+      c_it += t / SPB;
+    }
+  }
   // the next stage: query block m (-1: an index outside [0, NQB), skipped),
   // head h, 64-row stage sub of the block, and whether mask_mod applies.
   // Called exactly `total` times, so a head with stages left always exists.
@@ -729,7 +776,22 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
     mk_cur = mk_nxt;
   }
 
-  if (j_ok) {
+  if (j_ok && nsplit > 1) {
+    // this part's unscaled sums; the parts are added in order afterwards
+    const int64_t krow = (static_cast<int64_t>(b) * p.H_kv + hk) * kv_len + j;
+    const int64_t prow = static_cast<int64_t>(c) * p.B * p.H_kv * kv_len + krow;
+    float* pk = bp.part_dk + prow * D;
+    float* pv = bp.part_dv + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        *reinterpret_cast<f32x4*>(pk + dt * 32 + 8 * q4 + 4 * g) =
+            f32x4{dk[dt][4 * q4 + 0], dk[dt][4 * q4 + 1], dk[dt][4 * q4 + 2], dk[dt][4 * q4 + 3]};
+        *reinterpret_cast<f32x4*>(pv + dt * 32 + 8 * q4 + 4 * g) =
+            f32x4{dv[dt][4 * q4 + 0], dv[dt][4 * q4 + 1], dv[dt][4 * q4 + 2], dv[dt][4 * q4 + 3]};
+      }
+  } else if (j_ok) {
     const int64_t krow = (static_cast<int64_t>(b) * p.H_kv + hk) * kv_len + j;
     __bf16* outk = static_cast<__bf16*>(bp.dk) + krow * D;
     __bf16* outv = static_cast<__bf16*>(bp.dv) + krow * D;

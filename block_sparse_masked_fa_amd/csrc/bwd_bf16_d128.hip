@@ -7,8 +7,8 @@ namespace fa {
 int launch_bwd_bf16_d128(const BwdLaunch& p, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const FwdLaunch& f = p.f;
-  const int q_items = f.B * f.H * f.nqb;
-  const int kv_items = f.B * f.H_kv * f.nkvb;
+  const int q_items = f.B * f.H * f.nqb * f.nsplit;
+  const int kv_items = f.B * f.H_kv * f.nkvb * p.kv_splits;
   const dim3 qgrid(static_cast<unsigned>((q_items + 7) / 8 * 8));  // whole XCD rounds
   const dim3 kgrid(static_cast<unsigned>((kv_items + 7) / 8 * 8));
   switch ((f.block_m * 1000 + f.block_n) * 4 + f.score_kind) {

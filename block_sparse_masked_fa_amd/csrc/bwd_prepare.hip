@@ -5,6 +5,8 @@
 //     their origin) through a dense byte matrix of tile states: cleared,
 //     scattered per query-block row, then compacted per key-block column
 //     with wavefront ballots and prefix counts.
+// and the split backward's last step: the parts' fp32 gradient sums added in
+// part order, scaled and rounded to bf16.
 #include <hip/hip_runtime.h>
 
 #include "fwd_common.hpp"
@@ -98,7 +100,51 @@ __global__ __launch_bounds__(kThreads) void zero16_kernel(uint4* dst, int64_t n1
     dst[t] = uint4{0u, 0u, 0u, 0u};
 }
 
+// out[e] = bf16(mul * (parts[0][e] + parts[1][e] + ...)), parts added in
+// index order; 8 elements per thread and iteration, two segments (dK and
+// dV: same size, own scale) per launch.
+struct ReduceSeg {
+  const float* parts;
+  __bf16* out;
+  float mul;
+};
+
+__global__ __launch_bounds__(kThreads) void reduce_parts_kernel(ReduceSeg s0, ReduceSeg s1,
+                                                                int nseg, int64_t n8,
+                                                                int64_t part_elems, int nsplit) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int sg = 0; sg < nseg; ++sg) {
+    const ReduceSeg sd = sg == 0 ? s0 : s1;
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; t < n8; t += stride) {
+      const float* src = sd.parts + t * 8;
+      f32x4 a = *reinterpret_cast<const f32x4*>(src);
+      f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+      for (int c = 1; c < nsplit; ++c) {
+        src += part_elems;
+        a += *reinterpret_cast<const f32x4*>(src);
+        b += *reinterpret_cast<const f32x4*>(src + 4);
+      }
+      const f32x8 r = {a[0] * sd.mul, a[1] * sd.mul, a[2] * sd.mul, a[3] * sd.mul,
+                       b[0] * sd.mul, b[1] * sd.mul, b[2] * sd.mul, b[3] * sd.mul};
+      *reinterpret_cast<bf16x8*>(sd.out + t * 8) = __builtin_convertvector(r, bf16x8);
+    }
+  }
+}
+
 }  // namespace
+
+int launch_reduce_parts(const float* parts0, void* out0, float mul0, const float* parts1,
+                        void* out1, float mul1, uint64_t elems, int nsplit, void* stream) {
+  const int64_t n8 = static_cast<int64_t>(elems / 8);
+  if (n8 == 0) return hipSuccess;
+  const ReduceSeg s0{parts0, static_cast<__bf16*>(out0), mul0};
+  const ReduceSeg s1{parts1, static_cast<__bf16*>(out1), mul1};
+  const int64_t g = (n8 + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3(static_cast<unsigned>(g < 4096 ? g : 4096)),
+                     dim3(kThreads), 0, static_cast<hipStream_t>(stream), s0, s1,
+                     parts1 ? 2 : 1, n8, static_cast<int64_t>(elems), nsplit);
+  return hipGetLastError();
+}
 
 int launch_zero_fill(void* dst, uint64_t bytes, void* stream) {
   const int64_t n16 = static_cast<int64_t>(bytes / 16);

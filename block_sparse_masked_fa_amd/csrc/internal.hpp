@@ -93,6 +93,15 @@ struct BwdLaunch {
   void* dk;              // [B, H_kv, kv_len, D] contiguous, bf16
   void* dv;
   int32_t dq_kv_order;   // dQ accumulation over key blocks: 0 ascending, 1 descending
+  // Split mode (kv_splits > 1, f.nsplit the same count): each key block's
+  // visit sequence of the dK / dV kernel, and each query row's of the dQ
+  // kernel, is cut into kv_splits parts run by separate workgroups; every
+  // part writes its unscaled fp32 sums to part_* ([part][rows][D]), and
+  // launch_reduce_parts adds them in part order. NULL when kv_splits == 1.
+  int32_t kv_splits;
+  float* part_dq;        // [kv_splits, B, H, q_len, D]
+  float* part_dk;        // [kv_splits, B, H_kv, kv_len, D]
+  float* part_dv;
   // no query rows (q_len == 0) but keys: bytes of dk and of dv to clear,
   // nothing else runs
   uint64_t zero_bytes;
@@ -142,6 +151,11 @@ int launch_fwd_bf16_d128(const FwdLaunch& p, void* stream);
 int launch_fwd_fp32(const FwdLaunch& p, void* stream);
 int launch_split_combine(const CombineLaunch& p, void* stream);
 int launch_bwd_prepare(const BwdLaunch& p, void* stream);  // transposed lists
+// out_s = bf16(mul_s * sum over nsplit parts of parts_s), parts
+// [nsplit][elems] fp32, added in part order; segment 1 optional (parts1
+// NULL). elems a multiple of 8.
+int launch_reduce_parts(const float* parts0, void* out0, float mul0, const float* parts1,
+                        void* out1, float mul1, uint64_t elems, int nsplit, void* stream);
 int launch_zero_fill(void* dst, uint64_t bytes, void* stream);  // 16-byte aligned
 int launch_decode_paged(const DecodeLaunch& p, void* stream);
 int launch_masked_softmax(const SoftmaxLaunch& p, void* stream);

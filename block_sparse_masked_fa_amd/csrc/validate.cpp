@@ -339,12 +339,15 @@ namespace {
 uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 }  // namespace
 
-int bwd_workspace_layout(int32_t B, int32_t H, int32_t q_len,
-                         const fa_block_mask* bm, BwdWorkspace* ws,
-                         std::string* msg) {
+int bwd_workspace_layout(int32_t B, int32_t H, int32_t H_kv, int32_t q_len,
+                         int32_t kv_len, int32_t D, const fa_block_mask* bm,
+                         int32_t num_splits, BwdWorkspace* ws, std::string* msg) {
   if (!bm || !ws) return fail(msg, FA_ERR_NULL_POINTER, "block mask or output is NULL");
-  if (B < 0 || H < 0 || q_len < 0)
+  if (B < 0 || H < 0 || H_kv < 0 || q_len < 0 || kv_len < 0 || D < 0)
     return fail(msg, FA_ERR_INVALID_VALUE, "negative size");
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(msg, FA_ERR_INVALID_VALUE,
+                "num_splits must be in [1, " + std::to_string(kMaxSplits) + "]");
   if (bm->B < 1 || bm->H < 1 || bm->num_q_blocks < 0 || bm->num_kv_blocks < 0)
     return fail(msg, FA_ERR_INVALID_VALUE, "block mask dims must be positive");
   const uint64_t rows = static_cast<uint64_t>(B) * static_cast<uint64_t>(H) *
@@ -368,6 +371,17 @@ int bwd_workspace_layout(int32_t B, int32_t H, int32_t q_len,
   at = full ? align256(at + bh * nkvb * 4u) : at;
   ws->fqidx = at;
   at = full ? align256(at + bh * nkvb * nqb * 4u) : at;
+  // split mode: every part's fp32 sums of dQ, dK and dV
+  const uint64_t parts = num_splits > 1 ? static_cast<uint64_t>(num_splits) : 0u;
+  const uint64_t krows = static_cast<uint64_t>(B) * static_cast<uint64_t>(H_kv) *
+                         static_cast<uint64_t>(kv_len);
+  const uint64_t d = static_cast<uint64_t>(D);
+  ws->part_dq = at;
+  at = align256(at + parts * rows * d * 4u);
+  ws->part_dk = at;
+  at = align256(at + parts * krows * d * 4u);
+  ws->part_dv = at;
+  at = align256(at + parts * krows * d * 4u);
   ws->total = at;
   return FA_OK;
 }
@@ -377,8 +391,8 @@ int check_flex_attention_bwd(
     int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
     const void* k, const int64_t k_stride[3], const void* v,
     const int64_t v_stride[3], float scale, const fa_block_mask* bm,
-    const fa_score_mod* score, int32_t dq_kv_order, const void* o,
-    const float* lse, const void* dout, void* workspace,
+    const fa_score_mod* score, int32_t dq_kv_order, int32_t num_splits,
+    const void* o, const float* lse, const void* dout, void* workspace,
     uint64_t workspace_bytes, void* dq, void* dk, void* dv, BwdLaunch* out,
     bool* nothing_to_do, std::string* msg) {
   *nothing_to_do = false;
@@ -386,6 +400,9 @@ int check_flex_attention_bwd(
     return fail(msg, FA_ERR_UNSUPPORTED, "the backward is built for bf16 only");
   if (dq_kv_order != 0 && dq_kv_order != 1)
     return fail(msg, FA_ERR_INVALID_VALUE, "dq_kv_order must be 0 or 1");
+  if (num_splits < 1 || num_splits > kMaxSplits)
+    return fail(msg, FA_ERR_INVALID_VALUE,
+                "num_splits must be in [1, " + std::to_string(kMaxSplits) + "]");
   // the forward's checks (o is only read here; the descriptor field is unused)
   int st = check_flex_attention_fwd(dtype, B, H, H_kv, q_len, kv_len, D, q,
                                     q_stride, k, k_stride, v, v_stride, scale,
@@ -406,11 +423,16 @@ int check_flex_attention_bwd(
     out->dv = dv;
     return FA_OK;
   }
-  const int64_t kv_items = static_cast<int64_t>(B) * H_kv * bm->num_kv_blocks;
+  const int64_t kv_items = static_cast<int64_t>(B) * H_kv * bm->num_kv_blocks * num_splits;
   if (kv_items > INT32_MAX)
-    return fail(msg, FA_ERR_UNSUPPORTED, "B * H_kv * num_kv_blocks too large");
+    return fail(msg, FA_ERR_UNSUPPORTED, "B * H_kv * num_kv_blocks * num_splits too large");
+  const int64_t q_items = static_cast<int64_t>(B) * H * bm->num_q_blocks * num_splits;
+  if (q_items > INT32_MAX)
+    return fail(msg, FA_ERR_UNSUPPORTED, "B * H * num_q_blocks * num_splits too large");
   BwdWorkspace ws{};
-  if ((st = bwd_workspace_layout(B, H, q_len, bm, &ws, msg)) != FA_OK) return st;
+  if ((st = bwd_workspace_layout(B, H, H_kv, q_len, kv_len, D, bm, num_splits, &ws, msg)) !=
+      FA_OK)
+    return st;
   if (!o || !lse || !dout || !dq)
     return fail(msg, FA_ERR_NULL_POINTER, "o, lse, dout or dq is NULL");
   if (kv_len > 0 && (!dk || !dv))
@@ -447,6 +469,12 @@ int check_flex_attention_bwd(
   out->dk = dk;
   out->dv = dv;
   out->dq_kv_order = dq_kv_order;
+  out->f.nsplit = num_splits;
+  out->kv_splits = num_splits;
+  const bool split = num_splits > 1;
+  out->part_dq = split ? reinterpret_cast<float*>(w + ws.part_dq) : nullptr;
+  out->part_dk = split ? reinterpret_cast<float*>(w + ws.part_dk) : nullptr;
+  out->part_dv = split ? reinterpret_cast<float*>(w + ws.part_dv) : nullptr;
   return FA_OK;
 }
 

@@ -55,12 +55,13 @@ int check_split(int32_t dtype, int32_t num_splits, void* workspace,
 // the tile-state matrix and the transposed block lists, each section
 // 256-byte aligned.
 struct BwdWorkspace {
-  uint64_t delta, rowterm, states, qnum, qidx, fqnum, fqidx;  // byte offsets
+  // byte offsets; part_* only with num_splits > 1
+  uint64_t delta, rowterm, states, qnum, qidx, fqnum, fqidx, part_dq, part_dk, part_dv;
   uint64_t total;
 };
-int bwd_workspace_layout(int32_t B, int32_t H, int32_t q_len,
-                         const fa_block_mask* bm, BwdWorkspace* ws,
-                         std::string* msg);
+int bwd_workspace_layout(int32_t B, int32_t H, int32_t H_kv, int32_t q_len,
+                         int32_t kv_len, int32_t D, const fa_block_mask* bm,
+                         int32_t num_splits, BwdWorkspace* ws, std::string* msg);
 
 // Fills *out for the backward launchers on success (the forward checks plus
 // the backward's own restrictions). *nothing_to_do as for the forward.
@@ -69,8 +70,8 @@ int check_flex_attention_bwd(
     int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
     const void* k, const int64_t k_stride[3], const void* v,
     const int64_t v_stride[3], float scale, const fa_block_mask* bm,
-    const fa_score_mod* score, int32_t dq_kv_order, const void* o,
-    const float* lse, const void* dout, void* workspace,
+    const fa_score_mod* score, int32_t dq_kv_order, int32_t num_splits,
+    const void* o, const float* lse, const void* dout, void* workspace,
     uint64_t workspace_bytes, void* dq, void* dk, void* dv, BwdLaunch* out,
     bool* nothing_to_do, std::string* msg);
 

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -285,6 +285,15 @@ fa_status fa_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
  *              lists merged by block index) in ascending block order; 1:
  *              descending, a block's later keys first. Other values:
  *              FA_ERR_INVALID_VALUE.
+ *   num_splits 1 ... 64 (FA_ERR_INVALID_VALUE otherwise): 1 accumulates
+ *              each gradient row in one workgroup. More cut each dQ row's
+ *              and each dK / dV row's sequence of live blocks (in the
+ *              order above) into num_splits consecutive parts of equal
+ *              block count, run by separate workgroups, for grids too small
+ *              to fill the GPU; each part's fp32 sum goes to the workspace
+ *              and one more kernel adds the parts in part order, then
+ *              scales and rounds. Still deterministic; the results differ
+ *              from num_splits = 1 by rounding only.
  *   o          device bf16 [B, H, q_len, D], contiguous: the forward's output.
  *   lse        device fp32 [B, H, q_len], contiguous: the forward's lse.
  *              Gradients are only meaningful for the o and lse that the
@@ -302,24 +311,29 @@ fa_status fa_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
  * Five kernel launches: three that transpose the block lists into
  * per-key-block lists of query blocks (clear, scatter, compact), the dQ
  * kernel (which also forms delta = rowsum(dO * O)), then the dK / dV
- * kernel; asynchronous. */
+ * kernel, and with num_splits > 1 two that add the parts; asynchronous. */
 fa_status fa_flex_attention_bwd(
     int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t q_len,
     int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
     const void* k, const int64_t k_stride[3], const void* v,
     const int64_t v_stride[3], float scale, const fa_block_mask* bm,
-    const fa_score_mod* score, int32_t dq_kv_order, const void* o,
-    const float* lse, const void* dout, void* workspace,
+    const fa_score_mod* score, int32_t dq_kv_order, int32_t num_splits,
+    const void* o, const float* lse, const void* dout, void* workspace,
     uint64_t workspace_bytes, void* dq, void* dk, void* dv, void* stream);
 
 /* Workspace size of fa_flex_attention_bwd for a block mask: B * H * q_len
  * fp32 twice (delta and each row's exponent offset), then
  * bm->B * bm->H * NQB * NKVB bytes of tile states and the
  * transposed lists (per key block a count and NQB indices, int32, twice
- * when bm->separate_full_blocks), each part rounded up to 256 bytes.
- * Host only (bm's dims are read, not its arrays); nothing is launched. */
-fa_status fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t q_len,
-                                 const fa_block_mask* bm, uint64_t* bytes);
+ * when bm->separate_full_blocks), and with num_splits > 1 the parts' fp32
+ * sums: num_splits * D * (B * H * q_len + 2 * B * H_kv * kv_len) * 4
+ * bytes; each piece rounded up to 256 bytes. FA_ERR_INVALID_VALUE for
+ * negative sizes or num_splits outside 1 ... 64. Host only (bm's dims are
+ * read, not its arrays); nothing is launched. */
+fa_status fa_bwd_workspace_bytes(int32_t B, int32_t H, int32_t H_kv,
+                                 int32_t q_len, int32_t kv_len, int32_t D,
+                                 const fa_block_mask* bm, int32_t num_splits,
+                                 uint64_t* bytes);
 
 /* Decode step over a paged key/value cache (bf16). PagedAttention keeps the
  * key/value cache as pages, like virtual memory (frontiernews, "What

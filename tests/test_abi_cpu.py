@@ -353,32 +353,44 @@ def test_auto_num_splits():
     assert api.auto_num_splits(torch.bfloat16, 0, 1, 4, 256) == 1
 
 
-def _bwd_ws_bytes(B, H, q_len, nq, nk, Bm=1, Hm=1, full=True):
+def _bwd_ws_bytes(B, H, q_len, nq, nk, Bm=1, Hm=1, full=True, H_kv=None,
+                  kv_len=0, D=128, splits=1):
     # the documented layout: delta and the row exponent offsets, tile
     # states, then per key block a count and NQB indices (twice with full
-    # lists), each part rounded to 256
+    # lists), then with splits the parts' fp32 dQ, dK, dV; each piece
+    # rounded to 256
     r = lambda x: -(-x // 256) * 256  # noqa: E731
     n = 2 * r(B * H * q_len * 4) + r(Bm * Hm * nq * nk)
     n += r(Bm * Hm * nk * 4) + r(Bm * Hm * nk * nq * 4)
     if full:
         n += r(Bm * Hm * nk * 4) + r(Bm * Hm * nk * nq * 4)
+    if splits > 1:
+        n += r(splits * B * H * q_len * D * 4)
+        n += 2 * r(splits * B * H_kv * kv_len * D * 4)
     return n
 
 
 @needs_lib
 def test_bwd_workspace_bytes():
     bm = _good_bm(q_len=300, kv_len=200, block=128)       # 3 x 2 blocks
-    assert api.fa_bwd_workspace_bytes(2, 4, 300, bm) == _bwd_ws_bytes(2, 4, 300, 3, 2)
+    ws = lambda *a, **k: api.fa_bwd_workspace_bytes(*a, **k)  # noqa: E731
+    assert ws(2, 4, 2, 300, 200, 128, bm) == _bwd_ws_bytes(2, 4, 300, 3, 2)
+    assert ws(2, 4, 2, 300, 200, 64, bm, 3) == _bwd_ws_bytes(
+        2, 4, 300, 3, 2, H_kv=2, kv_len=200, D=64, splits=3)
     bm.separate_full_blocks = 0
-    assert api.fa_bwd_workspace_bytes(2, 4, 300, bm) == \
+    assert ws(2, 4, 2, 300, 200, 128, bm) == \
         _bwd_ws_bytes(2, 4, 300, 3, 2, full=False)
     bm = _good_bm(q_len=8192, kv_len=8192, block=128, B=4, H=16)
-    assert api.fa_bwd_workspace_bytes(4, 16, 8192, bm) == \
+    assert ws(4, 16, 16, 8192, 8192, 128, bm) == \
         _bwd_ws_bytes(4, 16, 8192, 64, 64, Bm=4, Hm=16)
-    with pytest.raises(C.FlexAttnError) as e:
-        api.fa_bwd_workspace_bytes(-1, 4, 300, bm)
-    assert e.value.status == C.FA_ERR_INVALID_VALUE
-    assert C.lib().fa_bwd_workspace_bytes(1, 1, 64, None, None) == \
+    assert ws(4, 16, 16, 8192, 8192, 128, bm, 64) == _bwd_ws_bytes(
+        4, 16, 8192, 64, 64, Bm=4, Hm=16, H_kv=16, kv_len=8192, splits=64)
+    for bad in ((-1, 4, 4, 300, 200, 128, bm), (1, 4, 4, 300, -2, 128, bm),
+                (1, 4, 4, 300, 200, 128, bm, 0), (1, 4, 4, 300, 200, 128, bm, 65)):
+        with pytest.raises(C.FlexAttnError) as e:
+            ws(*bad)
+        assert e.value.status == C.FA_ERR_INVALID_VALUE
+    assert C.lib().fa_bwd_workspace_bytes(1, 1, 1, 64, 64, 64, None, 1, None) == \
         C.FA_ERR_NULL_POINTER
 
 
@@ -389,7 +401,8 @@ def _bwd(**over):
              k_stride=(2 * 256 * 128, 256 * 128, 128), v=FAKE,
              v_stride=(2 * 256 * 128, 256 * 128, 128), scale=0.088,
              bm=bm, score=C.fa_score_mod(kind=C.FA_SCORE_NONE),
-             dq_kv_order=1, o=FAKE, lse=FAKE, dout=FAKE, workspace=FAKE,
+             dq_kv_order=1, num_splits=1, o=FAKE, lse=FAKE, dout=FAKE,
+             workspace=FAKE,
              workspace_bytes=_bwd_ws_bytes(2, 4, 256, 2, 2), dq=FAKE, dk=FAKE,
              dv=FAKE, stream=None)
     a.update(over)
@@ -405,6 +418,13 @@ def _bwd(**over):
                        C.fa_block_mask._fields_}, "block_n": 32,
                     "num_kv_blocks": 8})), C.FA_ERR_UNSUPPORTED),
     (dict(workspace_bytes=_bwd_ws_bytes(2, 4, 256, 2, 2) - 1),
+     C.FA_ERR_INVALID_VALUE),
+    (dict(num_splits=0), C.FA_ERR_INVALID_VALUE),
+    (dict(num_splits=65), C.FA_ERR_INVALID_VALUE),
+    # split mode needs room for the parts' sums
+    (dict(num_splits=2), C.FA_ERR_INVALID_VALUE),
+    (dict(num_splits=2, workspace_bytes=_bwd_ws_bytes(
+        2, 4, 256, 2, 2, H_kv=2, kv_len=256, splits=2) - 1),
      C.FA_ERR_INVALID_VALUE),
     (dict(workspace=None), C.FA_ERR_NULL_POINTER),
     (dict(workspace=FAKE + 16), C.FA_ERR_UNSUPPORTED),
@@ -511,6 +531,20 @@ def test_decode_refuses(over, status):
 def test_decode_empty_problem_is_a_noop():
     assert _decode(B=0, q=None, o=None, seq_lens=None, page_table=None,
                    k_pages=None, v_pages=None) == C.FA_OK
+
+
+def test_auto_bwd_splits():
+    # about two dK / dV workgroups per compute unit once one row per unit
+    # is short, at most 16 parts and at most one per key block
+    assert api.auto_bwd_splits(1, 1, 64, 256) == 8
+    assert api.auto_bwd_splits(1, 1, 8, 256) == 8
+    assert api.auto_bwd_splits(1, 1, 2, 256) == 2
+    assert api.auto_bwd_splits(1, 4, 16, 256) == 8
+    assert api.auto_bwd_splits(1, 1, 128, 256) == 4
+    assert api.auto_bwd_splits(1, 1, 255, 256) == 3
+    assert api.auto_bwd_splits(1, 1, 256, 256) == 1
+    assert api.auto_bwd_splits(4, 16, 64, 256) == 1
+    assert api.auto_bwd_splits(0, 16, 64, 256) == 1
 
 
 def test_auto_decode_splits():

@@ -39,7 +39,8 @@ def _doc_t(doc):
     return torch.from_numpy(np.ascontiguousarray(doc)).to(DEV) if doc is not None else None
 
 
-def gpu_fwd_bwd(w, q, k, v, do, doc=None, sep=True, bm=None, order=None):
+def gpu_fwd_bwd(w, q, k, v, do, doc=None, sep=True, bm=None, order=None,
+                splits=1):
     if bm is None:
         bm = fa.create_block_mask(w.mask, None, None, w.q_len, w.kv_len,
                                   device=DEV, BLOCK_SIZE=w.block_m,
@@ -51,7 +52,7 @@ def gpu_fwd_bwd(w, q, k, v, do, doc=None, sep=True, bm=None, order=None):
                                num_splits=1)
     dq, dk, dv = fa.flex_attention_backward(qd, kd, vd, o, lse, dod, bm,
                                             score_mod=sm, scale=w.scale,
-                                            dq_kv_order=order)
+                                            dq_kv_order=order, num_splits=splits)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -93,7 +94,9 @@ for D, blk in ((128, 128), (64, 128), (128, 64), (64, 64)):
 def test_small_backward(D, blk, mask, score):
     # several tiles and ragged tails on both axes, q_len != kv_len, grouped
     # heads (dK / dV sum over two query heads), both list layouts (with the
-    # descending and the ascending dQ order)
+    # descending and the ascending dQ order), unsplit and split into parts
+    # (the automatic count: here one part per key block, so some parts of
+    # short rows are empty)
     ql, kl = 3 * blk + 37, 2 * blk + 101
     w = WL.Workload("small", "bf16", 2, 4, 2, ql, kl, D, mask, blk, blk,
                     seed=0, window=blk + 13 if "window" in mask else None,
@@ -103,11 +106,13 @@ def test_small_backward(D, blk, mask, score):
            if mask == "document" else None)
     q, k, v, do = _inputs(w, 23)
     ref = oracle_bwd(w, q, k, v, do, doc)
-    for sep in (True, False):
-        print(f"[bwd small] D={D} blk={blk} {mask} {score} sep={sep}", flush=True)
-        got = gpu_fwd_bwd(w, q, k, v, do, doc, sep=sep, order=sep)
+    for sep, ns in ((True, 1), (False, 1), (False, None)):
+        print(f"[bwd small] D={D} blk={blk} {mask} {score} sep={sep} splits={ns}",
+              flush=True)
+        got = gpu_fwd_bwd(w, q, k, v, do, doc, sep=sep, order=sep, splits=ns)
         for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-            assert_grad_close(g, r, f"{name} D={D} blk={blk} {mask} {score} sep={sep}")
+            assert_grad_close(g, r, f"{name} D={D} blk={blk} {mask} {score} sep={sep} "
+                                    f"splits={ns}")
 
 
 @pytest.mark.parametrize("D,blk", [(128, 128), (64, 64)])
@@ -143,12 +148,13 @@ def test_backward_rows_without_keys():
     w = WL.Workload("empty", "bf16", 1, 2, 1, 400, 150, 64, "sliding_window",
                     64, 64, seed=0, window=60)
     q, k, v, do = _inputs(w, 6)
-    print("[bwd rows without keys]", flush=True)
-    got = gpu_fwd_bwd(w, q, k, v, do)
     ref = oracle_bwd(w, q, k, v, do)
-    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-        assert_grad_close(g, r, f"{name} rows without keys")
-    assert (got[0][:, :, 209:] == 0).all()
+    for ns in (1, 4):
+        print(f"[bwd rows without keys] splits={ns}", flush=True)
+        got = gpu_fwd_bwd(w, q, k, v, do, splits=ns)
+        for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+            assert_grad_close(g, r, f"{name} rows without keys splits={ns}")
+        assert (got[0][:, :, 209:] == 0).all()
 
 
 def test_backward_zero_lengths():
@@ -173,13 +179,13 @@ def test_backward_zero_lengths():
     lse0 = torch.zeros(1, 2, 0, device=DEV)
     dk = torch.full((1, 1, 200, 128), float("nan"), device=DEV, dtype=torch.bfloat16)
     dv = dk.clone()
-    nbytes = fa.fa_bwd_workspace_bytes(1, 2, 0, bm.to_c())
+    nbytes = fa.fa_bwd_workspace_bytes(1, 2, 1, 0, 200, 128, bm.to_c())
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
     print("[bwd zero-length queries]", flush=True)
     st = fa.fa_flex_attention_bwd(
         0, 1, 2, 1, 0, 200, 128, q0.data_ptr(), q0.stride()[:3], k.data_ptr(),
         k.stride()[:3], k.data_ptr(), k.stride()[:3], 128 ** -0.5, bm.to_c(),
-        None, 1, q0.data_ptr(), lse0.data_ptr(), q0.data_ptr(), ws.data_ptr(),
+        None, 1, 1, q0.data_ptr(), lse0.data_ptr(), q0.data_ptr(), ws.data_ptr(),
         nbytes, q0.data_ptr(), dk.data_ptr(), dv.data_ptr(), None)
     torch.cuda.synchronize()
     assert st == 0
@@ -277,10 +283,42 @@ def test_backward_block_size_pairs(D, bq, bk, mask, score):
     ref = oracle_bwd(w, q, k, v, do, doc)
     bm = fa.create_block_mask(mask, None, None, ql, kl, device=DEV,
                               BLOCK_SIZE=(bq, bk), window=w.window, doc_id=_doc_t(doc))
-    print(f"[bwd block pair] D={D} ({bq},{bk}) {mask} {score}", flush=True)
-    got = gpu_fwd_bwd(w, q, k, v, do, doc, bm=bm)
-    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-        assert_grad_close(g, r, f"{name} pair ({bq},{bk}) D={D} {mask} {score}")
+    for ns in (1, 2):
+        print(f"[bwd block pair] D={D} ({bq},{bk}) {mask} {score} splits={ns}",
+              flush=True)
+        got = gpu_fwd_bwd(w, q, k, v, do, doc, bm=bm, splits=ns)
+        for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+            assert_grad_close(g, r, f"{name} pair ({bq},{bk}) D={D} {mask} {score} "
+                                    f"splits={ns}")
+
+
+@pytest.mark.parametrize("mask,blk", [("causal", 64), ("document", 128),
+                                      ("sliding_window", 64)])
+def test_backward_split_parts(mask, blk):
+    # num_splits from 2 up to 64 (more parts than any row has blocks: the
+    # surplus parts are empty and write zero sums), grouped heads (the parts
+    # of a dK / dV row cut across its query heads), both dQ orders: within
+    # the bar of the oracle and of the unsplit result, each bit-reproducible
+    T = 9 * blk + 23
+    w = WL.Workload("parts", "bf16", 1, 6, 2, T, T, 128, mask, blk, blk, seed=0,
+                    window=2 * blk + 5 if "window" in mask else None,
+                    score="alibi")
+    doc = WL.doc_ids([T // 3, T // 2, T - T // 3 - T // 2]) if mask == "document" else None
+    q, k, v, do = _inputs(w, 61)
+    ref = oracle_bwd(w, q, k, v, do, doc)
+    base = gpu_fwd_bwd(w, q, k, v, do, doc, splits=1)
+    scale = [max(1.0, float(np.abs(x).max())) for x in ref]
+    for ns in (2, 5, 16, 64):
+        for order in (True, False):
+            print(f"[bwd split parts] {mask} blk={blk} splits={ns} descending={order}",
+                  flush=True)
+            a = gpu_fwd_bwd(w, q, k, v, do, doc, splits=ns, order=order)
+            b = gpu_fwd_bwd(w, q, k, v, do, doc, splits=ns, order=order)
+            for x, y in zip(a, b):
+                assert torch.equal(x, y)
+            for name, g, r, g0, sc in zip(("dQ", "dK", "dV"), a, ref, base, scale):
+                assert_grad_close(g, r, f"{name} {mask} splits={ns}")
+                assert (g.float() - g0.float()).abs().max().item() <= TOL_BWD * sc
 
 
 def test_backward_errors():
@@ -326,8 +364,9 @@ def test_workload_backward(name, workload_inputs):
     #   since every row of dS sums to 0
     w, q, k, v, do, doc = workload_inputs(name)
     assert w.q_len == w.kv_len
-    print(f"[bwd workload] {name}", flush=True)
-    dq, dk, dv = gpu_fwd_bwd(w, q, k, v, do, doc)
+    ns = None if name == "c2" else 1     # c2: the automatic split count
+    print(f"[bwd workload] {name} splits={ns}", flush=True)
+    dq, dk, dv = gpu_fwd_bwd(w, q, k, v, do, doc, splits=ns)
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and \
         torch.isfinite(dv).all()
     L = w.q_len
