@@ -56,6 +56,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kStageKeys = 64;
+constexpr int kSReadAhead = 6;  // K operand reads in flight ahead of the S product
 
 template <int D>
 __device__ __forceinline__ int kv_swizzle(int r) {
@@ -292,19 +293,34 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
     const bool masked = masked_at(it, n);
     const int j0 = n * BK + (SPB - 1 - st % SPB) * kStageKeys;
 
-    // ---- S^T = K Q^T for the stage's 64 keys
+    // ---- S^T = K Q^T for the stage's 64 keys, at normal priority (see the
+    // PV product below)
+    __builtin_amdgcn_s_setprio(0);
     f32x16 s[2];
     s[0] = f32x16{};
     s[1] = f32x16{};
+    u32x4 ka[DK][2];
 #pragma unroll
-    for (int dk = 0; dk < DK; ++dk) {
+    for (int dk = 0; dk < DK; ++dk)
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(sK + k_rd[dk] + jt * 32 * RB);
-        s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[dk],
-                                                        s[jt], 0, 0, 0);
-      }
+      for (int jt = 0; jt < 2; ++jt)
+        ka[dk][jt] = *reinterpret_cast<const u32x4*>(sK + k_rd[dk] + jt * 32 * RB);
+#pragma unroll
+    for (int dk = 0; dk < DK; ++dk)
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+        s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[dk][jt]),
+                                                        qf[dk], s[jt], 0, 0, 0);
+    // K operand reads kept kSReadAhead ahead of the products that use them
+    // (left to itself the scheduler issues each read just before its
+    // product and waits on it)
+    __builtin_amdgcn_sched_group_barrier(0x100, kSReadAhead, 0);  // LDS reads
+#pragma unroll
+    for (int t = 0; t < 2 * DK - kSReadAhead; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, kSReadAhead, 0);
 
     // ---- score_mod into the log2 domain (NONE keeps raw q.k: c > 0 is
     // applied in the exponent). Key of (jt, r): j0 + 4g + 32jt + 8(r/4) + r%4.
@@ -410,7 +426,11 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
       }
     }
 
-    // ---- O^T += V^T P^T (4 k-steps of 16 keys)
+    // ---- O^T += V^T P^T (4 k-steps of 16 keys). The wave raises its issue
+    // priority from here until its next stage's S product: of the two waves
+    // sharing a SIMD, the one whose P is ready gets its products issued ahead
+    // of the other's softmax arithmetic, which keeps the matrix core fed.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
