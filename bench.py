@@ -179,7 +179,7 @@ def main(argv=None) -> int:
     a = ap.parse_args(argv)
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        log("bench.py measures one GPU: this build has no multi-GPU path "
+        log("bench.py measures one GPU: the library has no multi-GPU path "
             "(run with --gpus 1).")
         return 2
 
