@@ -129,17 +129,19 @@ def test_backward_per_batch_documents_and_per_head_masks(D, blk):
     ref = oracle_bwd(w, q, k, v, do, doc)
     bm = fa.create_block_mask("document", B, None, T, T, device=DEV,
                               BLOCK_SIZE=blk, doc_id=_doc_t(doc))
-    print(f"[bwd per-batch docs] D={D} blk={blk}", flush=True)
-    got = gpu_fwd_bwd(w, q, k, v, do, doc, bm=bm)
-    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-        assert_grad_close(g, r, f"{name} per-batch docs D={D}")
+    for ns in (1, 3):
+        print(f"[bwd per-batch docs] D={D} blk={blk} splits={ns}", flush=True)
+        got = gpu_fwd_bwd(w, q, k, v, do, doc, bm=bm, splits=ns)
+        for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+            assert_grad_close(g, r, f"{name} per-batch docs D={D} splits={ns}")
     w2 = w.replace(mask="causal")
     ref2 = oracle_bwd(w2, q, k, v, do)
     bm2 = fa.create_block_mask("causal", B, H, T, T, device=DEV, BLOCK_SIZE=blk)
-    print(f"[bwd per-head lists] D={D} blk={blk}", flush=True)
-    got2 = gpu_fwd_bwd(w2, q, k, v, do, bm=bm2)
-    for name, g, r in zip(("dQ", "dK", "dV"), got2, ref2):
-        assert_grad_close(g, r, f"{name} per-head lists D={D}")
+    for ns in (1, 3):
+        print(f"[bwd per-head lists] D={D} blk={blk} splits={ns}", flush=True)
+        got2 = gpu_fwd_bwd(w2, q, k, v, do, bm=bm2, splits=ns)
+        for name, g, r in zip(("dQ", "dK", "dV"), got2, ref2):
+            assert_grad_close(g, r, f"{name} per-head lists D={D} splits={ns}")
 
 
 def test_backward_rows_without_keys():
@@ -212,12 +214,13 @@ def test_backward_strided_views_and_nan_tails():
     bm = fa.create_block_mask("local_window", None, None, ql, kl, device=DEV,
                               BLOCK_SIZE=64, window=50)
     o, lse = fa.flex_attention(qv, kv_, vv, bm, score_mod="alibi", num_splits=1)
-    print("[bwd strided views, NaN tails]", flush=True)
-    got = fa.flex_attention_backward(qv, kv_, vv, o, lse, do.to(DEV), bm,
-                                     score_mod="alibi")
-    torch.cuda.synchronize()
-    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
-        assert_grad_close(g, r, f"{name} strided views")
+    for ns in (1, 2):
+        print(f"[bwd strided views, NaN tails] splits={ns}", flush=True)
+        got = fa.flex_attention_backward(qv, kv_, vv, o, lse, do.to(DEV), bm,
+                                         score_mod="alibi", num_splits=ns)
+        torch.cuda.synchronize()
+        for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+            assert_grad_close(g, r, f"{name} strided views splits={ns}")
 
 
 def test_backward_deterministic():
