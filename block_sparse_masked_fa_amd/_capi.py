@@ -40,7 +40,10 @@ FA_SCORE_ALIBI = 2
 # largest num_splits of fa_flex_attention_fwd_split
 FA_MAX_SPLITS = 64
 
-ABI_VERSION = 8
+# bytes of the forward's scheduler workspace
+FA_FWD_WORKSPACE_BYTES = 256
+
+ABI_VERSION = 9
 
 
 class fa_mask_mod(ctypes.Structure):
@@ -92,8 +95,8 @@ SIGNATURES = {
         ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
         ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
         ctypes.c_float, ctypes.POINTER(fa_block_mask),
-        ctypes.POINTER(fa_score_mod), ctypes.c_void_p, ctypes.c_void_p,
-        ctypes.c_void_p]),
+        ctypes.POINTER(fa_score_mod), ctypes.c_void_p, ctypes.c_uint64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "fa_flex_attention_fwd_split": (ctypes.c_int, [
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,

@@ -25,6 +25,7 @@ import dataclasses
 import math
 from typing import Optional, Tuple, Union
 
+import numpy as np
 import torch
 
 from . import _capi as C
@@ -39,7 +40,7 @@ __all__ = [
     "flex_attention_backward", "fa_flex_attention_bwd",
     "fa_bwd_workspace_bytes", "auto_bwd_splits", "flex_attention_decode_paged",
     "fa_flex_attention_decode_paged", "auto_decode_splits",
-    "masked_softmax", "fa_masked_softmax",
+    "masked_softmax", "fa_masked_softmax", "fwd_workspace",
 ]
 
 FlexAttnError = C.FlexAttnError
@@ -166,12 +167,14 @@ def fa_flex_attention_fwd(dtype: int, B: int, H: int, H_kv: int, q_len: int,
                           k_stride, v: int, v_stride, scale: float,
                           bm: C.fa_block_mask, score: Optional[C.fa_score_mod],
                           o: int, lse: Optional[int],
-                          stream: Optional[int]) -> int:
+                          stream: Optional[int], workspace: Optional[int] = None,
+                          workspace_bytes: int = 0) -> int:
     return C.lib().fa_flex_attention_fwd(
         dtype, B, H, H_kv, q_len, kv_len, D,
         q, C.Stride3(*q_stride), k, C.Stride3(*k_stride),
         v, C.Stride3(*v_stride), scale, ctypes.byref(bm),
-        ctypes.byref(score) if score is not None else None, o, lse, stream)
+        ctypes.byref(score) if score is not None else None, workspace,
+        workspace_bytes, o, lse, stream)
 
 
 def fa_flex_attention_fwd_split(dtype: int, B: int, H: int, H_kv: int,
@@ -293,6 +296,36 @@ def auto_num_splits(dtype: torch.dtype, B: int, H: int, num_q_blocks: int,
 
 
 # ------------------------------------------------------------- BlockMask
+def _check_lists(num, idx, fnum, fidx, nkvb):
+    """Host check of caller-supplied lists: in every row the listed
+    in-range entries are distinct, and no block is in both lists."""
+    def listed(n, i):
+        n = n.cpu().numpy().clip(0, nkvb)
+        i = i.cpu().numpy()
+        keep = np.arange(nkvb)[None, None, None, :] < n[..., None]
+        keep &= (i >= 0) & (i < nkvb)
+        return i, keep
+
+    def seen(i, keep):
+        # per row, how often each block number is listed
+        rows = i.reshape(-1, nkvb)
+        k = keep.reshape(-1, nkvb)
+        cnt = np.zeros((rows.shape[0], nkvb), dtype=np.int64)
+        r, c = np.nonzero(k)
+        np.add.at(cnt, (r, rows[r, c]), 1)
+        return cnt
+
+    cnt = seen(*listed(num, idx))
+    if (cnt > 1).any():
+        raise ValueError("a row of kv_indices lists a block twice")
+    if fnum is not None:
+        fcnt = seen(*listed(fnum, fidx))
+        if (fcnt > 1).any():
+            raise ValueError("a row of full_kv_indices lists a block twice")
+        if ((cnt > 0) & (fcnt > 0)).any():
+            raise ValueError("a block is listed both as partial and as full")
+
+
 class BlockMask:
     """Block mask: index tensors (int32, on the device) plus the mask_mod
     they were built from. Built once, reused by any number of
@@ -342,25 +375,59 @@ class BlockMask:
                        full_kv_indices: Optional[torch.Tensor] = None, *,
                        mask_mod=None, q_len: int, kv_len: int,
                        BLOCK_SIZE: Union[int, Tuple[int, int]] = 128,
-                       window=None, doc_id=None) -> "BlockMask":
+                       window=None, doc_id=None,
+                       check_lists: bool = True) -> "BlockMask":
         """Wrap caller-provided index tensors (tensorplay
         create_block_mask page: precomputed metadata is supplied through
         BlockMask.from_kv_blocks). The mask_mod is still applied to the
-        listed partial blocks."""
+        listed partial blocks; full blocks are taken as wholly allowed.
+
+        Shapes: ``kv_num_blocks [B, H, NQB]`` and ``kv_indices [B, H, NQB,
+        NKVB]`` with NQB = ceil(q_len / block_m), NKVB = ceil(kv_len /
+        block_n) (B, H = 1 broadcast), the full pair the same, int32,
+        contiguous, on one device. Counts outside [0, NKVB] are clamped and
+        listed entries outside [0, NKVB) are skipped by the kernels. The
+        listed entries of a row must be distinct and the partial and full
+        lists disjoint (the forward would visit a repeated block twice);
+        ``check_lists`` verifies that on the host (one device-to-host copy)."""
         bm_, bn_ = ((BLOCK_SIZE, BLOCK_SIZE) if isinstance(BLOCK_SIZE, int)
                     else BLOCK_SIZE)
-        for t in (kv_num_blocks, kv_indices, full_kv_num_blocks,
-                  full_kv_indices):
-            if t is not None and (t.dtype != torch.int32 or not t.is_cuda
-                                  or not t.is_contiguous()):
-                raise ValueError("index tensors must be contiguous int32 "
-                                 "device tensors")
         if (full_kv_num_blocks is None) != (full_kv_indices is None):
             raise ValueError("give both full block tensors or neither")
+        tensors = [t for t in (kv_num_blocks, kv_indices, full_kv_num_blocks,
+                               full_kv_indices) if t is not None]
+        for t in tensors:
+            if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+                raise ValueError("index tensors must be contiguous int32 "
+                                 "device tensors")
+            if t.device != kv_num_blocks.device:
+                raise ValueError("index tensors must be on one device")
+        nqb, nkvb = fa_block_mask_dims(q_len, kv_len, bm_, bn_)
+        if kv_num_blocks.dim() != 3 or kv_num_blocks.shape[2] != nqb:
+            raise ValueError(f"kv_num_blocks must be [B, H, {nqb}] "
+                             f"(NQB = ceil(q_len / block_m))")
+        want = (*kv_num_blocks.shape, nkvb)
+        if tuple(kv_indices.shape) != want:
+            raise ValueError(f"kv_indices must be {list(want)} "
+                             f"(NKVB = ceil(kv_len / block_n))")
+        if full_kv_num_blocks is not None:
+            if full_kv_num_blocks.shape != kv_num_blocks.shape or \
+                    tuple(full_kv_indices.shape) != want:
+                raise ValueError("the full block tensors must have the "
+                                 "shapes of the partial ones")
         B, H = kv_num_blocks.shape[0], kv_num_blocks.shape[1]
-        return cls(_mask_from(mask_mod, window, doc_id), B, H, q_len, kv_len,
-                   bm_, bn_, kv_num_blocks, kv_indices, full_kv_num_blocks,
-                   full_kv_indices)
+        mask = _mask_from(mask_mod, window, doc_id)
+        if mask.kind == C.FA_MASK_DOCUMENT and mask.per_batch and \
+                mask.doc_id.shape[0] != B:
+            raise ValueError("per-batch doc_id [B, L] needs B = the index "
+                             "tensors' first dimension")
+        if mask.doc_id is not None and mask.doc_id.device != kv_num_blocks.device:
+            raise ValueError("doc_id must live on the index tensors' device")
+        if check_lists:
+            _check_lists(kv_num_blocks, kv_indices, full_kv_num_blocks,
+                         full_kv_indices, nkvb)
+        return cls(mask, B, H, q_len, kv_len, bm_, bn_, kv_num_blocks,
+                   kv_indices, full_kv_num_blocks, full_kv_indices)
 
     def __repr__(self):
         return (f"BlockMask(B={self.B}, H={self.H}, q_len={self.q_len}, "
@@ -426,13 +493,40 @@ def create_block_mask(mask_mod, B: Optional[int], H: Optional[int],
 
 _DTYPES = {torch.bfloat16: C.FA_BF16, torch.float32: C.FA_FP32}
 
+# One zeroed scheduler workspace per (device, stream): calls on one stream
+# run in order and each leaves the counters zero again; calls on different
+# streams must not share one.
+_SCHED_WS = {}
+
+
+def fwd_workspace(device: torch.device) -> torch.Tensor:
+    """The forward's scheduler workspace for the current stream of
+    ``device`` (allocated zeroed on first use)."""
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _SCHED_WS.get(key)
+    if ws is None:
+        ws = torch.zeros(C.FA_FWD_WORKSPACE_BYTES, dtype=torch.uint8,
+                         device=device)
+        _SCHED_WS[key] = ws
+    return ws
+
+
+def _check_doc_rows(block_mask: BlockMask, B: int) -> None:
+    """A per-batch doc_id is read at row b for every batch entry b < B (the
+    C ABI has no row count to check it against)."""
+    m = block_mask.mask
+    if m.kind == C.FA_MASK_DOCUMENT and m.per_batch and m.doc_id.shape[0] != B:
+        raise ValueError(f"per-batch doc_id has {m.doc_id.shape[0]} rows "
+                         f"for a batch of {B}")
+
 
 def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    block_mask: BlockMask, score_mod=None,
                    scale: Optional[float] = None, return_lse: bool = True,
                    out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None,
-                   num_splits: Optional[int] = None):
+                   num_splits: Optional[int] = None,
+                   persistent: bool = False):
     """Fused block-sparse attention forward.
 
     q: (B, H, Q_LEN, D); k, v: (B, H_kv, KV_LEN, D), bf16 or fp32, on the
@@ -444,7 +538,10 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     ``num_splits``: split-KV parts per query block (bf16 only). None picks
     :func:`auto_num_splits` for the device; 1 is one fa_flex_attention_fwd
     call, more is fa_flex_attention_fwd_split with a workspace allocated
-    here."""
+    here. ``persistent`` (num_splits 1): pass the stream's scheduler
+    workspace, so resident workgroups take query blocks from counters
+    (measured no faster on MI355X, whose clock drops as idle gaps close);
+    False (default) launches one workgroup per query block."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D (B, H, S, D)")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _DTYPES:
@@ -460,28 +557,40 @@ def flex_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     for t in (q, k, v):
         if t.numel() and t.stride(-1) != 1:
             raise ValueError("the head dimension must be contiguous")
+    _check_doc_rows(block_mask, B)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     score = _score_from(score_mod)
     if out is None:
         out = torch.empty((B, H, q_len, D), dtype=q.dtype, device=q.device)
-    if return_lse and lse is None:
-        lse = torch.empty((B, H, q_len), dtype=torch.float32, device=q.device)
+    elif (out.shape != (B, H, q_len, D) or out.dtype != q.dtype
+          or out.device != q.device or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous (B, H, Q_LEN, D) tensor "
+                         "of q's dtype on q's device")
     if not return_lse:
         lse = None
+    elif lse is None:
+        lse = torch.empty((B, H, q_len), dtype=torch.float32, device=q.device)
+    elif (lse.shape != (B, H, q_len) or lse.dtype != torch.float32
+          or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 (B, H, Q_LEN) tensor "
+                         "on q's device")
     if num_splits is None:
         num_splits = auto_num_splits(
             q.dtype, B, H, block_mask.num_q_blocks,
             torch.cuda.get_device_properties(q.device).multi_processor_count)
     with torch.cuda.device(q.device):
         if num_splits == 1:
+            ws = fwd_workspace(q.device) if persistent else None
             st = fa_flex_attention_fwd(
                 _DTYPES[q.dtype], B, H, H_kv, q_len, kv_len, D,
                 q.data_ptr(), q.stride()[:3], k.data_ptr(), k.stride()[:3],
                 v.data_ptr(), v.stride()[:3], float(scale),
                 block_mask.to_c(), score.to_c(), out.data_ptr(),
                 lse.data_ptr() if lse is not None else None,
-                _stream_handle(q.device))
+                _stream_handle(q.device),
+                ws.data_ptr() if ws is not None else None,
+                ws.numel() if ws is not None else 0)
             C.check(st, "fa_flex_attention_fwd")
             return out, lse
         nbytes = fa_split_workspace_bytes(B, H, q_len, D, num_splits)
@@ -532,6 +641,7 @@ def flex_attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     for t in (q, k, v):
         if t.numel() and t.stride(-1) != 1:
             raise ValueError("the head dimension must be contiguous")
+    _check_doc_rows(block_mask, B)
     o = o.contiguous()
     dout = dout.contiguous()
     lse = lse.contiguous()

@@ -75,7 +75,8 @@ fa_status fa_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H,
                                 const int64_t k_stride[3], const void* v,
                                 const int64_t v_stride[3], float scale,
                                 const fa_block_mask* bm,
-                                const fa_score_mod* score, void* o, float* lse,
+                                const fa_score_mod* score, void* workspace,
+                                uint64_t workspace_bytes, void* o, float* lse,
                                 void* stream) {
   std::string msg;
   fa::FwdLaunch p{};
@@ -84,6 +85,8 @@ fa_status fa_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H,
                                         q_stride, k, k_stride, v, v_stride,
                                         scale, bm, score, o, lse, &p, &nothing,
                                         &msg);
+  if (st != FA_OK) return finish(st, msg);
+  st = fa::check_fwd_workspace(dtype, workspace, workspace_bytes, &p, &msg);
   if (st != FA_OK) return finish(st, msg);
   if (nothing) return FA_OK;
   int err;

@@ -89,17 +89,28 @@ __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)p);
 }
 
-// Workgroup -> (head, query block, split part). Workgroups are dispatched
-// round-robin over the 8 XCDs (wg % 8). Logical items are dealt to XCDs in
-// contiguous ranges so that the query blocks of one head run on one XCD and
-// share its L2; within a head the heaviest query blocks (last rows under
-// causal masks) come first.
-__device__ __forceinline__ bool xcd_work_item(const FwdLaunch& p, WorkItem& w) {
+// The kernel's FwdLaunch argument read straight from the kernel argument
+// segment (it is the only argument, at offset 0) through a pointer the
+// compiler cannot see through: every use is a fresh scalar load (a scalar
+// cache hit) instead of a value held in scalar registers for the whole
+// kernel. Used for the fields a persistent workgroup needs only at item
+// boundaries.
+typedef const __attribute__((address_space(4))) FwdLaunch KArgs;
+__device__ __forceinline__ KArgs& kargs() {
+  KArgs* q = (KArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(q));
+  return *q;
+}
+
+// Logical item -> (head, query block, split part). Logical items are dealt
+// to the 8 XCDs in contiguous ranges (workgroups are dispatched round-robin,
+// wg % 8, so the range of XCD x is served by workgroups x, x + 8, ...): the
+// query blocks of one head run on one XCD and share its L2. Within a head the
+// heaviest query blocks (last rows under causal masks) come first.
+template <class Params>
+__device__ __forceinline__ bool logical_item(const Params& p, int logical, WorkItem& w) {
   const int total = p.B * p.H * p.nqb * p.nsplit;
-  const int per_xcd = (total + 7) >> 3;
-  const int wg = blockIdx.x;
-  const int logical = (wg & 7) * per_xcd + (wg >> 3);
-  if (logical >= total) return false;
+  if (logical < 0 || logical >= total) return false;
   w.c = logical % p.nsplit;  // the parts of one query block run side by side
   const int row = logical / p.nsplit;
   w.m = p.nqb - 1 - (row % p.nqb);
@@ -109,7 +120,87 @@ __device__ __forceinline__ bool xcd_work_item(const FwdLaunch& p, WorkItem& w) {
   return true;
 }
 
-template <int D, int BQ, int BK, int SCORE>
+// One workgroup per item: workgroup wg serves slot wg / 8 of XCD wg % 8.
+__device__ __forceinline__ bool xcd_work_item(const FwdLaunch& p, WorkItem& w) {
+  const int total = p.B * p.H * p.nqb * p.nsplit;
+  const int per_xcd = (total + 7) >> 3;
+  const int wg = blockIdx.x;
+  return logical_item(p, (wg & 7) * per_xcd + (wg >> 3), w);
+}
+
+// Persistent schedule (p.sched != NULL): gridDim.x workgroups (a multiple of
+// 8, about two per compute unit) stay resident and take items one after
+// another. Slot j of XCD x first takes the j-th item of its XCD's range; after
+// that each XCD's range is handed out by its own counter, sched[x] (item
+// slots + the counter's old value), and a workgroup whose range is used up
+// takes items from the following XCDs' ranges. A workgroup that finds every
+// range used up adds one to sched[8]; the last one to do so puts all nine
+// counters back to zero, so the array is zero again for the next launch.
+// Returns the logical item, or -1 when no range has an item left.
+constexpr int kSchedCounters = 9;
+static_assert(kSchedCounters * 4 <= FA_FWD_WORKSPACE_BYTES, "scheduler counters fit the workspace");
+
+// Launch shape (host): a persistent grid of two workgroups per compute unit
+// when the launch has scheduler counters and more items than that; else one
+// workgroup per item (counters dropped), rounded up to whole XCD rounds.
+inline FwdLaunch fwd_schedule(const FwdLaunch& p, int items, unsigned* wgs) {
+  FwdLaunch q = p;
+  int dev = 0, cus = 0;
+  if (q.sched && hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus > 0) {
+    const int slots = (2 * cus + 7) / 8 * 8;
+    if (items > slots) {
+      *wgs = static_cast<unsigned>(slots);
+      return q;
+    }
+  }
+  q.sched = nullptr;
+  *wgs = static_cast<unsigned>((items + 7) / 8 * 8);
+  return q;
+}
+
+// The item a counter value `got` from XCD range xs names, or -2 when that
+// range is used up (no atomics: usable inside the stage loop).
+template <class Params>
+__device__ __forceinline__ int sched_check(const Params& p, unsigned got, int xs) {
+  const int total = p.B * p.H * p.nqb * p.nsplit;
+  const int per_xcd = (total + 7) >> 3;
+  const int slots = static_cast<int>(gridDim.x >> 3);
+  const int64_t k = static_cast<int64_t>(got) + slots;
+  const int64_t logical = static_cast<int64_t>(xs & 7) * per_xcd + k;
+  return k < per_xcd && logical < total ? static_cast<int>(logical) : -2;
+}
+
+template <class Params>
+__device__ __forceinline__ int sched_resolve(const Params& p, unsigned got, int& xs) {
+  const int total = p.B * p.H * p.nqb * p.nsplit;
+  const int per_xcd = (total + 7) >> 3;
+  const int slots = static_cast<int>(gridDim.x >> 3);
+  const int x0 = static_cast<int>(blockIdx.x & 7);
+  for (;;) {
+    const int x = xs & 7;
+    const int64_t k = static_cast<int64_t>(got) + slots;
+    const int64_t logical = static_cast<int64_t>(x) * per_xcd + k;
+    if (k < per_xcd && logical < total) return static_cast<int>(logical);
+    if (++xs >= x0 + 8) return -1;
+    got = __hip_atomic_fetch_add(p.sched + (xs & 7), 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ __forceinline__ void sched_finish(const FwdLaunch& p) {
+  const unsigned n = __hip_atomic_fetch_add(p.sched + 8, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  if (n == gridDim.x - 1) {
+    for (int c = 0; c < kSchedCounters; ++c)
+      __hip_atomic_store(p.sched + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// DOC: the document mask (per-key document ids staged in LDS and compared on
+// partial blocks); every other built-in mask is an interval test only.
+template <int D, int BQ, int BK, int SCORE, bool DOC>
 __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) {
   constexpr int NW = BQ / 32;             // wavefronts
   constexpr int NT = NW * 64;             // threads
@@ -122,87 +213,66 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
   constexpr int DK = D / 16;
   constexpr int DT = D / 32;
 
-  __shared__ __attribute__((aligned(1024))) char sK0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sV0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sK1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sV1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) int sDoc0[kStageKeys];
-  __shared__ __attribute__((aligned(16))) int sDoc1[kStageKeys];
+  // LDS: two stage buffers (K and V tiles), their document ids, and the
+  // persistent schedule's next item (-1 for none), in one array so that
+  // every address is one base plus a constant
+  constexpr int OFF_DOC = 4 * STAGE_BYTES;
+  constexpr int OFF_NEXT = OFF_DOC + 2 * kStageKeys * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[OFF_NEXT + 16];
+  char* const sK0 = smem;
+  char* const sV0 = smem + STAGE_BYTES;
+  char* const sK1 = smem + 2 * STAGE_BYTES;
+  char* const sV1 = smem + 3 * STAGE_BYTES;
+  int* const sDoc0 = reinterpret_cast<int*>(smem + OFF_DOC);
+  int* const sDoc1 = reinterpret_cast<int*>(smem + OFF_DOC + kStageKeys * 4);
+  int& sNext = *reinterpret_cast<int*>(smem + OFF_NEXT);
 
-  WorkItem w;
-  if (!xcd_work_item(p, w)) return;
-
+  const bool persistent = p.sched != nullptr;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lq = lane & 31;
   const int g = lane >> 5;
 
-  const int hk = w.h / (p.H / p.H_kv);
-  const int i = w.m * BQ + wave * 32 + lq;
-  const bool i_ok = i < p.q_len;
+  // ---- the first item
+  WorkItem w;
+  int xs = static_cast<int>(blockIdx.x & 7);  // XCD range being drained
+  bool have;
+  if (!persistent) {
+    have = xcd_work_item(p, w);
+  } else {
+    const int total = p.B * p.H * p.nqb * p.nsplit;
+    const int per_xcd = (total + 7) >> 3;
+    const int j = static_cast<int>(blockIdx.x >> 3);
+    int first = j < per_xcd ? xs * per_xcd + j : total;
+    if (first >= total) {
+      // this slot's static item is past its XCD's range: take one from the
+      // counters (the same for every wave: one lane asks, LDS broadcasts)
+      if (tid == 0) {
+        const unsigned got = __hip_atomic_fetch_add(p.sched + xs, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        sNext = sched_resolve(p, got, xs);
+      }
+      __syncthreads();
+      first = __builtin_amdgcn_readfirstlane(sNext);
+      __syncthreads();
+    }
+    have = logical_item(p, first, w);
+  }
+  if (!have) {
+    if (persistent && tid == 0) sched_finish(p);
+    return;
+  }
+
   const int kv_len = p.kv_len;
   const int mkind = p.mask.kind;
   const int window = p.mask.window;
-  // document ids of this batch entry (one shared array when the stride is 0)
-  const int* doc = p.mask.doc_id + static_cast<int64_t>(w.b) * p.mask.doc_stride;
-  const bool doc_mask = mkind == FA_MASK_DOCUMENT;
-
-  const __bf16* qp = static_cast<const __bf16*>(p.q) + w.b * p.qs[0] + w.h * p.qs[1];
-  const char* kbase = reinterpret_cast<const char*>(
-      static_cast<const __bf16*>(p.k) + w.b * p.ks[0] + hk * p.ks[1]);
-  const char* vbase = reinterpret_cast<const char*>(
-      static_cast<const __bf16*>(p.v) + w.b * p.vs[0] + hk * p.vs[1]);
+  constexpr bool doc_mask = DOC;
   const int64_t kstride = p.ks[2] * 2;  // bytes
   const int64_t vstride = p.vs[2] * 2;
-
-  // Q^T as the MFMA B operand: column = query lq, k slots d in [16dk + 8g, +8)
-  bf16x8 qf[DK];
-  {
-    const __bf16* row = qp + static_cast<int64_t>(i_ok ? i : 0) * p.qs[2];
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk) {
-      u32x4 x = i_ok ? *reinterpret_cast<const u32x4*>(row + dk * 16 + g * 8)
-                     : u32x4{0u, 0u, 0u, 0u};
-      qf[dk] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
-  const int di = doc_mask ? doc[i_ok ? i : 0] : 0;
-
-  // the row's block lists (broadcast over batch / head when Bm / Hm is 1)
-  const int bb = p.Bm == 1 ? 0 : w.b;
-  const int hh = p.Hm == 1 ? 0 : w.h;
-  const int64_t lrow = (static_cast<int64_t>(bb) * p.Hm + hh) * p.nqb + w.m;
   const int nkvb = p.nkvb;
-  const int nf = p.fnum ? min(max(p.fnum[lrow], 0), nkvb) : 0;
-  const int np = min(max(p.num[lrow], 0), nkvb);
-  // block lists through the constant address space: uniform scalar loads,
-  // tracked by lgkmcnt, so reading them never waits on in-flight tile DMA
-  const const_i32* fl = (const const_i32*)(p.fidx ? p.fidx + lrow * nkvb : p.idx);
-  const const_i32* pl = (const const_i32*)(p.idx + lrow * nkvb);
-  const int nblocks = nf + np;
-  // split-KV part w.c of nsplit: visits [v0, v0 + nvis) of the row's order
-  const int per_part = (nblocks + p.nsplit - 1) / p.nsplit;
-  const int v0 = min(w.c * per_part, nblocks);
-  const int nvis = min(per_part, nblocks - v0);
-  const int nstages = nvis * SPB;
 
-  const ScoreConsts sc = make_score_consts(p, w.h);
-  // mask_mod as an interval of key indices per row: j in [lo_abs, lo_abs + span)
-  // (64-bit so that any window >= 1 is exact; keys are >= 0, so the
-  // interval start is clamped there)
-  const int hi_abs =
-      mkind == FA_MASK_NONE ? kv_len
-      : mkind == FA_MASK_LOCAL_WINDOW
-          ? static_cast<int>(min(static_cast<int64_t>(i) + window, static_cast<int64_t>(kv_len)))
-          : min(i + 1, kv_len);
-  const int lo_abs =
-      (mkind == FA_MASK_SLIDING_WINDOW || mkind == FA_MASK_LOCAL_WINDOW)
-          ? static_cast<int>(max(static_cast<int64_t>(i) - window + 1, static_cast<int64_t>(0)))
-          : 0;
-  const unsigned span = static_cast<unsigned>(max(hi_abs - lo_abs, 0));
-
-  // ---- per-lane byte offsets, fixed for the whole row
+  // ---- per-lane byte offsets, fixed for the whole launch
   int k_rd[DK];  // K operand: row lq (+32 jt), chunk 2dk + g
   {
     const int s = kv_swizzle<D>(lq);
@@ -230,30 +300,87 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
     dma_v[rd] = static_cast<uint32_t>(r * vstride) + col;
   }
 
+  // ---- an item's uniform state: its key/value heads, block lists and
+  // visits (split-KV part w.c of nsplit visits [v0, v0 + nvis) of the row)
+  struct Item {
+    WorkItem w;
+    const char* kbase;
+    const char* vbase;
+    const int* doc;       // document ids of this batch entry
+    const const_i32* pl;  // partial list, through the constant address
+    const const_i32* fl;  // space: uniform scalar loads, tracked by
+    int np, nf, v0, nvis; // lgkmcnt (never waits on tile DMA)
+                          // stages with keys:
+    int nstages;
+  };
+  auto make_item = [&](const WorkItem& wi0) -> Item {
+    KArgs& p = kargs();
+    // (uniform by construction; stated so that every derived address is
+    // scalar)
+    WorkItem wi;
+    wi.b = __builtin_amdgcn_readfirstlane(wi0.b);
+    wi.h = __builtin_amdgcn_readfirstlane(wi0.h);
+    wi.m = __builtin_amdgcn_readfirstlane(wi0.m);
+    wi.c = __builtin_amdgcn_readfirstlane(wi0.c);
+    Item u;
+    u.w = wi;
+    const int hk = wi.h / (p.H / p.H_kv);
+    u.kbase = reinterpret_cast<const char*>(
+        static_cast<const __bf16*>(p.k) + wi.b * p.ks[0] + hk * p.ks[1]);
+    u.vbase = reinterpret_cast<const char*>(
+        static_cast<const __bf16*>(p.v) + wi.b * p.vs[0] + hk * p.vs[1]);
+    u.doc = p.mask.doc_id + static_cast<int64_t>(wi.b) * p.mask.doc_stride;
+    // the row's block lists (broadcast over batch / head when Bm / Hm is 1)
+    const int bb = p.Bm == 1 ? 0 : wi.b;
+    const int hh = p.Hm == 1 ? 0 : wi.h;
+    const int64_t lrow = (static_cast<int64_t>(bb) * p.Hm + hh) * p.nqb + wi.m;
+    u.nf = p.fnum ? min(max(((const const_i32*)p.fnum)[lrow], 0), nkvb) : 0;
+    u.np = min(max(((const const_i32*)p.num)[lrow], 0), nkvb);
+    u.fl = hw::uniform_ptr((const const_i32*)(p.fidx ? p.fidx + lrow * nkvb : p.idx));
+    u.pl = hw::uniform_ptr((const const_i32*)(p.idx + lrow * nkvb));
+    u.kbase = hw::uniform_ptr(u.kbase);
+    u.vbase = hw::uniform_ptr(u.vbase);
+    u.doc = hw::uniform_ptr(u.doc);
+    const int nblocks = u.nf + u.np;
+    const int per_part = (nblocks + p.nsplit - 1) / p.nsplit;
+    u.v0 = min(wi.c * per_part, nblocks);
+    u.nvis = min(per_part, nblocks - u.v0);
+    u.nstages = u.nvis * SPB;
+    return u;
+  };
+
   // visiting order: partial blocks, then full blocks, each list from the
   // last block to the first; inside a block the later 64 keys come first
   // (`it` counts the visits of this workgroup's part)
-  auto block_at = [&](int it) -> int {
-    const int v = v0 + it;
-    return v < np ? pl[np - 1 - v] : fl[nf - 1 - (v - np)];
+  auto block_at = [&](const Item& u, int it) -> int {
+    const int v = u.v0 + it;
+    // (the list pointers restated as uniform where they are used: the
+    // lookup must be a scalar load, which never waits on tile DMA)
+    return v < u.np ? hw::uniform_ptr(u.pl)[u.np - 1 - v]
+                    : hw::uniform_ptr(u.fl)[u.nf - 1 - (v - u.np)];
   };
-  auto masked_at = [&](int it, int n) -> bool {
-    return v0 + it < np || (n + 1) * BK > kv_len;
+  auto masked_at = [&](const Item& u, int it, int n) -> bool {
+    return u.v0 + it < u.np || (n + 1) * BK > kv_len;
+  };
+  // block of stage st (one scalar load per key block: the stages of a block
+  // share it); -1 past the item's last stage or for an index outside
+  // [0, nkvb)
+  auto stage_block = [&](const Item& u, int st) -> int {
+    if (st >= u.nstages) return -1;
+    const int b = block_at(u, st / SPB);
+    return static_cast<unsigned>(b) < static_cast<unsigned>(nkvb) ? b : -1;
   };
 
-  // Issue the DMA of stage `st` (block visit st / SPB) into one buffer. Each
+  // Issue the DMA of stage `st` (block n) of item u into one buffer. Each
   // tile is read through a buffer resource whose base is the stage's first
   // row and whose size ends at the sequence end: rows past it read as zeros
   // (the hardware range check), so the tail needs no special path.
-  // block of stage st (one scalar load per key block: the stages of a block
-  // share it), -1 for an index outside [0, nkvb)
-  auto stage_block = [&](int st) -> int {
-    const int b = block_at(st / SPB);
-    return static_cast<unsigned>(b) < static_cast<unsigned>(nkvb) ? b : -1;
-  };
-  auto issue = [&](int st, int n, char* sK, char* sV, int* sD) {
-    const int it = st / SPB;
+  auto issue = [&](const Item& u, int st, int n, char* sK, char* sV, int* sD) {
+    // (uniform; stated so that the buffer descriptors are scalar)
+    n = __builtin_amdgcn_readfirstlane(n);
+    st = __builtin_amdgcn_readfirstlane(st);
     if (n < 0) return;
+    const int it = st / SPB;
     const int j0 = n * BK + (SPB - 1 - st % SPB) * kStageKeys;
     // Rows of the stage inside the sequence. A stage of the last, ragged
     // key block may lie wholly past the end (its later keys come first):
@@ -265,249 +392,369 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
     const int vrec = rows_left >= kStageKeys ? 0x7fffffff
                      : rows_left <= 0       ? 0
                                             : (rows_left - 1) * static_cast<int>(vstride) + RB;
-    const hw::i32x4 kr = hw::make_rsrc(kbase + (rows_left > 0 ? j0 * kstride : 0), krec);
-    const hw::i32x4 vr = hw::make_rsrc(vbase + (rows_left > 0 ? j0 * vstride : 0), vrec);
+    const hw::i32x4 kr = hw::make_rsrc(u.kbase + (rows_left > 0 ? j0 * kstride : 0), krec);
+    const hw::i32x4 vr = hw::make_rsrc(u.vbase + (rows_left > 0 ? j0 * vstride : 0), vrec);
+    // this wave's 1 KB segments: base + wave KB (+ NW KB per round)
+    const uint32_t lk = hw::opaque_u32(hw::lds_addr(sK) + wave * 1024);
+    const uint32_t lv = lk + static_cast<uint32_t>(sV - sK);
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
-      const int seg = (rd * NW + wave) * 1024;
-      hw::dma_tile16(kr, hw::lds_addr(sK + seg), dma_k[rd], 0);
-      hw::dma_tile16(vr, hw::lds_addr(sV + seg), dma_v[rd], 0);
+      hw::dma_tile16(kr, lk + rd * NW * 1024, dma_k[rd], 0);
+      hw::dma_tile16(vr, lv + rd * NW * 1024, dma_v[rd], 0);
     }
-    if (doc_mask && masked_at(it, n) && wave == 0) {
+    if constexpr (doc_mask) {
+      if (masked_at(u, it, n) && wave == 0) {
       const int j = min(j0 + lane, kv_len - 1);
-      hw::dma_dword(doc, hw::lds_addr(sD), static_cast<uint32_t>(j * 4));
+      hw::dma_dword(u.doc, hw::lds_addr(sD), static_cast<uint32_t>(j * 4));
+      }
     }
   };
 
-  float m_run = FA_NEG_INF;  // reference max, log2 domain
-  float l_run = 0.0f;        // this lane's share of the row sum, in two
-  float l_run2 = 0.0f;       // independent accumulators
-  f32x16 oacc[DT];
+  // Q^T as the MFMA B operand: column = query lq, k slots d in [16dk + 8g, +8)
+  bf16x8 qf[DK];
+  auto load_q = [&](const WorkItem& wi) {
+    KArgs& p = kargs();
+    const int i = wi.m * BQ + wave * 32 + lq;
+    const bool ok = i < p.q_len;
+    const __bf16* row = static_cast<const __bf16*>(p.q) + wi.b * p.qs[0] + wi.h * p.qs[1] +
+                        static_cast<int64_t>(ok ? i : 0) * p.qs[2];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
+    for (int dk = 0; dk < DK; ++dk) {
+      u32x4 x = ok ? *reinterpret_cast<const u32x4*>(row + dk * 16 + g * 8)
+                   : u32x4{0u, 0u, 0u, 0u};
+      qf[dk] = __builtin_bit_cast(bf16x8, x);
+    }
+  };
+  auto load_di = [&](const Item& u) -> int {
+    const int i = u.w.m * BQ + wave * 32 + lq;
+    if constexpr (doc_mask) return u.doc[i < p.q_len ? i : 0];
+    return 0;
+  };
+
+  Item cur = make_item(w);
+  load_q(cur.w);
+  int di = load_di(cur);
+  // the setup loads (Q, document id) complete before the first tile DMA, so
+  // the per-stage waits below only ever wait for tiles
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  issue(cur, 0, stage_block(cur, 0), sK0, sV0, sDoc0);
+
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  // persistent schedule, lane 0 of wave 0 only: the counter value asked for
+  // (xs: the XCD range it came from)
+  unsigned pending = 0;
 
-  auto compute = [&](int st, int n, const char* sK, const char* sV, const int* sD) {
-    const int it = st / SPB;
-    if (n < 0) return;
-    const bool masked = masked_at(it, n);
-    const int j0 = n * BK + (SPB - 1 - st % SPB) * kStageKeys;
+  for (;;) {
+    // ---- this item's per-lane terms
+    const int i = cur.w.m * BQ + wave * 32 + lq;
+    const bool i_ok = i < kargs().q_len;
+    const ScoreConsts sc = make_score_consts(kargs(), cur.w.h);
+    // mask_mod as an interval of key indices per row: j in [lo_abs, lo_abs + span)
+    // (64-bit so that any window >= 1 is exact; keys are >= 0, so the
+    // interval start is clamped there)
+    const int hi_abs =
+        mkind == FA_MASK_NONE ? kv_len
+        : mkind == FA_MASK_LOCAL_WINDOW
+            ? static_cast<int>(min(static_cast<int64_t>(i) + window, static_cast<int64_t>(kv_len)))
+            : min(i + 1, kv_len);
+    const int lo_abs =
+        (mkind == FA_MASK_SLIDING_WINDOW || mkind == FA_MASK_LOCAL_WINDOW)
+            ? static_cast<int>(max(static_cast<int64_t>(i) - window + 1, static_cast<int64_t>(0)))
+            : 0;
+    const unsigned span = static_cast<unsigned>(max(hi_abs - lo_abs, 0));
 
-    // ---- S^T = K Q^T for the stage's 64 keys, at normal priority (see the
-    // PV product below)
-    __builtin_amdgcn_s_setprio(0);
-    f32x16 s[2];
-    s[0] = f32x16{};
-    s[1] = f32x16{};
-    u32x4 ka[DK][2];
+    float m_run = FA_NEG_INF;  // reference max, log2 domain
+    float l_run = 0.0f;        // this lane's share of the row sum, in two
+    float l_run2 = 0.0f;       // independent accumulators
+    f32x16 oacc[DT];
 #pragma unroll
-    for (int dk = 0; dk < DK; ++dk)
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-        ka[dk][jt] = *reinterpret_cast<const u32x4*>(sK + k_rd[dk] + jt * 32 * RB);
-#pragma unroll
-    for (int dk = 0; dk < DK; ++dk)
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-        s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[dk][jt]),
-                                                        qf[dk], s[jt], 0, 0, 0);
-    // K operand reads kept kSReadAhead ahead of the products that use them
-    // (left to itself the scheduler issues each read just before its
-    // product and waits on it)
-    __builtin_amdgcn_sched_group_barrier(0x100, kSReadAhead, 0);  // LDS reads
-#pragma unroll
-    for (int t = 0; t < 2 * DK - kSReadAhead; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kSReadAhead, 0);
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
 
-    // ---- score_mod into the log2 domain (NONE keeps raw q.k: c > 0 is
-    // applied in the exponent). Key of (jt, r): j0 + 4g + 32jt + 8(r/4) + r%4.
-    if constexpr (SCORE == FA_SCORE_ALIBI) {
-      const float bias0 = sc.slope2 * static_cast<float>(j0 + 4 * g - i);
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float b = __builtin_fmaf(sc.slope2, static_cast<float>(32 * jt + 8 * (r >> 2) + (r & 3)), bias0);
-          s[jt][r] = __builtin_fmaf(s[jt][r], sc.c, b);
-        }
-    } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
-      // cap * tanh(x) * log2e with tanh x = 1 - 2 / (e^{2x} + 1)
-      const float k2 = 2.0f * sc.cap_in * kLog2e;
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = exp2_hw(s[jt][r] * k2);
-          const float t = __builtin_amdgcn_rcpf(e + 1.0f);
-          s[jt][r] = __builtin_fmaf(-2.0f * sc.cap_out, t, sc.cap_out);
-        }
-    }
+    // the next item (persistent schedule, logical index, -1 for none):
+    // known to every wave from the top of stage 1 on; its first stage is
+    // fetched during this item's last stage
+    int next_logical = -1;
+    auto compute = [&](int st, int n, const char* sK, const char* sV, const int* sD) {
+      const int it = st / SPB;
+      if (n < 0) return;
+      const bool masked = masked_at(cur, it, n);
+      const int j0 = n * BK + (SPB - 1 - st % SPB) * kStageKeys;
 
-    // ---- mask_mod on partial and sequence-tail blocks only. Every built-in
-    // mask bounds a row's keys to an interval (causal: j <= i, sliding
-    // window: i - W < j <= i, local window: |i - j| < W, and j < kv_len),
-    // so the test is one unsigned
-    // compare of the key's offset in the interval against its length, plus
-    // the document-id equality for document masks.
-    if (masked) {
-      const int lo = lo_abs - (j0 + 4 * g);  // interval start, lane-relative
-      if (doc_mask) {
+      // ---- S^T = K Q^T for the stage's 64 keys, at normal priority (see the
+      // PV product below)
+      __builtin_amdgcn_s_setprio(0);
+      f32x16 s[2];
+      s[0] = f32x16{};
+      s[1] = f32x16{};
+      u32x4 ka[DK][2];
+#pragma unroll
+      for (int dk = 0; dk < DK; ++dk)
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
+          ka[dk][jt] = *reinterpret_cast<const u32x4*>(sK + k_rd[dk] + jt * 32 * RB);
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const int jl = 32 * jt + 8 * r4;
-            const int4 t = *reinterpret_cast<const int4*>(sD + 4 * g + jl);
-            const int dj[4] = {t.x, t.y, t.z, t.w};
+      for (int dk = 0; dk < DK; ++dk)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const bool ok = (static_cast<unsigned>(jl + c - lo) < span) & (dj[c] == di);
-              s[jt][4 * r4 + c] = ok ? s[jt][4 * r4 + c] : FA_NEG_INF;
-            }
-          }
-      } else {
+        for (int jt = 0; jt < 2; ++jt)
+          s[jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ka[dk][jt]),
+                                                          qf[dk], s[jt], 0, 0, 0);
+      // K operand reads kept kSReadAhead ahead of the products that use them
+      // (left to itself the scheduler issues each read just before its
+      // product and waits on it)
+      __builtin_amdgcn_sched_group_barrier(0x100, kSReadAhead, 0);  // LDS reads
+#pragma unroll
+      for (int t = 0; t < 2 * DK - kSReadAhead; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kSReadAhead, 0);
+
+      // (the loads replace Q: they must not be scheduled above the S product)
+
+      // ---- score_mod into the log2 domain (NONE keeps raw q.k: c > 0 is
+      // applied in the exponent). Key of (jt, r): j0 + 4g + 32jt + 8(r/4) + r%4.
+      if constexpr (SCORE == FA_SCORE_ALIBI) {
+        const float bias0 = sc.slope2 * static_cast<float>(j0 + 4 * g - i);
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int jl = 32 * jt + 8 * (r >> 2) + (r & 3);
-            s[jt][r] = static_cast<unsigned>(jl - lo) < span ? s[jt][r] : FA_NEG_INF;
+            const float b = __builtin_fmaf(sc.slope2, static_cast<float>(32 * jt + 8 * (r >> 2) + (r & 3)), bias0);
+            s[jt][r] = __builtin_fmaf(s[jt][r], sc.c, b);
+          }
+      } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
+        // cap * tanh(x) * log2e with tanh x = 1 - 2 / (e^{2x} + 1)
+        const float k2 = 2.0f * sc.cap_in * kLog2e;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = exp2_hw(s[jt][r] * k2);
+            const float t = __builtin_amdgcn_rcpf(e + 1.0f);
+            s[jt][r] = __builtin_fmaf(-2.0f * sc.cap_out, t, sc.cap_out);
           }
       }
-    }
 
-    // ---- online softmax. Row max: four independent chains, then the
-    // exchange with lane ^ 32 (the other half of the row's keys).
-    float mx4[4] = {FA_NEG_INF, FA_NEG_INF, FA_NEG_INF, FA_NEG_INF};
+      // ---- mask_mod on partial and sequence-tail blocks only. Every built-in
+      // mask bounds a row's keys to an interval (causal: j <= i, sliding
+      // window: i - W < j <= i, local window: |i - j| < W, and j < kv_len),
+      // so the test is one unsigned compare of the key's offset in the
+      // interval against its length, plus the document-id equality for
+      // document masks.
+      if (masked) {
+        const int lo = lo_abs - (j0 + 4 * g);  // interval start, lane-relative
+        if constexpr (doc_mask) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+          for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int r = 0; r < 8; ++r) mx4[c] = __builtin_fmaxf(mx4[c], s[c >> 1][8 * (c & 1) + r]);
-    float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
-    mx = row_pair_max(mx);
-    if constexpr (SCORE == FA_SCORE_NONE) mx *= sc.c;  // raw -> log2 domain
-    const bool raise = mx > m_run + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float m_new = raise ? mx : m_run;
-      const float alpha = (m_new == m_run) ? 1.0f : exp2_hw(m_run - m_new);
-      l_run *= alpha;
-      l_run2 *= alpha;
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const int jl = 32 * jt + 8 * r4;
+              const int4 t = *reinterpret_cast<const int4*>(sD + 4 * g + jl);
+              const int dj[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == FA_NEG_INF) ? 0.0f : m_run;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      f32x8 pf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = s[kk >> 1][(kk & 1) * 8 + e];
-        if constexpr (SCORE == FA_SCORE_NONE) {
-          pf[e] = exp2_hw(__builtin_fmaf(x, sc.c, -m_use));
+              for (int c = 0; c < 4; ++c) {
+                const bool ok = (static_cast<unsigned>(jl + c - lo) < span) & (dj[c] == di);
+                s[jt][4 * r4 + c] = ok ? s[jt][4 * r4 + c] : FA_NEG_INF;
+              }
+            }
         } else {
-          pf[e] = exp2_hw(x - m_use);
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int jl = 32 * jt + 8 * (r >> 2) + (r & 3);
+              s[jt][r] = static_cast<unsigned>(jl - lo) < span ? s[jt][r] : FA_NEG_INF;
+            }
         }
       }
-      pb[kk] = __builtin_convertvector(pf, bf16x8);
-      const u32x4 pw = __builtin_bit_cast(u32x4, pb[kk]);
+
+      // ---- online softmax. Row max: four independent chains, then the
+      // exchange with lane ^ 32 (the other half of the row's keys).
+      float mx4[4] = {FA_NEG_INF, FA_NEG_INF, FA_NEG_INF, FA_NEG_INF};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // copy the word out first: bit-casting a vector element in place
-        // mis-compiles (every iteration reads element 0)
-        const uint32_t word = pw[e];
-        float& acc = (e & 1) ? l_run2 : l_run;
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, acc,
-                                              false);
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) mx4[c] = __builtin_fmaxf(mx4[c], s[c >> 1][8 * (c & 1) + r]);
+      float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
+      mx = row_pair_max(mx);
+      if constexpr (SCORE == FA_SCORE_NONE) mx *= sc.c;  // raw -> log2 domain
+      const bool raise = mx > m_run + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float m_new = raise ? mx : m_run;
+        const float alpha = (m_new == m_run) ? 1.0f : exp2_hw(m_run - m_new);
+        l_run *= alpha;
+        l_run2 *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
       }
+      const float m_use = (m_run == FA_NEG_INF) ? 0.0f : m_run;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        f32x8 pf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = s[kk >> 1][(kk & 1) * 8 + e];
+          if constexpr (SCORE == FA_SCORE_NONE) {
+            pf[e] = exp2_hw(__builtin_fmaf(x, sc.c, -m_use));
+          } else {
+            pf[e] = exp2_hw(x - m_use);
+          }
+        }
+        pb[kk] = __builtin_convertvector(pf, bf16x8);
+        const u32x4 pw = __builtin_bit_cast(u32x4, pb[kk]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // copy the word out first: bit-casting a vector element in place
+          // mis-compiles (every iteration reads element 0)
+          const uint32_t word = pw[e];
+          float& acc = (e & 1) ? l_run2 : l_run;
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, acc,
+                                                false);
+        }
+      }
+
+      // ---- O^T += V^T P^T (4 k-steps of 16 keys). The wave raises its issue
+      // priority from here until its next stage's S product: of the two waves
+      // sharing a SIMD, the one whose P is ready gets its products issued ahead
+      // of the other's softmax arithmetic, which keeps the matrix core fed.
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const i16x4 lo = lds_read_tr(sV + v_rd[0][dt] + kk * 16 * RB);
+          const i16x4 hi = lds_read_tr(sV + v_rd[1][dt] + kk * 16 * RB);
+          const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[kk],
+                                                             oacc[dt], 0, 0, 0);
+        }
+      }
+    };
+
+    // ---- main loop over stages, unrolled by two so each LDS buffer is its
+    // own object; the DMA of stage st + 1 overlaps the compute of stage st.
+    // At the top of each stage this lane's DMA has landed (vmcnt), then
+    // every lane's (barrier), which also frees the other buffer. Persistent
+    // schedule: lane 0 asks for the next item after the barrier of stage 0
+    // and publishes it before the barrier of stage 1; an item with an even
+    // number of stages ends in buffer 1, and the next item's first stage
+    // goes to buffer 0 during its last stage. n_cur: block of stage st;
+    // n_nxt: of stage st + 1.
+    int n_cur = stage_block(cur, 0);
+    const int nstages = cur.nstages;
+    bool first_issued = false;  // the next item's first stage is in flight
+    for (int st = 0; st < nstages; st += 2) {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+      __syncthreads();
+      if (persistent && st == 0 && tid == 0)
+        pending = __hip_atomic_fetch_add(kargs().sched + (xs & 7), 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      int n_nxt = st + 1 >= nstages ? -1 : (st + 1) % SPB == 0 ? stage_block(cur, st + 1) : n_cur;
+      if (st + 1 < nstages) issue(cur, st + 1, n_nxt, sK1, sV1, sDoc1);
+      compute(st, n_cur, sK0, sV0, sDoc0);
+      if (st + 1 >= nstages) break;
+      n_cur = n_nxt;
+      __builtin_amdgcn_s_waitcnt(0x0f70);
+      // (one counter only here; moving on to other ranges, which takes
+      // further atomics, waits for the end of the item)
+      if (persistent && st == 0 && tid == 0) sNext = sched_check(kargs(), pending, xs);
+      __syncthreads();
+      if (persistent && st == 0) next_logical = __builtin_amdgcn_readfirstlane(sNext);
+      n_nxt = st + 2 >= nstages ? -1 : (st + 2) % SPB == 0 ? stage_block(cur, st + 2) : n_cur;
+      if (st + 2 < nstages) {
+        issue(cur, st + 2, n_nxt, sK0, sV0, sDoc0);
+      } else if (next_logical >= 0) {  // (-2: not known yet)
+        WorkItem wn;
+        logical_item(kargs(), next_logical, wn);
+        const Item u = make_item(wn);
+        issue(u, 0, stage_block(u, 0), sK0, sV0, sDoc0);
+        first_issued = true;
+      }
+      compute(st + 1, n_cur, sK1, sV1, sDoc1);
+      n_cur = n_nxt;
     }
 
-    // ---- O^T += V^T P^T (4 k-steps of 16 keys). The wave raises its issue
-    // priority from here until its next stage's S product: of the two waves
-    // sharing a SIMD, the one whose P is ready gets its products issued ahead
-    // of the other's softmax arithmetic, which keeps the matrix core fed.
-    __builtin_amdgcn_s_setprio(1);
+    // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
+    {
+    KArgs& p = kargs();
+    const float l_tot = row_pair_sum(l_run + l_run2);
+    if (p.nsplit > 1) {
+      // split-KV part: the unnormalised accumulator and (m, l) for the merge
+      if (i_ok) {
+        const int64_t prow =
+            (static_cast<int64_t>(cur.w.c) * p.B * p.H + static_cast<int64_t>(cur.w.b) * p.H +
+             cur.w.h) * p.q_len + i;
+        float* po = p.part_o + prow * D;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const i16x4 lo = lds_read_tr(sV + v_rd[0][dt] + kk * 16 * RB);
-        const i16x4 hi = lds_read_tr(sV + v_rd[1][dt] + kk * 16 * RB);
-        const i16x8 a8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a8), pb[kk],
-                                                           oacc[dt], 0, 0, 0);
+          for (int q4 = 0; q4 < 4; ++q4)
+            *reinterpret_cast<f32x4*>(po + dt * 32 + 8 * q4 + 4 * g) =
+                f32x4{oacc[dt][4 * q4 + 0], oacc[dt][4 * q4 + 1], oacc[dt][4 * q4 + 2],
+                      oacc[dt][4 * q4 + 3]};
+        if (g == 0) {
+          p.part_ml[2 * prow] = m_run;
+          p.part_ml[2 * prow + 1] = l_tot;
+        }
       }
-    }
-  };
-
-  // ---- main loop over stages, unrolled by two so each LDS buffer is its
-  // own object; the DMA of stage st + 1 overlaps the compute of stage st.
-  // The setup loads (Q, document id) complete before the first tile DMA, so
-  // the per-stage waits below only ever wait for tiles.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  // n_cur: block of stage st; n_nxt: of stage st + 1 (loaded with its DMA)
-  int n_cur = nstages > 0 ? stage_block(0) : -1;
-  if (nstages > 0) issue(0, n_cur, sK0, sV0, sDoc0);
-  for (int st = 0; st < nstages; st += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's DMA landed
-    __syncthreads();                     // every lane's DMA landed; buffer 1 free
-    // (no lookup past the last stage: the list index would leave the row)
-    int n_nxt = st + 1 >= nstages ? -1 : (st + 1) % SPB == 0 ? stage_block(st + 1) : n_cur;
-    if (st + 1 < nstages) issue(st + 1, n_nxt, sK1, sV1, sDoc1);
-    compute(st, n_cur, sK0, sV0, sDoc0);
-    if (st + 1 >= nstages) break;
-    n_cur = n_nxt;
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-    n_nxt = st + 2 >= nstages ? -1 : (st + 2) % SPB == 0 ? stage_block(st + 2) : n_cur;
-    if (st + 2 < nstages) issue(st + 2, n_nxt, sK0, sV0, sDoc0);
-    compute(st + 1, n_cur, sK1, sV1, sDoc1);
-    n_cur = n_nxt;
-  }
-
-  // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2
-  const float l_tot = row_pair_sum(l_run + l_run2);
-  if (p.nsplit > 1) {
-    // split-KV part: the unnormalised accumulator and (m, l) for the merge
-    if (i_ok) {
-      const int64_t prow =
-          (static_cast<int64_t>(w.c) * p.B * p.H + static_cast<int64_t>(w.b) * p.H + w.h) *
-              p.q_len + i;
-      float* po = p.part_o + prow * D;
+    } else if (i_ok) {
+      const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+      const int64_t orow = (static_cast<int64_t>(cur.w.b) * p.H + cur.w.h) * p.q_len + i;
+      __bf16* op = static_cast<__bf16*>(p.o) + orow * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4*>(po + dt * 32 + 8 * q4 + 4 * g) =
-              f32x4{oacc[dt][4 * q4 + 0], oacc[dt][4 * q4 + 1], oacc[dt][4 * q4 + 2],
-                    oacc[dt][4 * q4 + 3]};
-      if (g == 0) {
-        p.part_ml[2 * prow] = m_run;
-        p.part_ml[2 * prow + 1] = l_tot;
-      }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v4 = {oacc[dt][4 * q4 + 0] * inv, oacc[dt][4 * q4 + 1] * inv,
+                            oacc[dt][4 * q4 + 2] * inv, oacc[dt][4 * q4 + 3] * inv};
+          *reinterpret_cast<bf16x4*>(op + dt * 32 + 8 * q4 + 4 * g) =
+              __builtin_convertvector(v4, bf16x4);
+        }
+      if (g == 0 && p.lse)
+        p.lse[orow] = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : FA_NEG_INF;
     }
-    return;
-  }
-  if (i_ok) {
-    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    const int64_t orow = (static_cast<int64_t>(w.b) * p.H + w.h) * p.q_len + i;
-    __bf16* op = static_cast<__bf16*>(p.o) + orow * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v4 = {oacc[dt][4 * q4 + 0] * inv, oacc[dt][4 * q4 + 1] * inv,
-                          oacc[dt][4 * q4 + 2] * inv, oacc[dt][4 * q4 + 3] * inv};
-        *reinterpret_cast<bf16x4*>(op + dt * 32 + 8 * q4 + 4 * g) =
-            __builtin_convertvector(v4, bf16x4);
+    }
+    if (persistent && (nstages < 2 || next_logical == -2)) {
+      // the next item was not published in the loop (fewer than two
+      // stages), or this workgroup's range is used up: ask the counters,
+      // moving on to the following XCDs' ranges
+      if (tid == 0) {
+        if (nstages == 0)
+          pending = __hip_atomic_fetch_add(kargs().sched + (xs & 7), 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+        if (nstages >= 2) {  // the published value was this range's last word
+          if (++xs < static_cast<int>(blockIdx.x & 7) + 8)
+            sNext = sched_resolve(kargs(),
+                                  __hip_atomic_fetch_add(kargs().sched + (xs & 7), 1u,
+                                                         __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT),
+                                  xs);
+          else
+            sNext = -1;
+        } else {
+          sNext = sched_resolve(kargs(), pending, xs);
+        }
       }
-    if (g == 0 && p.lse)
-      p.lse[orow] = l_tot > 0.0f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : FA_NEG_INF;
+      __syncthreads();
+      next_logical = __builtin_amdgcn_readfirstlane(sNext);
+    }
+    if (next_logical < 0) break;
+    WorkItem wn;
+    logical_item(kargs(), next_logical, wn);
+    cur = make_item(wn);
+    if (!first_issued) {
+      // odd stage count or none: both buffers may still be read until every
+      // wave is here
+      __syncthreads();
+      issue(cur, 0, stage_block(cur, 0), sK0, sV0, sDoc0);
+    }
+    // the next item's Q (its first stage is already in flight)
+    load_q(cur.w);
+    di = load_di(cur);
   }
+  if (persistent && tid == 0) sched_finish(p);
 }
 
 }  // namespace fa

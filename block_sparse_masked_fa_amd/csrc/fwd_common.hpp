@@ -50,8 +50,8 @@ struct ScoreConsts {
   float cap_out;  // cap * log2e
 };
 
-__device__ __forceinline__ ScoreConsts make_score_consts(const FwdLaunch& p,
-                                                         int h) {
+template <class Params>
+__device__ __forceinline__ ScoreConsts make_score_consts(const Params& p, int h) {
   ScoreConsts k;
   k.c = p.scale * kLog2e;
   // slope_h = 2^(-8 (h + 1) / H)

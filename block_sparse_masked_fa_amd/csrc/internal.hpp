@@ -56,6 +56,10 @@ struct FwdLaunch {
   int32_t nsplit;
   float* part_o;
   float* part_ml;
+  // persistent schedule (bf16, nsplit == 1): kSchedCounters zero-initialised
+  // uint32 counters that the kernel leaves zero again; NULL = one workgroup
+  // per item
+  unsigned int* sched;
 };
 
 // Split-KV merge of the partial results described at FwdLaunch.

@@ -299,6 +299,20 @@ int check_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len, int32_t D,
   return FA_OK;
 }
 
+int check_fwd_workspace(int32_t dtype, void* workspace, uint64_t workspace_bytes,
+                        FwdLaunch* p, std::string* msg) {
+  p->sched = nullptr;
+  if (!workspace) return FA_OK;
+  if (!aligned16(workspace))
+    return fail(msg, FA_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (workspace_bytes < FA_FWD_WORKSPACE_BYTES)
+    return fail(msg, FA_ERR_INVALID_VALUE,
+                "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                    std::to_string(FA_FWD_WORKSPACE_BYTES));
+  if (dtype == FA_BF16) p->sched = static_cast<unsigned int*>(workspace);
+  return FA_OK;
+}
+
 int check_split(int32_t dtype, int32_t num_splits, void* workspace,
                 uint64_t workspace_bytes, FwdLaunch* p, CombineLaunch* cl,
                 std::string* msg) {

@@ -47,6 +47,11 @@ int check_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len, int32_t D,
 
 // Checks the split-KV arguments on top of a filled forward descriptor and
 // sets its split fields (and *cl for the merge kernel).
+// Forward scheduler workspace: NULL (one workgroup per query block) or at
+// least FA_FWD_WORKSPACE_BYTES, 16-byte aligned; sets p->sched for bf16.
+int check_fwd_workspace(int32_t dtype, void* workspace, uint64_t workspace_bytes,
+                        FwdLaunch* p, std::string* msg);
+
 int check_split(int32_t dtype, int32_t num_splits, void* workspace,
                 uint64_t workspace_bytes, FwdLaunch* p, CombineLaunch* cl,
                 std::string* msg);

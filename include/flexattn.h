@@ -49,7 +49,10 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 8
+#define FA_ABI_VERSION 9
+
+/* Bytes of the forward's scheduler workspace (see fa_flex_attention_fwd). */
+#define FA_FWD_WORKSPACE_BYTES 256
 
 typedef enum fa_status {
   FA_OK = 0,
@@ -201,7 +204,27 @@ fa_status fa_create_block_mask(const fa_mask_mod* mask, int32_t B, int32_t H,
  *              Index arrays may come from
  *              fa_create_block_mask or from the caller; entries outside
  *              [0, NKVB) are skipped and counts are clamped to [0, NKVB].
+ *              Caller lists must name each block of a row at most once,
+ *              in the partial or in the full list, not both: a repeated
+ *              entry is visited once per listing (its keys then count
+ *              twice in the softmax), while the backward's transposed
+ *              lists keep it once. Full blocks are taken as wholly
+ *              allowed (mask_mod is not evaluated on them). With a
+ *              per-batch doc_id (doc_stride != 0) the array must hold B
+ *              rows of doc_len ids; the library cannot check this.
  *   score      host pointer to the score_mod (NULL = none).
+ *   workspace  NULL, or device memory owned by the caller of at least
+ *              FA_FWD_WORKSPACE_BYTES bytes, 16-byte aligned, all zero
+ *              before its first use (workspace_bytes: its size). With a
+ *              workspace the bf16 kernel keeps about two workgroups per
+ *              compute unit resident and hands them query blocks one after
+ *              another from counters kept there (the next block's first
+ *              key/value tiles load while the current block finishes); the
+ *              kernel leaves the counters zero again, so one workspace
+ *              serves any number of calls in stream order. Calls in flight
+ *              at the same time need separate workspaces. NULL: one
+ *              workgroup per query block. Results are the same either way
+ *              (same arithmetic per row). The fp32 instance ignores it.
  *   o          device [B, H, q_len, D], contiguous, dtype; 16-byte aligned.
  *   lse        device fp32 [B, H, q_len], contiguous; may be NULL.
  *              lse = ln sum_j exp(s_j) over the allowed keys of the row, in
@@ -216,7 +239,8 @@ fa_status fa_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H,
                                 const int64_t k_stride[3], const void* v,
                                 const int64_t v_stride[3], float scale,
                                 const fa_block_mask* bm,
-                                const fa_score_mod* score, void* o, float* lse,
+                                const fa_score_mod* score, void* workspace,
+                                uint64_t workspace_bytes, void* o, float* lse,
                                 void* stream);
 
 /* Split-KV forward: the same operation as fa_flex_attention_fwd (same
@@ -230,8 +254,8 @@ fa_status fa_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H,
  * is small against its 256 compute units, at the price of the partial
  * results' round trip through memory.
  *
- *   num_splits       1 ... 64. 1 is fa_flex_attention_fwd (workspace may be
- *                    NULL). A part whose share of a row is empty writes a
+ *   num_splits       1 ... 64. 1 is fa_flex_attention_fwd without a
+ *                    scheduler workspace (workspace may be NULL). A part whose share of a row is empty writes a
  *                    neutral partial result.
  *   dtype            FA_BF16 when num_splits > 1 (else FA_ERR_UNSUPPORTED).
  *   workspace        device memory owned by the caller, 16-byte aligned, at

@@ -57,3 +57,34 @@ def assert_close(o_gpu, lse_gpu, o_ref, lse_ref, tol, what=""):
     assert err_o <= tol, f"{what}: max |O - oracle| = {err_o:.3g} > {tol}"
     assert err_l <= tol, f"{what}: max |LSE - oracle| = {err_l:.3g} > {tol}"
     return err_o, err_l
+
+
+def caller_lists(kind, mask, q_len, kv_len, block_m, block_n, window=None,
+                 doc_id=None):
+    """Index lists for BlockMask.from_kv_blocks, built on the host:
+    "oracle": the oracle's create_block_mask arrays; "no_skip": every key
+    block of every row listed as partial (no full list); "clamped": the
+    oracle's arrays with out-of-range entries after each row's partial
+    blocks and a partial count above NKVB (the kernels clamp the count and
+    skip the entries). Returns (num, idx, fnum, fidx), fnum/fidx None for
+    no_skip."""
+    ref = O.create_block_mask(mask, 1, 1, q_len, kv_len, block_m, block_n,
+                              window=window, doc_id=doc_id)
+    nqb, nkvb = ref["kv_indices"].shape[2], ref["kv_indices"].shape[3]
+    if kind == "no_skip":
+        num = np.full((1, 1, nqb), nkvb, dtype=np.int32)
+        idx = np.broadcast_to(np.arange(nkvb, dtype=np.int32),
+                              (1, 1, nqb, nkvb)).copy()
+        return num, idx, None, None
+    num = ref["kv_num_blocks"].astype(np.int32).copy()
+    idx = ref["kv_indices"].astype(np.int32).copy()
+    fnum = ref["full_kv_num_blocks"].astype(np.int32).copy()
+    fidx = ref["full_kv_indices"].astype(np.int32).copy()
+    if kind == "clamped":
+        bad = np.array([-1, nkvb, nkvb + 7, 2 ** 31 - 1, -(2 ** 31)],
+                       dtype=np.int64)
+        for m in range(nqb):
+            c = int(num[0, 0, m])
+            idx[0, 0, m, c:] = np.resize(bad, nkvb - c).astype(np.int32)
+            num[0, 0, m] = nkvb + 3 + m
+    return num, idx, fnum, fidx

@@ -192,7 +192,7 @@ def _fwd(**over):
              k_stride=(4 * 256 * 128, 256 * 128, 128), v=FAKE,
              v_stride=(4 * 256 * 128, 256 * 128, 128), scale=0.088,
              bm=_good_bm(), score=C.fa_score_mod(kind=C.FA_SCORE_NONE),
-             o=FAKE, lse=FAKE, stream=None)
+             o=FAKE, lse=FAKE, stream=None, workspace=None, workspace_bytes=0)
     a.update(over)
     return api.fa_flex_attention_fwd(**a)
 
@@ -239,6 +239,8 @@ def _fwd(**over):
     (dict(q_stride=(4 * 256 * 128, 256 * 128, 100)), C.FA_ERR_UNSUPPORTED),
     (dict(k_stride=(4 * 256 * 128, -128, 128)), C.FA_ERR_INVALID_VALUE),
     (dict(B=-1), C.FA_ERR_INVALID_VALUE),
+    (dict(workspace=FAKE + 4, workspace_bytes=256), C.FA_ERR_UNSUPPORTED),
+    (dict(workspace=FAKE, workspace_bytes=255), C.FA_ERR_INVALID_VALUE),
 ])
 def test_fwd_refuses(over, status):
     if "bm" in over and over["bm"] is None:
@@ -246,7 +248,7 @@ def test_fwd_refuses(over, status):
         st = C.lib().fa_flex_attention_fwd(
             C.FA_BF16, 1, 1, 1, 256, 256, 128, FAKE, C.Stride3(1, 1, 128),
             FAKE, C.Stride3(1, 1, 128), FAKE, C.Stride3(1, 1, 128), 0.1,
-            None, None, FAKE, FAKE, None)
+            None, None, None, 0, FAKE, FAKE, None)
         assert st == status
         return
     st = _fwd(**over)

@@ -13,8 +13,8 @@ import torch
 import block_sparse_masked_fa_amd as fa
 import workloads as WL
 from oracle import oracle as O
-from tests.helpers import TOL, assert_close, oracle_case, sample_rows, \
-    torch_dtype
+from tests.helpers import TOL, assert_close, caller_lists, oracle_case, \
+    sample_rows, torch_dtype
 
 pytestmark = pytest.mark.gpu
 
@@ -392,3 +392,74 @@ def test_errors_surface_as_exceptions():
     q = torch.randn(1, 1, 256, 96, device=DEV).to(torch.bfloat16)
     with pytest.raises(fa.FlexAttnError, match="UNSUPPORTED"):
         fa.flex_attention(q, q, q, bm)
+
+
+@pytest.mark.parametrize("blk", [128, 64])
+@pytest.mark.parametrize("mask,score", [("causal", "alibi"),
+                                        ("sliding_window", "none"),
+                                        ("document", "softcap")])
+def test_caller_lists(blk, mask, score):
+    # BlockMask.from_kv_blocks (the tensorplay create_block_mask page's route
+    # for precomputed metadata), unsplit and split: lists from the oracle's
+    # create_block_mask, every block listed as partial (the no-skip mode
+    # bench.py times), and lists with out-of-range entries and counts above
+    # NKVB (skipped and clamped). Each gives the plain attention.
+    ql = kl = 3 * blk + 45
+    w = WL.Workload("small", "bf16", 2, 4, 2, ql, kl, 128, mask, blk, blk,
+                    seed=0, window=blk + 9 if mask == "sliding_window" else None,
+                    score=score, softcap=5.0 if score == "softcap" else None)
+    rng = np.random.default_rng(zlib.crc32(f"lists{blk}{mask}{score}".encode()))
+    doc = (np.sort(rng.integers(0, 4, ql)).astype(np.int32)
+           if mask == "document" else None)
+    q, k, v = _inputs(w, 71)
+    o_ref, l_ref = oracle_case(q, k, v, w, doc)
+    doc_t = torch.from_numpy(doc).to(DEV) if doc is not None else None
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV) if a is not None else None
+    for kind in ("oracle", "no_skip", "clamped"):
+        num, idx, fnum, fidx = caller_lists(kind, mask, ql, kl, blk, blk,
+                                            window=w.window, doc_id=doc)
+        bm = fa.BlockMask.from_kv_blocks(t(num), t(idx), t(fnum), t(fidx),
+                                         mask_mod=mask, q_len=ql, kv_len=kl,
+                                         BLOCK_SIZE=blk, window=w.window,
+                                         doc_id=doc_t)
+        for ns in (1, 3):
+            print(f"[fwd caller lists] blk={blk} {mask} {score} {kind} splits={ns}",
+                  flush=True)
+            o, lse = run_gpu(w, q, k, v, doc, bm=bm, num_splits=ns)
+            assert_close(o, lse, o_ref, l_ref, TOL["bf16"],
+                         f"caller lists {kind} blk={blk} {mask} {score} split {ns}")
+
+
+def test_caller_lists_are_checked():
+    # shapes, dtype, and the uniqueness / disjointness rule are refused on
+    # the host before any launch
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+    num, idx, fnum, fidx = caller_lists("oracle", "causal", 300, 300, 128, 128)
+    kw = dict(mask_mod="causal", q_len=300, kv_len=300, BLOCK_SIZE=128)
+    fa.BlockMask.from_kv_blocks(t(num), t(idx), t(fnum), t(fidx), **kw)
+    with pytest.raises(ValueError):
+        fa.BlockMask.from_kv_blocks(t(num[0]), t(idx[0]), **kw)
+    with pytest.raises(ValueError):
+        fa.BlockMask.from_kv_blocks(t(num), t(idx[..., :2]), **kw)
+    with pytest.raises(ValueError):
+        fa.BlockMask.from_kv_blocks(t(num), t(idx), t(fnum), None, **kw)
+    dup = idx.copy()
+    dup[0, 0, 2, 1] = dup[0, 0, 2, 0]
+    n2 = num.copy()
+    n2[0, 0, 2] = 2
+    with pytest.raises(ValueError):
+        fa.BlockMask.from_kv_blocks(t(n2), t(dup), **kw)
+    both = fidx.copy()  # row 1: partial {1}, full {0} -> full {1}
+    both[0, 0, 1, 0] = idx[0, 0, 1, 0]
+    with pytest.raises(ValueError):
+        fa.BlockMask.from_kv_blocks(t(num), t(idx), t(fnum), t(both), **kw)
+    # out = / lse = of the wrong shape or dtype
+    w = WL.Workload("small", "bf16", 1, 2, 2, 300, 300, 64, "causal", 128, 128, seed=0)
+    q, k, v = (x.to(DEV) for x in _inputs(w, 1))
+    bm = fa.create_block_mask("causal", None, None, 300, 300, device=DEV)
+    with pytest.raises(ValueError):
+        fa.flex_attention(q, k, v, bm, out=torch.empty(1, 2, 299, 64, dtype=torch.bfloat16,
+                                                       device=DEV))
+    with pytest.raises(ValueError):
+        fa.flex_attention(q, k, v, bm, lse=torch.empty(1, 2, 300, device=DEV,
+                                                       dtype=torch.float64))

@@ -14,7 +14,7 @@ import torch
 import block_sparse_masked_fa_amd as fa
 import workloads as WL
 from oracle import oracle as O
-from tests.helpers import sample_rows
+from tests.helpers import caller_lists, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -404,3 +404,36 @@ def test_workload_backward(name, workload_inputs):
         krel = (dk.double().sum(dim=2).abs() / dk.double().abs().sum(dim=2)).max().item()
         print(f"[bwd workload] {name}: |sum dK| / sum |dK| = {krel:.3g}", flush=True)
         assert krel <= 1e-2
+
+
+@pytest.mark.parametrize("mask,score", [("causal", "none"), ("sliding_window", "alibi"),
+                                        ("document", "softcap")])
+def test_backward_caller_lists(mask, score):
+    # BlockMask.from_kv_blocks lists (oracle-built, all-partial no-skip,
+    # out-of-range entries with counts above NKVB): the backward's transposed
+    # lists are built from them and the gradients match the oracle, unsplit
+    # and in parts
+    blk = 128
+    ql = kl = 3 * blk + 45
+    w = WL.Workload("small", "bf16", 2, 4, 2, ql, kl, 128, mask, blk, blk,
+                    seed=0, window=blk + 9 if mask == "sliding_window" else None,
+                    score=score, softcap=5.0 if score == "softcap" else None)
+    rng = np.random.default_rng(zlib.crc32(f"bwdlists{mask}{score}".encode()))
+    doc = (np.sort(rng.integers(0, 4, ql)).astype(np.int32)
+           if mask == "document" else None)
+    q, k, v, do = _inputs(w, 73)
+    ref = oracle_bwd(w, q, k, v, do, doc)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV) if a is not None else None
+    for kind in ("oracle", "no_skip", "clamped"):
+        num, idx, fnum, fidx = caller_lists(kind, mask, ql, kl, blk, blk,
+                                            window=w.window, doc_id=doc)
+        bm = fa.BlockMask.from_kv_blocks(t(num), t(idx), t(fnum), t(fidx),
+                                         mask_mod=mask, q_len=ql, kv_len=kl,
+                                         BLOCK_SIZE=blk, window=w.window,
+                                         doc_id=_doc_t(doc))
+        for ns in (1, 3):
+            print(f"[bwd caller lists] {mask} {score} {kind} splits={ns}", flush=True)
+            got = gpu_fwd_bwd(w, q, k, v, do, doc, bm=bm, splits=ns)
+            for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+                assert_grad_close(g, r, f"{name} caller lists {kind} {mask} {score} "
+                                        f"splits={ns}")

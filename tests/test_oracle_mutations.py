@@ -63,6 +63,12 @@ MUTATIONS = [
     ("ragged tile counted full", "padded = np.zeros((len(rows), nkvb * block_n), dtype=bool)",
      "padded = np.ones((len(rows), nkvb * block_n), dtype=bool)",
      ["test_block_mask_lists_are_permutations_and_partition"]),
+    ("row chunk shifted", "ri = rows[r0:r0 + step]",
+     "ri = rows[r0 + (r0 > 0):r0 + step + (r0 > 0)]",
+     ["test_row_chunks_match_brute_force"]),
+    ("row chunk skipped", "for r0 in range(0, len(rows), step):",
+     "for r0 in range(0, len(rows), step + (step > 2)):",
+     ["test_row_chunks_match_brute_force"]),
     ("index tail reversed",
      "idx[m] = np.concatenate([cols[selected[m]], cols[~selected[m]]])",
      "idx[m] = np.concatenate([cols[selected[m]], cols[~selected[m]][::-1]])",

@@ -291,6 +291,34 @@ def test_attention_matches_brute_force(seed, mask, score):
     np.testing.assert_allclose(l, np.array(bl), rtol=0, atol=1e-12)
 
 
+def test_row_chunks_match_brute_force():
+    # The oracle evaluates the requested rows in chunks of at most
+    # chunk_bytes of fp64 scores. Force three rows per chunk: every chunk
+    # after the first (and a row subset whose chunk edges fall between
+    # unevenly spaced rows) must give the one-chunk result, and the brute
+    # force's values on those rows.
+    rng = np.random.default_rng(4242)
+    B, H, T, D = 1, 2, 13, 4
+    q = _rand(rng, B, H, T, D)
+    k = _rand(rng, B, H, T, D)
+    v = _rand(rng, B, H, T, D)
+    small = 8 * T * 3
+    for mask, kw in (("causal", {}), ("sliding_window", {"window": 4})):
+        bo, bl = brute.attention(_nested(q), _nested(k), _nested(v),
+                                 mask=mask, window=kw.get("window"))
+        bo, bl = np.array(bo), np.array(bl)
+        for rows in (None, np.array([0, 2, 3, 5, 6, 7, 9, 11, 12])):
+            o1, l1 = O.attention(q, k, v, mask=mask, rows=rows, **kw)
+            oc, lc = O.attention(q, k, v, mask=mask, rows=rows,
+                                 chunk_bytes=small, **kw)
+            sel = np.arange(T) if rows is None else rows
+            # (the matrix product may round differently per chunk shape)
+            np.testing.assert_allclose(oc, o1, rtol=0, atol=1e-14)
+            np.testing.assert_allclose(lc, l1, rtol=0, atol=1e-14)
+            np.testing.assert_allclose(oc, bo[:, :, sel], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lc, bl[:, :, sel], rtol=0, atol=1e-12)
+
+
 def test_per_batch_document_ids():
     # a batch of packed sequences: entry b uses its own ids. Brute force
     # (independent loops) agrees, each entry equals the shared-id
