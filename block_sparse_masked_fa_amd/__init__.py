@@ -14,7 +14,7 @@ from .api import (  # noqa: F401
     fa_split_workspace_bytes, flex_attention, flex_attention_backward,
     auto_bwd_splits, auto_decode_splits, fa_flex_attention_decode_paged,
     flex_attention_decode_paged, local_window, no_mask, masked_softmax,
-    fa_masked_softmax, fwd_workspace,
+    fa_masked_softmax, fwd_workspace, fa_flex_attention_fwd_split_noalloc,
     sliding_window,
     softcap,
 )

@@ -43,6 +43,9 @@ FA_MAX_SPLITS = 64
 # bytes of the forward's scheduler workspace
 FA_FWD_WORKSPACE_BYTES = 256
 
+# bytes of fa_flex_attention_fwd_split_noalloc's fixed device scratch
+FA_NOALLOC_SCRATCH_BYTES = 32 << 20
+
 ABI_VERSION = 9
 
 
@@ -106,6 +109,15 @@ SIGNATURES = {
         ctypes.c_float, ctypes.POINTER(fa_block_mask),
         ctypes.POINTER(fa_score_mod), ctypes.c_int32, ctypes.c_void_p,
         ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "fa_flex_attention_fwd_split_noalloc": (ctypes.c_int, [
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+        ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+        ctypes.c_float, ctypes.POINTER(fa_block_mask),
+        ctypes.POINTER(fa_score_mod), ctypes.c_int32, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p]),
     "fa_split_workspace_bytes": (ctypes.c_int, [
         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
         ctypes.c_int32, ctypes.POINTER(ctypes.c_uint64)]),

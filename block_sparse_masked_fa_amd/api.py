@@ -41,6 +41,7 @@ __all__ = [
     "fa_bwd_workspace_bytes", "auto_bwd_splits", "flex_attention_decode_paged",
     "fa_flex_attention_decode_paged", "auto_decode_splits",
     "masked_softmax", "fa_masked_softmax", "fwd_workspace",
+    "fa_flex_attention_fwd_split_noalloc",
 ]
 
 FlexAttnError = C.FlexAttnError
@@ -192,6 +193,23 @@ def fa_flex_attention_fwd_split(dtype: int, B: int, H: int, H_kv: int,
         v, C.Stride3(*v_stride), scale, ctypes.byref(bm),
         ctypes.byref(score) if score is not None else None, num_splits,
         workspace, workspace_bytes, o, lse, stream)
+
+
+def fa_flex_attention_fwd_split_noalloc(dtype: int, B: int, H: int,
+                                        H_kv: int, q_len: int, kv_len: int,
+                                        D: int, q: int, q_stride, k: int,
+                                        k_stride, v: int, v_stride,
+                                        scale: float, bm: C.fa_block_mask,
+                                        score: Optional[C.fa_score_mod],
+                                        num_splits: int, o: int,
+                                        lse: Optional[int],
+                                        stream: Optional[int]) -> int:
+    return C.lib().fa_flex_attention_fwd_split_noalloc(
+        dtype, B, H, H_kv, q_len, kv_len, D,
+        q, C.Stride3(*q_stride), k, C.Stride3(*k_stride),
+        v, C.Stride3(*v_stride), scale, ctypes.byref(bm),
+        ctypes.byref(score) if score is not None else None, num_splits,
+        o, lse, stream)
 
 
 def fa_split_workspace_bytes(B: int, H: int, q_len: int, D: int,

@@ -29,6 +29,7 @@ SOURCES = [
     "fwd_bf16_d128.hip",
     "fwd_fp32.hip",
     "fwd_combine.hip",
+    "fwd_noalloc.hip",
     "bwd_prepare.hip",
     "bwd_bf16_d64.hip",
     "bwd_bf16_d128.hip",

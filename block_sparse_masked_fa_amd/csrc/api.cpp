@@ -27,6 +27,10 @@ fa_status hip_status(int err, const char* what) {
 
 }  // namespace
 
+namespace fa {
+void record_error(const std::string& msg) { g_last_error = msg; }
+}  // namespace fa
+
 extern "C" {
 
 int32_t fa_abi_version(void) { return FA_ABI_VERSION; }

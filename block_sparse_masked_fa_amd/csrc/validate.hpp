@@ -41,17 +41,20 @@ int check_flex_attention_fwd(int32_t dtype, int32_t B, int32_t H, int32_t H_kv,
 // Largest number of split-KV parts per query block.
 constexpr int kMaxSplits = 64;
 
+// Sets the message fa_last_error() returns on the calling thread.
+void record_error(const std::string& msg);
+
 int check_split_workspace_bytes(int32_t B, int32_t H, int32_t q_len, int32_t D,
                                 int32_t num_splits, uint64_t* bytes,
                                 std::string* msg);
 
-// Checks the split-KV arguments on top of a filled forward descriptor and
-// sets its split fields (and *cl for the merge kernel).
 // Forward scheduler workspace: NULL (one workgroup per query block) or at
 // least FA_FWD_WORKSPACE_BYTES, 16-byte aligned; sets p->sched for bf16.
 int check_fwd_workspace(int32_t dtype, void* workspace, uint64_t workspace_bytes,
                         FwdLaunch* p, std::string* msg);
 
+// Checks the split-KV arguments on top of a filled forward descriptor and
+// sets its split fields (and *cl for the merge kernel).
 int check_split(int32_t dtype, int32_t num_splits, void* workspace,
                 uint64_t workspace_bytes, FwdLaunch* p, CombineLaunch* cl,
                 std::string* msg);

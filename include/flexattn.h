@@ -54,6 +54,10 @@ extern "C" {
 /* Bytes of the forward's scheduler workspace (see fa_flex_attention_fwd). */
 #define FA_FWD_WORKSPACE_BYTES 256
 
+/* Bytes of the fixed device scratch of fa_flex_attention_fwd_split_noalloc
+ * (32 MiB per GPU the library runs on). */
+#define FA_NOALLOC_SCRATCH_BYTES (32ull << 20)
+
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL_POINTER = 1,   /* a required pointer is NULL                 */
@@ -272,6 +276,32 @@ fa_status fa_flex_attention_fwd_split(
     const int64_t v_stride[3], float scale, const fa_block_mask* bm,
     const fa_score_mod* score, int32_t num_splits, void* workspace,
     uint64_t workspace_bytes, void* o, float* lse, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation as fa_flex_attention_fwd_split, with the parts' partial results
+ * kept in a fixed scratch array of FA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on (from the first call on that GPU until the
+ * process ends) instead of a caller workspace. No allocation of any kind.
+ *
+ *   num_splits  1 ... 64; the partial results must fit the scratch:
+ *               fa_split_workspace_bytes(B, H, q_len, D, num_splits) <=
+ *               FA_NOALLOC_SCRATCH_BYTES, else FA_ERR_INVALID_VALUE before
+ *               anything is launched. 1 runs fa_flex_attention_fwd without a
+ *               scheduler workspace (no scratch used).
+ *   Every other argument is as for fa_flex_attention_fwd_split.
+ * Calls on one GPU share its scratch: calls whose kernels may run at the
+ * same time on one GPU (different streams, or different host threads) race
+ * and give wrong results; serialise them. The scratch needs no clearing (each
+ * part writes every row it owns before the merge reads it). Two kernel
+ * launches (num_splits > 1); asynchronous. */
+fa_status fa_flex_attention_fwd_split_noalloc(
+    int32_t dtype, int32_t B, int32_t H, int32_t H_kv, int32_t q_len,
+    int32_t kv_len, int32_t D, const void* q, const int64_t q_stride[3],
+    const void* k, const int64_t k_stride[3], const void* v,
+    const int64_t v_stride[3], float scale, const fa_block_mask* bm,
+    const fa_score_mod* score, int32_t num_splits, void* o, float* lse,
+    void* stream);
 
 /* Workspace size of fa_flex_attention_fwd_split: num_splits * B * H * q_len
  * * (D + 2) * 4 bytes (fp32 partial outputs, then per-row maximum and
