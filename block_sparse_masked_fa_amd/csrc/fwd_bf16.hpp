@@ -511,37 +511,33 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
 
       // (the loads replace Q: they must not be scheduled above the S product)
 
-      // ---- score_mod into the log2 domain (NONE keeps raw q.k: c > 0 is
-      // applied in the exponent). Key of (jt, r): j0 + 4g + 32jt + 8(r/4) + r%4.
-      if constexpr (SCORE == FA_SCORE_ALIBI) {
-        const float bias0 = sc.slope2 * static_cast<float>(j0 + 4 * g - i);
+      // ---- score_mod, mask_mod and the row max. Every score ends up as a
+      // value x whose log2-domain score is one FMA away, s2 = x sa + sb
+      // (sa, sb fixed for the lane over the stage), so the exponent below is
+      // one FMA and one exp2 per score:
+      //   NONE     x = q.k                        sa = scale log2e, sb = 0
+      //   ALIBI    x = q.k scale / slope + (jl)   sa = slope log2e,
+      //            (jl = the key's offset in the    sb = slope log2e (j0 + 4g - i)
+      //            stage: a literal per register)
+      //   SOFTCAP  full stage: x = 1 / (e^{2 q.k scale / cap} + 1),
+      //            sa = -2 cap log2e, sb = cap log2e (cap tanh = cap - 2 cap x);
+      //            the row max is taken on q.k (tanh is increasing) before x is
+      //            formed. Masked stage: x = s2 itself (sa = 1, sb = 0).
+      // Key of (jt, r): j0 + 4g + 32jt + 8(r/4) + r%4; masked keys get x =
+      // -inf before the max (p = 0).
+      float sa, sb;
+      float mx4[4] = {FA_NEG_INF, FA_NEG_INF, FA_NEG_INF, FA_NEG_INF};
+      // max of this lane's 32 values (four independent chains); the lane
+      // ^ 32 holds the row's other keys, exchanged by row_pair_max once the
+      // value is in a form both lanes share
+      auto lane_max = [&]() -> float {
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float b = __builtin_fmaf(sc.slope2, static_cast<float>(32 * jt + 8 * (r >> 2) + (r & 3)), bias0);
-            s[jt][r] = __builtin_fmaf(s[jt][r], sc.c, b);
-          }
-      } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
-        // cap * tanh(x) * log2e with tanh x = 1 - 2 / (e^{2x} + 1)
-        const float k2 = 2.0f * sc.cap_in * kLog2e;
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = exp2_hw(s[jt][r] * k2);
-            const float t = __builtin_amdgcn_rcpf(e + 1.0f);
-            s[jt][r] = __builtin_fmaf(-2.0f * sc.cap_out, t, sc.cap_out);
-          }
-      }
-
-      // ---- mask_mod on partial and sequence-tail blocks only. Every built-in
-      // mask bounds a row's keys to an interval (causal: j <= i, sliding
-      // window: i - W < j <= i, local window: |i - j| < W, and j < kv_len),
-      // so the test is one unsigned compare of the key's offset in the
-      // interval against its length, plus the document-id equality for
-      // document masks.
-      if (masked) {
+          for (int r = 0; r < 8; ++r) mx4[c] = __builtin_fmaxf(mx4[c], s[c >> 1][8 * (c & 1) + r]);
+        return __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
+      };
+      auto apply_mask = [&]() {
         const int lo = lo_abs - (j0 + 4 * g);  // interval start, lane-relative
         if constexpr (doc_mask) {
 #pragma unroll
@@ -566,18 +562,57 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
               s[jt][r] = static_cast<unsigned>(jl - lo) < span ? s[jt][r] : FA_NEG_INF;
             }
         }
+      };
+      float mx;  // row max in the log2 domain
+      if constexpr (SCORE == FA_SCORE_ALIBI) {
+        sa = sc.slope2;
+        sb = sc.slope2 * static_cast<float>(j0 + 4 * g - i);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[jt][r] = __builtin_fmaf(s[jt][r], sc.c_over_slope2,
+                                      static_cast<float>(32 * jt + 8 * (r >> 2) + (r & 3)));
+        if (masked) apply_mask();
+        // (sb differs between the two halves of the row: exchange in the
+        // log2 domain; -inf stays -inf)
+        mx = row_pair_max(__builtin_fmaf(lane_max(), sa, sb));
+      } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
+        const float k2 = 2.0f * sc.cap_in * kLog2e;
+        if (!masked) {
+          const float mraw = row_pair_max(lane_max());
+          mx = mraw == FA_NEG_INF
+                   ? FA_NEG_INF
+                   : __builtin_fmaf(-2.0f * sc.cap_out,
+                                    __builtin_amdgcn_rcpf(exp2_hw(mraw * k2) + 1.0f), sc.cap_out);
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              s[jt][r] = __builtin_amdgcn_rcpf(exp2_hw(s[jt][r] * k2) + 1.0f);
+          sa = -2.0f * sc.cap_out;
+          sb = sc.cap_out;
+        } else {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float t = __builtin_amdgcn_rcpf(exp2_hw(s[jt][r] * k2) + 1.0f);
+              s[jt][r] = __builtin_fmaf(-2.0f * sc.cap_out, t, sc.cap_out);
+            }
+          apply_mask();
+          mx = row_pair_max(lane_max());
+          sa = 1.0f;
+          sb = 0.0f;
+        }
+      } else {
+        if (masked) apply_mask();
+        mx = row_pair_max(lane_max()) * sc.c;  // raw -> log2 domain
+        sa = sc.c;
+        sb = 0.0f;
       }
 
-      // ---- online softmax. Row max: four independent chains, then the
-      // exchange with lane ^ 32 (the other half of the row's keys).
-      float mx4[4] = {FA_NEG_INF, FA_NEG_INF, FA_NEG_INF, FA_NEG_INF};
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) mx4[c] = __builtin_fmaxf(mx4[c], s[c >> 1][8 * (c & 1) + r]);
-      float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
-      mx = row_pair_max(mx);
-      if constexpr (SCORE == FA_SCORE_NONE) mx *= sc.c;  // raw -> log2 domain
+      // ---- online softmax: lazy rescale, then p = exp2(s2 - m_ref)
       const bool raise = mx > m_run + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(raise)) {
         const float m_new = raise ? mx : m_run;
@@ -589,19 +624,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
         m_run = m_new;
       }
       const float m_use = (m_run == FA_NEG_INF) ? 0.0f : m_run;
+      const float ofs = sb - m_use;
       bf16x8 pb[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         f32x8 pf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = s[kk >> 1][(kk & 1) * 8 + e];
-          if constexpr (SCORE == FA_SCORE_NONE) {
-            pf[e] = exp2_hw(__builtin_fmaf(x, sc.c, -m_use));
-          } else {
-            pf[e] = exp2_hw(x - m_use);
-          }
-        }
+        for (int e = 0; e < 8; ++e)
+          pf[e] = exp2_hw(__builtin_fmaf(s[kk >> 1][(kk & 1) * 8 + e], sa, ofs));
         pb[kk] = __builtin_convertvector(pf, bf16x8);
         const u32x4 pw = __builtin_bit_cast(u32x4, pb[kk]);
 #pragma unroll

@@ -44,10 +44,11 @@ __device__ __forceinline__ float tanh_def(float x) {
 //   ALIBI    s2 = (raw * scale - slope_h * (i - j)) * log2e
 //   SOFTCAP  s2 = cap * tanh(raw * scale / cap) * log2e
 struct ScoreConsts {
-  float c;        // scale * log2e
-  float slope2;   // slope_h * log2e
-  float cap_in;   // scale / cap
-  float cap_out;  // cap * log2e
+  float c;              // scale * log2e
+  float slope2;         // slope_h * log2e
+  float c_over_slope2;  // scale / slope_h
+  float cap_in;         // scale / cap
+  float cap_out;        // cap * log2e
 };
 
 template <class Params>
@@ -55,7 +56,9 @@ __device__ __forceinline__ ScoreConsts make_score_consts(const Params& p, int h)
   ScoreConsts k;
   k.c = p.scale * kLog2e;
   // slope_h = 2^(-8 (h + 1) / H)
-  k.slope2 = exp2_hw(-8.0f * static_cast<float>(h + 1) / static_cast<float>(p.H)) * kLog2e;
+  const float slope = exp2_hw(-8.0f * static_cast<float>(h + 1) / static_cast<float>(p.H));
+  k.slope2 = slope * kLog2e;
+  k.c_over_slope2 = p.scale / slope;
   k.cap_in = p.score_kind == FA_SCORE_SOFTCAP ? p.scale / p.softcap : 0.0f;
   k.cap_out = p.score_kind == FA_SCORE_SOFTCAP ? p.softcap * kLog2e : 0.0f;
   return k;
