@@ -41,10 +41,16 @@ SOURCES = [
 # accumulator sets and their operands live at one wave per SIMD; LLVM's
 # iterative ILP scheduler keeps their LDS reads ahead of the MFMAs that use
 # them where the default scheduler serialises read, wait and MFMA (measured:
-# about 20% less time for the dK / dV kernel).
+# about 20% less time for the dK / dV kernel). VGPR-form MFMAs: left to its
+# heuristic, the compiler gives every MFMA of the dK / dV kernel accumulation
+# registers (AGPRs), so the S and dP tiles that the VALU works on are copied
+# out of them each stage (64 moves per stage); in VGPR form they stay put and
+# the resident K^T and V^T operands move to AGPRs, which MFMA reads directly.
+BWD_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
+             "-mllvm", "--amdgpu-mfma-vgpr-form"]
 EXTRA_FLAGS = {
-    "bwd_bf16_d64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-    "bwd_bf16_d128.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+    "bwd_bf16_d64.hip": BWD_FLAGS,
+    "bwd_bf16_d128.hip": BWD_FLAGS,
 }
 
 ARCH = "gfx950"

@@ -38,8 +38,9 @@ namespace fa {
 
 // Workgroup -> (batch, key head, key block) for the dK / dV kernel: dealt to
 // the 8 XCDs in contiguous ranges (one head's blocks share an L2).
-__device__ __forceinline__ bool xcd_kv_item(const FwdLaunch& p, int nsplit, int& b, int& hk,
-                                            int& n, int& c) {
+template <class Params>
+__device__ __forceinline__ bool xcd_kv_item(const Params& p, int nsplit, int& b, int& hk, int& n,
+                                            int& c) {
   const int total = p.B * p.H_kv * p.nkvb * nsplit;
   const int per_xcd = (total + 7) >> 3;
   const int wg = blockIdx.x;
@@ -428,9 +429,20 @@ __global__ __launch_bounds__(BQ * 2, 256 / BQ) void bwd_dq_kernel(const BwdLaunc
 }
 
 // ------------------------------------------------------------- dK, dV
+// The kernel's BwdLaunch argument read from the kernel argument segment
+// through a pointer the compiler cannot see through: fields used once per
+// stage are fresh scalar loads (scalar cache hits) instead of values held in
+// scalar registers across the stage loop, which at one wave per SIMD with
+// the accumulators resident would otherwise spill.
+typedef const __attribute__((address_space(4))) BwdLaunch KBArgs;
+__device__ __forceinline__ KBArgs& kbargs() {
+  KBArgs* q = (KBArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(q));
+  return *q;
+}
+
 template <int D, int BQ, int BK, int SCORE>
 __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp) {
-  const FwdLaunch& p = bp.f;
   constexpr int NW = BK / 32;
   constexpr int NT = NW * 64;
   constexpr int SPB = BQ / kStageKeys;  // 64-row query stages per query block
@@ -441,90 +453,89 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
   constexpr int ROUNDS = STAGE_BYTES / (NT * 16);
   constexpr int DK = D / 16;
   constexpr int DT = D / 32;
-
-  __shared__ __attribute__((aligned(1024))) char sQ0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sO0[STAGE_BYTES];  // dO
-  __shared__ __attribute__((aligned(1024))) char sQ1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char sO1[STAGE_BYTES];
-  // per query row of the stage: LSE, delta, document id
-  __shared__ __attribute__((aligned(16))) float sL0[kStageKeys], sL1[kStageKeys];
-  __shared__ __attribute__((aligned(16))) float sE0[kStageKeys], sE1[kStageKeys];
-  __shared__ __attribute__((aligned(16))) int sD0[kStageKeys], sD1[kStageKeys];
+  // one LDS array: per buffer Q and dO tiles, then per query row of the
+  // stage its exponent offset, delta and document id
+  constexpr int OFF_Q = 0, OFF_O = STAGE_BYTES, OFF_L = 2 * STAGE_BYTES;
+  constexpr int OFF_E = OFF_L + kStageKeys * 4, OFF_D = OFF_E + kStageKeys * 4;
+  constexpr int BUF = OFF_D + kStageKeys * 4;
+  constexpr int BUF1 = (BUF + 1023) / 1024 * 1024;  // second buffer, 1 KB aligned
+  __shared__ __attribute__((aligned(1024))) char smem[BUF1 + BUF];
 
   int b, hk, n, c;
-  const int nsplit = bp.kv_splits;
-  if (!xcd_kv_item(p, nsplit, b, hk, n, c)) return;
+  if (!xcd_kv_item(kbargs().f, kbargs().kv_splits, b, hk, n, c)) return;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lq = lane & 31;
   const int g = lane >> 5;
-  const int group = p.H / p.H_kv;
 
-  const int q_len = p.q_len;
-  const int kv_len = p.kv_len;
-  const int j = n * BK + wave * 32 + lq;  // this lane's key
-  const bool j_ok = j < kv_len;
-  const int mkind = p.mask.kind;
-  const int window = p.mask.window;
-  const int* doc = p.mask.doc_id + static_cast<int64_t>(b) * p.mask.doc_stride;
-  const bool doc_mask = mkind == FA_MASK_DOCUMENT;
-  const int dj = doc_mask ? doc[j_ok ? j : 0] : 0;
-
-  // K^T and V^T as MFMA B operands: column = key lq, k slots d in [16dk + 8g, +8)
-  bf16x8 kf[DK], vf[DK];
+  int j, dj;  // this lane's key and its document id
+  bool j_ok;
+  unsigned ispan;
+  int ilo;
+  bf16x8 kf[DK], vf[DK];  // K^T and V^T as MFMA B operands
+  int64_t qstride;
   {
-    const __bf16* kr = static_cast<const __bf16*>(p.k) + b * p.ks[0] + hk * p.ks[1] +
-                       static_cast<int64_t>(j_ok ? j : 0) * p.ks[2];
-    const __bf16* vr = static_cast<const __bf16*>(p.v) + b * p.vs[0] + hk * p.vs[1] +
-                       static_cast<int64_t>(j_ok ? j : 0) * p.vs[2];
+    KBArgs& P = kbargs();
+    const int kv_len = P.f.kv_len, q_len = P.f.q_len;
+    j = n * BK + wave * 32 + lq;
+    j_ok = j < kv_len;
+    const int mkind = P.f.mask.kind;
+    const int window = P.f.mask.window;
+    dj = mkind == FA_MASK_DOCUMENT
+             ? P.f.mask.doc_id[static_cast<int64_t>(b) * P.f.mask.doc_stride + (j_ok ? j : 0)]
+             : 0;
+    // column = key lq, k slots d in [16dk + 8g, +8)
+    const __bf16* kr = static_cast<const __bf16*>(P.f.k) + b * P.f.ks[0] + hk * P.f.ks[1] +
+                       static_cast<int64_t>(j_ok ? j : 0) * P.f.ks[2];
+    const __bf16* vr = static_cast<const __bf16*>(P.f.v) + b * P.f.vs[0] + hk * P.f.vs[1] +
+                       static_cast<int64_t>(j_ok ? j : 0) * P.f.vs[2];
 #pragma unroll
     for (int dk = 0; dk < DK; ++dk) {
       const u32x4 z = {0u, 0u, 0u, 0u};
       kf[dk] = __builtin_bit_cast(bf16x8, j_ok ? *reinterpret_cast<const u32x4*>(kr + dk * 16 + g * 8) : z);
       vf[dk] = __builtin_bit_cast(bf16x8, j_ok ? *reinterpret_cast<const u32x4*>(vr + dk * 16 + g * 8) : z);
     }
+    // mask_mod as an interval of query rows per key: i in [ilo, ilo + ispan)
+    // (the end of the sequence is part of the interval)
+    const int ihi =
+        !j_ok ? 0
+        : mkind == FA_MASK_SLIDING_WINDOW || mkind == FA_MASK_LOCAL_WINDOW
+            ? static_cast<int>(min(static_cast<int64_t>(j) + window, static_cast<int64_t>(q_len)))
+            : q_len;
+    ilo = mkind == FA_MASK_LOCAL_WINDOW
+              ? static_cast<int>(max(static_cast<int64_t>(j) - window + 1, static_cast<int64_t>(0)))
+          : mkind == FA_MASK_NONE ? 0
+                                  : j;
+    ispan = static_cast<unsigned>(max(ihi - ilo, 0));
+    qstride = P.f.qs[2] * 2;  // bytes
   }
 
-  // mask_mod as an interval of query rows per key: i in [ilo, ilo + ispan)
-  const int ihi =
-      !j_ok ? 0
-      : mkind == FA_MASK_NONE ? q_len
-      : mkind == FA_MASK_SLIDING_WINDOW || mkind == FA_MASK_LOCAL_WINDOW
-          ? static_cast<int>(min(static_cast<int64_t>(j) + window, static_cast<int64_t>(q_len)))
-          : q_len;
-  const int ilo = mkind == FA_MASK_LOCAL_WINDOW
-                      ? static_cast<int>(max(static_cast<int64_t>(j) - window + 1, static_cast<int64_t>(0)))
-                      : mkind == FA_MASK_NONE ? 0 : j;
-  const unsigned ispan = static_cast<unsigned>(max(ihi - ilo, 0));
-
-  int k_rd[DK];  // row lq (+32 jt) of a Q / dO tile as the A operand
+  int k_rd[DK];  // row lq (+32 it) of a Q / dO tile as the A operand
   {
-    const int s = kv_swizzle<D>(lq);
+    const int sw = kv_swizzle<D>(lq);
 #pragma unroll
-    for (int dk = 0; dk < DK; ++dk) k_rd[dk] = lq * RB + (((2 * dk + g) ^ s) << 4);
+    for (int dk = 0; dk < DK; ++dk) k_rd[dk] = lq * RB + (((2 * dk + g) ^ sw) << 4);
   }
   int v_rd[2][DT];  // transposed reads of a Q / dO tile
 #pragma unroll
   for (int t2 = 0; t2 < 2; ++t2) {
     const int r = 8 * t2 + 4 * g + ((lane & 15) >> 2);
-    const int s = kv_swizzle<D>(r);
+    const int sw = kv_swizzle<D>(r);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const int d = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-      v_rd[t2][dt] = r * RB + (((d >> 3) ^ s) << 4) + ((d & 7) << 1);
+      v_rd[t2][dt] = r * RB + (((d >> 3) ^ sw) << 4) + ((d & 7) << 1);
     }
   }
-  const int64_t qstride = p.qs[2] * 2;  // bytes
-  const int64_t ostride = static_cast<int64_t>(D) * 2;
   uint32_t dma_q[ROUNDS], dma_o[ROUNDS];
 #pragma unroll
   for (int rd = 0; rd < ROUNDS; ++rd) {
     const int r = (rd * NW + wave) * RPK + lane / CPR;
     const uint32_t col = static_cast<uint32_t>(((lane % CPR) ^ kv_swizzle<D>(r)) * 16);
     dma_q[rd] = static_cast<uint32_t>(r * qstride) + col;
-    dma_o[rd] = static_cast<uint32_t>(r * ostride) + col;
+    dma_o[rd] = static_cast<uint32_t>(r * (D * 2)) + col;
   }
 
   f32x16 dk[DT], dv[DT];
@@ -533,90 +544,84 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
-
-  const int bb = p.Bm == 1 ? 0 : b;
-  const int nqb = p.nqb;
-  const int nkvb = p.nkvb;
   __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): setup loads landed
 
-  // The stages of every query head of the group form one flat sequence
-  // (head by head; per head its partial list, then its full list; a query
-  // block's 64-row stages in order), walked by one loop so that the dK / dV
-  // accumulators stay in place across heads.
-  auto head_lists = [&](int gi, int& np, int& nf, const const_i32*& pl, const const_i32*& fl) {
-    const int hh = p.Hm == 1 ? 0 : hk * group + gi;
-    const int64_t col = (static_cast<int64_t>(bb) * p.Hm + hh) * nkvb + n;
-    np = min(max(((const const_i32*)bp.qnum)[col], 0), nqb);
-    nf = bp.fqnum ? min(max(((const const_i32*)bp.fqnum)[col], 0), nqb) : 0;
-    pl = (const const_i32*)(bp.qidx + col * nqb);
-    fl = (const const_i32*)(bp.fqidx ? bp.fqidx + col * nqb : bp.qidx);
+  // The block visits of every query head of the group form one flat
+  // sequence (head by head; per head its partial list, then its full list),
+  // walked by one loop so that the dK / dV accumulators stay in place across
+  // heads; a visit is SPB 64-row stages. Cursor: head cg of the group, its
+  // list counts, the next visit of that head.
+  int cg = -1, c_np = 0, c_nf = 0, c_it = 0;
+  auto head_counts = [&](int gi, int& np, int& nf) {
+    KBArgs& P = kbargs();
+    const int group = P.f.H / P.f.H_kv;
+    const int hh = P.f.Hm == 1 ? 0 : hk * group + gi;
+    const int64_t col = (static_cast<int64_t>(P.f.Bm == 1 ? 0 : b) * P.f.Hm + hh) * P.f.nkvb + n;
+    np = min(max(((const const_i32*)P.qnum)[col], 0), P.f.nqb);
+    nf = P.fqnum ? min(max(((const const_i32*)P.fqnum)[col], 0), P.f.nqb) : 0;
   };
-  int all_blocks = 0;
-  for (int gi = 0; gi < group; ++gi) {
-    int np, nf;
-    const const_i32 *pl, *fl;
-    head_lists(gi, np, nf, pl, fl);
-    all_blocks += np + nf;
-  }
-  // part c of nsplit: block visits [v0, v0 + nvis) of the sequence
-  const int per_part = (all_blocks + nsplit - 1) / nsplit;
-  const int v0 = min(c * per_part, all_blocks);
-  const int total = min(per_part, all_blocks - v0) * SPB;
-
-  // cursor over the sequence: head cg, its lists, the next block visit
-  int cg = -1, c_np = 0, c_nf = 0, c_left = 0, c_it = 0, c_sub = 0, c_m = -1;
-  const const_i32* c_pl = nullptr;
-  const const_i32* c_fl = nullptr;
-  // skip the visits of the earlier parts (whole blocks: c_sub stays 0)
+  int total;  // stages of this part
   {
-    int skip = v0 * SPB;
+    KBArgs& P = kbargs();
+    const int group = P.f.H / P.f.H_kv;
+    const int nsplit = P.kv_splits;
+    int all_blocks = 0;
+    for (int gi = 0; gi < group; ++gi) {
+      int np, nf;
+      head_counts(gi, np, nf);
+      all_blocks += np + nf;
+    }
+    // part c of nsplit: block visits [v0, v0 + nvis) of the sequence
+    const int per_part = (all_blocks + nsplit - 1) / nsplit;
+    const int v0 = min(c * per_part, all_blocks);
+    total = min(per_part, all_blocks - v0) * SPB;
+    // skip the visits of the earlier parts
+    int skip = v0;
     while (skip > 0) {
-      if (c_left == 0) {
+      if (c_it == c_np + c_nf) {
         ++cg;
-        head_lists(cg, c_np, c_nf, c_pl, c_fl);
-        c_left = (c_np + c_nf) * SPB;
+        head_counts(cg, c_np, c_nf);
         c_it = 0;
         continue;
       }
-      const int t = min(skip, c_left);
+      const int t = min(skip, c_np + c_nf - c_it);
       skip -= t;
-      c_left -= t;
-      c_it += t / SPB;
+      c_it += t;
     }
   }
-  // the next stage: query block m (-1: an index outside [0, NQB), skipped),
-  // head h, 64-row stage sub of the block, and whether mask_mod applies.
-  // Called exactly `total` times, so a head with stages left always exists.
-  auto next_stage = [&](int& m, int& h, int& sub, bool& masked) {
-    while (c_left == 0) {
+  // the next visit: query block m (-1: an index outside [0, NQB), skipped),
+  // head h, and whether mask_mod applies. Called once per visit, so a head
+  // with visits left always exists.
+  auto next_visit = [&](int& m, int& h, bool& masked) {
+    while (c_it == c_np + c_nf) {
       ++cg;
-      head_lists(cg, c_np, c_nf, c_pl, c_fl);
-      c_left = (c_np + c_nf) * SPB;
+      head_counts(cg, c_np, c_nf);
       c_it = 0;
-      c_sub = 0;
     }
-    if (c_sub == 0) {
-      const int mm = c_it < c_np ? c_pl[c_it] : c_fl[c_it - c_np];
-      c_m = static_cast<unsigned>(mm) < static_cast<unsigned>(nqb) ? mm : -1;
-    }
-    m = c_m;
+    KBArgs& P = kbargs();
+    const int group = P.f.H / P.f.H_kv;
+    const int nqb = P.f.nqb;
+    const int hh = P.f.Hm == 1 ? 0 : hk * group + cg;
+    const int64_t col = (static_cast<int64_t>(P.f.Bm == 1 ? 0 : b) * P.f.Hm + hh) * P.f.nkvb + n;
+    const bool part = c_it < c_np;
+    const int mm = part ? ((const const_i32*)P.qidx)[col * nqb + c_it]
+                        : ((const const_i32*)P.fqidx)[col * nqb + c_it - c_np];
+    m = static_cast<unsigned>(mm) < static_cast<unsigned>(nqb) ? mm : -1;
     h = hk * group + cg;
-    sub = c_sub;
-    masked = c_it < c_np || (c_m + 1) * BQ > q_len || (n + 1) * BK > kv_len;
-    if (++c_sub == SPB) {
-      c_sub = 0;
-      ++c_it;
-    }
-    --c_left;
+    masked = part || (m + 1) * BQ > P.f.q_len || (n + 1) * BK > P.f.kv_len;
+    ++c_it;
   };
 
-  auto issue = [&](int m, int h, int sub, char* sQ, char* sO, float* sL, float* sE, int* sD) {
+  // DMA of stage (m, h, sub) into the buffer at LDS byte offset `buf`
+  auto issue = [&](int m, int h, int sub, int buf, bool masked) {
     if (m < 0) return;
+    KBArgs& P = kbargs();
+    const int q_len = P.f.q_len;
     const char* qbase = reinterpret_cast<const char*>(
-        static_cast<const __bf16*>(p.q) + b * p.qs[0] + h * p.qs[1]);
-    const int64_t rowbase = (static_cast<int64_t>(b) * p.H + h) * q_len;  // dO, LSE, delta
+        static_cast<const __bf16*>(P.f.q) + b * P.f.qs[0] + h * P.f.qs[1]);
+    const int64_t rowbase = (static_cast<int64_t>(b) * P.f.H + h) * q_len;  // dO, LSE, delta
     const char* obase =
-        reinterpret_cast<const char*>(static_cast<const __bf16*>(bp.dout) + rowbase * D);
+        reinterpret_cast<const char*>(static_cast<const __bf16*>(P.dout) + rowbase * D);
     const int i0 = m * BQ + sub * kStageKeys;
     const int rows_left = q_len - i0;
     const int qrec = rows_left >= kStageKeys ? 0x7fffffff
@@ -624,27 +629,34 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
                                             : (rows_left - 1) * static_cast<int>(qstride) + RB;
     const int orec = rows_left >= kStageKeys ? 0x7fffffff
                      : rows_left <= 0       ? 0
-                                            : (rows_left - 1) * static_cast<int>(ostride) + RB;
+                                            : (rows_left - 1) * (D * 2) + RB;
     const hw::i32x4 qr = hw::make_rsrc(qbase + (rows_left > 0 ? i0 * qstride : 0), qrec);
-    const hw::i32x4 orr = hw::make_rsrc(obase + (rows_left > 0 ? i0 * ostride : 0), orec);
+    const hw::i32x4 orr = hw::make_rsrc(obase + (rows_left > 0 ? static_cast<int64_t>(i0) * (D * 2) : 0), orec);
+    const uint32_t lb = hw::opaque_u32(hw::lds_addr(smem) + buf) + wave * 1024;
 #pragma unroll
     for (int rd = 0; rd < ROUNDS; ++rd) {
-      const int seg = (rd * NW + wave) * 1024;
-      hw::dma_tile16(qr, hw::lds_addr(sQ + seg), dma_q[rd], 0);
-      hw::dma_tile16(orr, hw::lds_addr(sO + seg), dma_o[rd], 0);
+      hw::dma_tile16(qr, lb + OFF_Q + rd * NW * 1024, dma_q[rd], 0);
+      hw::dma_tile16(orr, lb + OFF_O + rd * NW * 1024, dma_o[rd], 0);
     }
     if (wave == 0) {
+      const uint32_t lr = hw::opaque_u32(hw::lds_addr(smem) + buf);
       const uint32_t r4 = static_cast<uint32_t>(min(i0 + lane, q_len - 1)) * 4;
-      hw::dma_dword(reinterpret_cast<const int*>(bp.rowterm + rowbase), hw::lds_addr(sL), r4);
-      hw::dma_dword(reinterpret_cast<const int*>(bp.delta + rowbase), hw::lds_addr(sE), r4);
-      if (doc_mask) hw::dma_dword(doc, hw::lds_addr(sD), r4);
+      hw::dma_dword(reinterpret_cast<const int*>(P.rowterm + rowbase), lr + OFF_L, r4);
+      hw::dma_dword(reinterpret_cast<const int*>(P.delta + rowbase), lr + OFF_E, r4);
+      if (masked && P.f.mask.kind == FA_MASK_DOCUMENT)
+        hw::dma_dword(P.f.mask.doc_id + static_cast<int64_t>(b) * P.f.mask.doc_stride,
+                      lr + OFF_D, r4);
     }
   };
 
-  auto compute = [&](int m, int h, int sub, bool masked, const char* sQ, const char* sO,
-                     const float* sL, const float* sE, const int* sD) {
+  auto compute = [&](int m, int h, int sub, bool masked, const char* sB) {
     if (m < 0) return;
-    const ScoreConsts sc = make_score_consts(p, h);
+    const char* sQ = sB + OFF_Q;
+    const char* sO = sB + OFF_O;
+    const float* sL = reinterpret_cast<const float*>(sB + OFF_L);
+    const float* sE = reinterpret_cast<const float*>(sB + OFF_E);
+    const int* sD = reinterpret_cast<const int*>(sB + OFF_D);
+    const ScoreConsts sc = make_score_consts(kbargs().f, h);
     const int i0 = m * BQ + sub * kStageKeys;
 
     // Two halves of 32 query rows each (it), one after the other: the
@@ -672,37 +684,55 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
       // row's exponent offset (rowterm, from the dQ kernel) folds in -LSE
       // and ALiBi's row part; the key part of ALiBi is tj.
       const float tj = SCORE == FA_SCORE_ALIBI ? sc.slope2 * static_cast<float>(j) : 0.0f;
+      float fp[16];  // score_mod' (soft-cap), else 1
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int il = 32 * it + 8 * r4 + 4 * g;  // first of 4 consecutive rows
         const f32x4 rt4 = *reinterpret_cast<const f32x4*>(sL + il);
-        const f32x4 del4 = *reinterpret_cast<const f32x4*>(sE + il);
-        int4 d4 = {dj, dj, dj, dj};
-        if (doc_mask && masked) d4 = *reinterpret_cast<const int4*>(sD + il);
-        const int dqs[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int r = 4 * r4 + c;
-          float arg, fp = 1.0f;
+        for (int cc = 0; cc < 4; ++cc) {
+          const int r = 4 * r4 + cc;
+          float arg;
+          fp[r] = 1.0f;
           if constexpr (SCORE == FA_SCORE_ALIBI) {
-            arg = __builtin_fmaf(s[r], sc.c, rt4[c] + tj);
+            arg = __builtin_fmaf(s[r], sc.c, rt4[cc] + tj);
           } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
             const float e = exp2_hw(s[r] * (2.0f * sc.cap_in * kLog2e));
             const float tt = __builtin_amdgcn_rcpf(e + 1.0f);
-            arg = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out + rt4[c]);
-            fp = 4.0f * tt * (1.0f - tt);
+            arg = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out + rt4[cc]);
+            fp[r] = 4.0f * tt * (1.0f - tt);
           } else {
-            arg = __builtin_fmaf(s[r], sc.c, rt4[c]);
+            arg = __builtin_fmaf(s[r], sc.c, rt4[cc]);
           }
-          float pr = exp2_hw(arg);
-          if (masked) {
-            const int irow = i0 + il + c;
+          s[r] = exp2_hw(arg);  // P
+        }
+      }
+      // mask_mod on partial and tail stages only (a uniform branch)
+      if (masked) {
+        const int q_len = kbargs().f.q_len;
+        const bool doc_mask = kbargs().f.mask.kind == FA_MASK_DOCUMENT;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int il = 32 * it + 8 * r4 + 4 * g;
+          int4 d4 = {dj, dj, dj, dj};
+          if (doc_mask) d4 = *reinterpret_cast<const int4*>(sD + il);
+          const int dqs[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc) {
+            const int irow = i0 + il + cc;
             const bool ok =
-                (static_cast<unsigned>(irow - ilo) < ispan) & (dqs[c] == dj) & (irow < q_len);
-            pr = ok ? pr : 0.0f;
+                (static_cast<unsigned>(irow - ilo) < ispan) & (dqs[cc] == dj) & (irow < q_len);
+            s[4 * r4 + cc] = ok ? s[4 * r4 + cc] : 0.0f;
           }
-          s[r] = pr;                                  // P
-          dpm[r] = pr * (dpm[r] - del4[c]) * fp;      // dT
+        }
+      }
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 del4 = *reinterpret_cast<const f32x4*>(sE + 32 * it + 8 * r4 + 4 * g);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          const int r = 4 * r4 + cc;
+          dpm[r] = s[r] * (dpm[r] - del4[cc]) * fp[r];  // dT
         }
       }
       bf16x8 pb[2], tb[2];
@@ -744,20 +774,33 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
     }
   };
 
+  // Stage loop, unrolled by two so that each LDS buffer is addressed with
+  // constant offsets; the DMA of stage st + 1 overlaps the compute of stage
+  // st. (m, h, masked): the visit of the stage; sub: its 64-row part.
+  int c_m = -1, c_h = 0, c_sub = 0;
+  bool c_mk = false;
+  auto next_stage = [&](int& m, int& h, int& sub, bool& masked) {
+    if (c_sub == 0) next_visit(c_m, c_h, c_mk);
+    m = c_m;
+    h = c_h;
+    sub = c_sub;
+    masked = c_mk;
+    if (++c_sub == SPB) c_sub = 0;
+  };
   int m_cur = -1, h_cur = 0, sub_cur = 0, m_nxt = -1, h_nxt = 0, sub_nxt = 0;
   bool mk_cur = false, mk_nxt = false;
   if (total > 0) {
     next_stage(m_cur, h_cur, sub_cur, mk_cur);
-    issue(m_cur, h_cur, sub_cur, sQ0, sO0, sL0, sE0, sD0);
+    issue(m_cur, h_cur, sub_cur, 0, mk_cur);
   }
   for (int st = 0; st < total; st += 2) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this lane's DMA landed
     __syncthreads();                     // every lane's DMA landed; buffer 1 free
     if (st + 1 < total) {
       next_stage(m_nxt, h_nxt, sub_nxt, mk_nxt);
-      issue(m_nxt, h_nxt, sub_nxt, sQ1, sO1, sL1, sE1, sD1);
+      issue(m_nxt, h_nxt, sub_nxt, BUF1, mk_nxt);
     }
-    compute(m_cur, h_cur, sub_cur, mk_cur, sQ0, sO0, sL0, sE0, sD0);
+    compute(m_cur, h_cur, sub_cur, mk_cur, smem);
     if (st + 1 >= total) break;
     m_cur = m_nxt;
     h_cur = h_nxt;
@@ -767,21 +810,23 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
     __syncthreads();
     if (st + 2 < total) {
       next_stage(m_nxt, h_nxt, sub_nxt, mk_nxt);
-      issue(m_nxt, h_nxt, sub_nxt, sQ0, sO0, sL0, sE0, sD0);
+      issue(m_nxt, h_nxt, sub_nxt, 0, mk_nxt);
     }
-    compute(m_cur, h_cur, sub_cur, mk_cur, sQ1, sO1, sL1, sE1, sD1);
+    compute(m_cur, h_cur, sub_cur, mk_cur, smem + BUF1);
     m_cur = m_nxt;
     h_cur = h_nxt;
     sub_cur = sub_nxt;
     mk_cur = mk_nxt;
   }
 
-  if (j_ok && nsplit > 1) {
+  KBArgs& P = kbargs();
+  const int kv_len = P.f.kv_len;
+  if (j_ok && P.kv_splits > 1) {
     // this part's unscaled sums; the parts are added in order afterwards
-    const int64_t krow = (static_cast<int64_t>(b) * p.H_kv + hk) * kv_len + j;
-    const int64_t prow = static_cast<int64_t>(c) * p.B * p.H_kv * kv_len + krow;
-    float* pk = bp.part_dk + prow * D;
-    float* pv = bp.part_dv + prow * D;
+    const int64_t krow = (static_cast<int64_t>(b) * P.f.H_kv + hk) * kv_len + j;
+    const int64_t prow = static_cast<int64_t>(c) * P.f.B * P.f.H_kv * kv_len + krow;
+    float* pk = P.part_dk + prow * D;
+    float* pv = P.part_dv + prow * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -792,15 +837,16 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
             f32x4{dv[dt][4 * q4 + 0], dv[dt][4 * q4 + 1], dv[dt][4 * q4 + 2], dv[dt][4 * q4 + 3]};
       }
   } else if (j_ok) {
-    const int64_t krow = (static_cast<int64_t>(b) * p.H_kv + hk) * kv_len + j;
-    __bf16* outk = static_cast<__bf16*>(bp.dk) + krow * D;
-    __bf16* outv = static_cast<__bf16*>(bp.dv) + krow * D;
+    const int64_t krow = (static_cast<int64_t>(b) * P.f.H_kv + hk) * kv_len + j;
+    __bf16* outk = static_cast<__bf16*>(P.dk) + krow * D;
+    __bf16* outv = static_cast<__bf16*>(P.dv) + krow * D;
+    const float scale = P.f.scale;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 k4 = {dk[dt][4 * q4 + 0] * p.scale, dk[dt][4 * q4 + 1] * p.scale,
-                          dk[dt][4 * q4 + 2] * p.scale, dk[dt][4 * q4 + 3] * p.scale};
+        const f32x4 k4 = {dk[dt][4 * q4 + 0] * scale, dk[dt][4 * q4 + 1] * scale,
+                          dk[dt][4 * q4 + 2] * scale, dk[dt][4 * q4 + 3] * scale};
         const f32x4 v4 = {dv[dt][4 * q4 + 0], dv[dt][4 * q4 + 1], dv[dt][4 * q4 + 2],
                           dv[dt][4 * q4 + 3]};
         *reinterpret_cast<bf16x4*>(outk + dt * 32 + 8 * q4 + 4 * g) = __builtin_convertvector(k4, bf16x4);
