@@ -36,6 +36,11 @@
 
 namespace fa {
 
+// The soft-cap's derivative enters dT as t (1 - t) with t = 1 / (e^{2x} + 1),
+// which is (1 - tanh^2 x) / 4; the factor 4, a power of two, is applied to
+// the fp32 sums at the end (exact: scaling by 4 commutes with rounding).
+constexpr float kSoftcapGrad = 4.0f;
+
 // Workgroup -> (batch, key head, key block) for the dK / dV kernel: dealt to
 // the 8 XCDs in contiguous ranges (one head's blocks share an L2).
 template <class Params>
@@ -301,28 +306,35 @@ __global__ __launch_bounds__(BQ * 2, 256 / BQ) void bwd_dq_kernel(const BwdLaunc
                                                      dp, 0, 0, 0);
       }
 
-      // score_mod into the log2 domain and its derivative (soft-cap); key of
-      // element r: j0 + 32 jt + 8 (r / 4) + 4 g + r % 4
+      // P = 2^(score_mod in the log2 domain - LSE log2 e), with the row's
+      // LSE folded into the exponent's FMA, and score_mod' (soft-cap); key of
+      // element r: j0 + 32 jt + 8 (r / 4) + 4 g + r % 4. A row without keys
+      // has lse2 = +inf: every P is 0.
       float fp[16];
       // ALiBi bias slope2 (j - i) = bias0 + slope2 (8 (r / 4) + r % 4)
       const float bias0 =
-          SCORE == FA_SCORE_ALIBI ? sc.slope2 * static_cast<float>(j0 + 4 * g + 32 * jt - i) : 0.0f;
+          SCORE == FA_SCORE_ALIBI
+              ? sc.slope2 * static_cast<float>(j0 + 4 * g + 32 * jt - i) - lse2
+              : 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         fp[r] = 1.0f;
+        float arg;
         if constexpr (SCORE == FA_SCORE_ALIBI) {
           const float bj =
               __builtin_fmaf(sc.slope2, static_cast<float>(8 * (r >> 2) + (r & 3)), bias0);
-          s[r] = __builtin_fmaf(s[r], sc.c, bj);
+          arg = __builtin_fmaf(s[r], sc.c, bj);
         } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
           const float e = exp2_hw(s[r] * (2.0f * sc.cap_in * kLog2e));
           const float tt = __builtin_amdgcn_rcpf(e + 1.0f);  // tanh = 1 - 2 tt
-          s[r] = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out);
-          fp[r] = 4.0f * tt * (1.0f - tt);                   // 1 - tanh^2
+          arg = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out - lse2);
+          fp[r] = __builtin_fmaf(-tt, tt, tt);  // (1 - tanh^2) / 4
         } else {
-          s[r] *= sc.c;
+          arg = __builtin_fmaf(s[r], sc.c, -lse2);
         }
+        s[r] = exp2_hw(arg);
       }
+      // mask_mod on partial and tail stages only (a uniform branch)
       if (masked) {
         const int lo = lo_abs - (j0 + 4 * g);
 #pragma unroll
@@ -336,12 +348,12 @@ __global__ __launch_bounds__(BQ * 2, 256 / BQ) void bwd_dq_kernel(const BwdLaunc
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const bool ok = (static_cast<unsigned>(jl + c - lo) < span) & (dj[c] == di);
-            s[4 * r4 + c] = ok ? s[4 * r4 + c] : FA_NEG_INF;
+            s[4 * r4 + c] = ok ? s[4 * r4 + c] : 0.0f;
           }
         }
       }
 
-      // P, dS = P (dP - delta), dT = dS score_mod' -> bf16 B operands
+      // dS = P (dP - delta), dT = dS score_mod' -> bf16 B operands
       bf16x8 tb[2];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
@@ -349,8 +361,7 @@ __global__ __launch_bounds__(BQ * 2, 256 / BQ) void bwd_dq_kernel(const BwdLaunc
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = h2 * 8 + e;
-          const float pr = exp2_hw(s[r] - lse2);
-          tf[e] = pr * (dp[r] - delta_i) * fp[r];
+          tf[e] = s[r] * (dp[r] - delta_i) * fp[r];
         }
         tb[h2] = __builtin_convertvector(tf, bf16x8);
       }
@@ -406,23 +417,27 @@ __global__ __launch_bounds__(BQ * 2, 256 / BQ) void bwd_dq_kernel(const BwdLaunc
     mk_cur = mk_nxt;
   }
 
+  constexpr float gs = SCORE == FA_SCORE_SOFTCAP ? kSoftcapGrad : 1.0f;
   if (i_ok && p.nsplit > 1) {
-    // this part's unscaled sum; the parts are added in order afterwards
+    // this part's sum without the scale; the parts are added in order
+    // afterwards
     float* po = bp.part_dq + (static_cast<int64_t>(w.c) * p.B * p.H * p.q_len + orow) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
         *reinterpret_cast<f32x4*>(po + dt * 32 + 8 * q4 + 4 * g) =
-            f32x4{dq[dt][4 * q4 + 0], dq[dt][4 * q4 + 1], dq[dt][4 * q4 + 2], dq[dt][4 * q4 + 3]};
+            f32x4{dq[dt][4 * q4 + 0] * gs, dq[dt][4 * q4 + 1] * gs, dq[dt][4 * q4 + 2] * gs,
+                  dq[dt][4 * q4 + 3] * gs};
   } else if (i_ok) {
     __bf16* out = static_cast<__bf16*>(bp.dq) + orow * D;
+    const float sq = p.scale * gs;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v4 = {dq[dt][4 * q4 + 0] * p.scale, dq[dt][4 * q4 + 1] * p.scale,
-                          dq[dt][4 * q4 + 2] * p.scale, dq[dt][4 * q4 + 3] * p.scale};
+        const f32x4 v4 = {dq[dt][4 * q4 + 0] * sq, dq[dt][4 * q4 + 1] * sq,
+                          dq[dt][4 * q4 + 2] * sq, dq[dt][4 * q4 + 3] * sq};
         *reinterpret_cast<bf16x4*>(out + dt * 32 + 8 * q4 + 4 * g) = __builtin_convertvector(v4, bf16x4);
       }
   }
@@ -700,7 +715,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
             const float e = exp2_hw(s[r] * (2.0f * sc.cap_in * kLog2e));
             const float tt = __builtin_amdgcn_rcpf(e + 1.0f);
             arg = __builtin_fmaf(-2.0f * sc.cap_out, tt, sc.cap_out + rt4[cc]);
-            fp[r] = 4.0f * tt * (1.0f - tt);
+            fp[r] = __builtin_fmaf(-tt, tt, tt);  // (1 - tanh^2) / 4
           } else {
             arg = __builtin_fmaf(s[r], sc.c, rt4[cc]);
           }
@@ -821,8 +836,10 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
 
   KBArgs& P = kbargs();
   const int kv_len = P.f.kv_len;
+  constexpr float gs = SCORE == FA_SCORE_SOFTCAP ? kSoftcapGrad : 1.0f;
   if (j_ok && P.kv_splits > 1) {
-    // this part's unscaled sums; the parts are added in order afterwards
+    // this part's sums without the scale; the parts are added in order
+    // afterwards
     const int64_t krow = (static_cast<int64_t>(b) * P.f.H_kv + hk) * kv_len + j;
     const int64_t prow = static_cast<int64_t>(c) * P.f.B * P.f.H_kv * kv_len + krow;
     float* pk = P.part_dk + prow * D;
@@ -832,7 +849,8 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         *reinterpret_cast<f32x4*>(pk + dt * 32 + 8 * q4 + 4 * g) =
-            f32x4{dk[dt][4 * q4 + 0], dk[dt][4 * q4 + 1], dk[dt][4 * q4 + 2], dk[dt][4 * q4 + 3]};
+            f32x4{dk[dt][4 * q4 + 0] * gs, dk[dt][4 * q4 + 1] * gs, dk[dt][4 * q4 + 2] * gs,
+                  dk[dt][4 * q4 + 3] * gs};
         *reinterpret_cast<f32x4*>(pv + dt * 32 + 8 * q4 + 4 * g) =
             f32x4{dv[dt][4 * q4 + 0], dv[dt][4 * q4 + 1], dv[dt][4 * q4 + 2], dv[dt][4 * q4 + 3]};
       }
@@ -840,7 +858,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
     const int64_t krow = (static_cast<int64_t>(b) * P.f.H_kv + hk) * kv_len + j;
     __bf16* outk = static_cast<__bf16*>(P.dk) + krow * D;
     __bf16* outv = static_cast<__bf16*>(P.dv) + krow * D;
-    const float scale = P.f.scale;
+    const float scale = P.f.scale * gs;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
