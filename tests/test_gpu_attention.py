@@ -80,6 +80,35 @@ def test_small_full_rows(dtype, D, blk, mask, score):
                      f"{dtype} D={D} blk={blk} {mask} {score} sep={sep}")
 
 
+SERIES = []
+for D, blk in ((128, 128), (64, 128), (128, 64)):
+    for mask in ("causal", "document", "none", "sliding_window"):
+        SERIES.append((D, blk, mask))
+
+
+@pytest.mark.parametrize("D,blk,mask", SERIES)
+def test_softcap_large_cap(D, blk, mask):
+    # soft-cap 50 (the document workload's cap) at a small size: capped
+    # scores close to the raw ones on N(0, 1) data, and on the rows of the
+    # second query block, scaled by 3, well into the cap's curve; every row
+    # against the oracle
+    ql, kl = 3 * blk + 37, 3 * blk + 11
+    w = WL.Workload("small", "bf16", 2, 4, 2, ql, kl, D, mask, blk, blk,
+                    seed=0, window=2 * blk + 13 if "window" in mask else None,
+                    score="softcap", softcap=50.0)
+    rng = np.random.default_rng(zlib.crc32(f"series{D}{blk}{mask}".encode()))
+    doc = (np.sort(rng.integers(0, 3, max(ql, kl))).astype(np.int32)
+           if mask == "document" else None)
+    q, k, v = _inputs(w, 41)
+    q[:, :, blk:2 * blk] = (q[:, :, blk:2 * blk].float() * 3.0).to(q.dtype)
+    print(f"[fwd softcap 50] D={D} blk={blk} {mask}", flush=True)
+    o_ref, l_ref = oracle_case(q, k, v, w, doc)
+    for sep in (True, False):
+        o, lse = run_gpu(w, q, k, v, doc, sep=sep)
+        assert_close(o, lse, o_ref, l_ref, TOL["bf16"],
+                     f"softcap 50 D={D} blk={blk} {mask} sep={sep}")
+
+
 PAIRS = []
 for D in (128, 64):
     for bq, bk in ((128, 64), (64, 128)):
