@@ -76,3 +76,23 @@ def test_noalloc_refuses_more_than_its_scratch():
     st, _, _ = _noalloc(q, q, q, bm, None, 0.088, 64)
     assert st == C.FA_ERR_INVALID_VALUE
     assert b"scratch" in C.lib().fa_last_error()
+
+
+def test_noalloc_one_part_is_the_plain_forward():
+    # num_splits = 1 uses no scratch: the forward itself (D = 64, document
+    # mask with soft-cap), bitwise equal to flex_attention unsplit
+    w = WL.Workload("small", "bf16", 2, 4, 2, 700, 700, 64, "document", 128,
+                    128, seed=0, score="softcap", softcap=20.0)
+    rng = np.random.default_rng(5)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(DEV) for x in WL.draw_qkv(rng, w))
+    doc = torch.from_numpy(np.sort(rng.integers(0, 3, 700)).astype(np.int32)).to(DEV)
+    bm = fa.create_block_mask("document", None, None, 700, 700, device=DEV, doc_id=doc)
+    print("[noalloc] one part", flush=True)
+    st, o_n, l_n = _noalloc(q, k, v, bm,
+                            C.fa_score_mod(kind=C.FA_SCORE_SOFTCAP, softcap=20.0),
+                            w.scale, 1)
+    C.check(st, "fa_flex_attention_fwd_split_noalloc")
+    o_w, l_w = fa.flex_attention(q, k, v, bm, score_mod=("softcap", 20.0), scale=w.scale,
+                                 num_splits=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o_n, o_w) and torch.equal(l_n, l_w)
