@@ -32,6 +32,8 @@
 // an interval of query rows per key.
 #pragma once
 
+#include <type_traits>
+
 #include "fwd_bf16.hpp"
 
 namespace fa {
@@ -460,20 +462,30 @@ template <int D, int BQ, int BK, int SCORE>
 __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp) {
   constexpr int NW = BK / 32;
   constexpr int NT = NW * 64;
-  constexpr int SPB = BQ / kStageKeys;  // 64-row query stages per query block
+  // query rows per stage: the whole 128-row query block for 128-key
+  // workgroups (one per CU, so LDS holds two 64 KB stage buffers, and the
+  // per-stage fixed cost of DMA issue, list walk and barrier is paid once per
+  // 128 rows), else 64 (smaller workgroups keep two per CU)
+  constexpr int SR = BQ >= 128 && BK >= 128 ? 128 : kStageKeys;
+  constexpr int SPB = BQ / SR;  // stages per query block
   constexpr int RB = D * 2;
   constexpr int CPR = D / 8;
   constexpr int RPK = 1024 / RB;
-  constexpr int STAGE_BYTES = kStageKeys * RB;
+  constexpr int STAGE_BYTES = SR * RB;
   constexpr int ROUNDS = STAGE_BYTES / (NT * 16);
   constexpr int DK = D / 16;
   constexpr int DT = D / 32;
-  // one LDS array: per buffer Q and dO tiles, then per query row of the
-  // stage its exponent offset, delta and document id
-  constexpr int OFF_Q = 0, OFF_O = STAGE_BYTES, OFF_L = 2 * STAGE_BYTES;
-  constexpr int OFF_E = OFF_L + kStageKeys * 4, OFF_D = OFF_E + kStageKeys * 4;
-  constexpr int BUF = OFF_D + kStageKeys * 4;
+  // one LDS array: per buffer, per query row of the stage its exponent
+  // offset, delta and document id, then the Q and dO tiles (1 KB aligned).
+  // Every read of the first buffer is a lane offset plus an immediate below
+  // 64 KB (the ds_read offset field); with 128-row stages the second buffer
+  // lies beyond that and its lane offsets are formed once per stage.
+  constexpr int OFF_L = 0, OFF_E = SR * 4, OFF_D = 2 * SR * 4;
+  constexpr int OFF_Q = (3 * SR * 4 + 1023) / 1024 * 1024, OFF_O = OFF_Q + STAGE_BYTES;
+  constexpr int BUF = OFF_O + STAGE_BYTES;
   constexpr int BUF1 = (BUF + 1023) / 1024 * 1024;  // second buffer, 1 KB aligned
+  constexpr int MAX_IMM = OFF_O + (SR - 16) * RB;  // largest immediate of a tile read
+  static_assert(MAX_IMM < 65536, "first buffer's reads within the ds_read offset range");
   __shared__ __attribute__((aligned(1024))) char smem[BUF1 + BUF];
 
   int b, hk, n, c;
@@ -564,7 +576,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
   // The block visits of every query head of the group form one flat
   // sequence (head by head; per head its partial list, then its full list),
   // walked by one loop so that the dK / dV accumulators stay in place across
-  // heads; a visit is SPB 64-row stages. Cursor: head cg of the group, its
+  // heads; a visit is SPB stages of SR rows. Cursor: head cg of the group, its
   // list counts, the next visit of that head.
   int cg = -1, c_np = 0, c_nf = 0, c_it = 0;
   auto head_counts = [&](int gi, int& np, int& nf) {
@@ -637,12 +649,12 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
     const int64_t rowbase = (static_cast<int64_t>(b) * P.f.H + h) * q_len;  // dO, LSE, delta
     const char* obase =
         reinterpret_cast<const char*>(static_cast<const __bf16*>(P.dout) + rowbase * D);
-    const int i0 = m * BQ + sub * kStageKeys;
+    const int i0 = m * BQ + sub * SR;
     const int rows_left = q_len - i0;
-    const int qrec = rows_left >= kStageKeys ? 0x7fffffff
+    const int qrec = rows_left >= SR ? 0x7fffffff
                      : rows_left <= 0       ? 0
                                             : (rows_left - 1) * static_cast<int>(qstride) + RB;
-    const int orec = rows_left >= kStageKeys ? 0x7fffffff
+    const int orec = rows_left >= SR ? 0x7fffffff
                      : rows_left <= 0       ? 0
                                             : (rows_left - 1) * (D * 2) + RB;
     const hw::i32x4 qr = hw::make_rsrc(qbase + (rows_left > 0 ? i0 * qstride : 0), qrec);
@@ -653,9 +665,9 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
       hw::dma_tile16(qr, lb + OFF_Q + rd * NW * 1024, dma_q[rd], 0);
       hw::dma_tile16(orr, lb + OFF_O + rd * NW * 1024, dma_o[rd], 0);
     }
-    if (wave == 0) {
-      const uint32_t lr = hw::opaque_u32(hw::lds_addr(smem) + buf);
-      const uint32_t r4 = static_cast<uint32_t>(min(i0 + lane, q_len - 1)) * 4;
+    if (wave < SR / 64) {  // one wave per 64 rows of the stage
+      const uint32_t lr = hw::opaque_u32(hw::lds_addr(smem) + buf) + wave * 256;
+      const uint32_t r4 = static_cast<uint32_t>(min(i0 + wave * 64 + lane, q_len - 1)) * 4;
       hw::dma_dword(reinterpret_cast<const int*>(P.rowterm + rowbase), lr + OFF_L, r4);
       hw::dma_dword(reinterpret_cast<const int*>(P.delta + rowbase), lr + OFF_E, r4);
       if (masked && P.f.mask.kind == FA_MASK_DOCUMENT)
@@ -664,28 +676,52 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
     }
   };
 
-  auto compute = [&](int m, int h, int sub, bool masked, const char* sB) {
+  // score constants: those that do not depend on the head once; ALiBi's key
+  // term slope_h log2e j formed again only when the head changes (the
+  // stages of one head follow each other)
+  const ScoreConsts sc = make_score_consts(kbargs().f, 0);
+  float tj = 0.0f;
+  int tj_h = -1;
+  auto compute = [&](auto second, int m, int h, int sub, bool masked) {
     if (m < 0) return;
-    const char* sQ = sB + OFF_Q;
-    const char* sO = sB + OFF_O;
-    const float* sL = reinterpret_cast<const float*>(sB + OFF_L);
-    const float* sE = reinterpret_cast<const float*>(sB + OFF_E);
-    const int* sD = reinterpret_cast<const int*>(sB + OFF_D);
-    const ScoreConsts sc = make_score_consts(kbargs().f, h);
-    const int i0 = m * BQ + sub * kStageKeys;
-
-    // Two halves of 32 query rows each (it), one after the other: the
-    // live fp32 tiles per half are one S and one dP tile, which leaves the
-    // compiler registers to keep several LDS reads in flight.
+    // lane offsets into this stage's buffer (see the LDS layout above)
+    constexpr int BO = decltype(second)::value ? BUF1 : 0;
+    constexpr bool far = BO + MAX_IMM >= 65536;
+    constexpr int BI = far ? 0 : BO;  // buffer offset left in the immediates
+    int kq[DK], vq[2][DT];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int dd = 0; dd < DK; ++dd) kq[dd] = far ? hw::opaque_v(k_rd[dd] + BO) : k_rd[dd];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        vq[t2][dt] = far ? hw::opaque_v(v_rd[t2][dt] + BO) : v_rd[t2][dt];
+    const int rq = far ? hw::opaque_v(BO + 16 * g) : 16 * g;  // row terms of rows 4g..
+    const char* sQ = smem + BI + OFF_Q;
+    const char* sO = smem + BI + OFF_O;
+    const float* sL = reinterpret_cast<const float*>(smem + BI + OFF_L + rq);
+    const float* sE = reinterpret_cast<const float*>(smem + BI + OFF_E + rq);
+    const int* sD = reinterpret_cast<const int*>(smem + BI + OFF_D + rq);
+    if constexpr (SCORE == FA_SCORE_ALIBI) {
+      if (h != tj_h) {
+        tj = make_score_consts(kbargs().f, h).slope2 * static_cast<float>(j);
+        tj_h = h;
+      }
+    }
+    const int i0 = m * BQ + sub * SR;
+
+    // Parts of 32 query rows each (it), one after the other: the live fp32
+    // tiles per part are one S and one dP tile, which leaves the compiler
+    // registers to keep several LDS reads in flight.
+#pragma unroll
+    for (int it = 0; it < SR / 32; ++it) {
       // S = Q K^T and dP = dO V^T for rows [32 it, 32 it + 32) of the stage
       f32x16 s = f32x16{}, dpm = f32x16{};
       u32x4 qa[DK], oa[DK];
 #pragma unroll
       for (int dd = 0; dd < DK; ++dd) {
-        qa[dd] = *reinterpret_cast<const u32x4*>(sQ + k_rd[dd] + it * 32 * RB);
-        oa[dd] = *reinterpret_cast<const u32x4*>(sO + k_rd[dd] + it * 32 * RB);
+        qa[dd] = *reinterpret_cast<const u32x4*>(sQ + kq[dd] + it * 32 * RB);
+        oa[dd] = *reinterpret_cast<const u32x4*>(sO + kq[dd] + it * 32 * RB);
       }
 #pragma unroll
       for (int dd = 0; dd < DK; ++dd) {
@@ -698,11 +734,10 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
       // element r: query row i0 + 32 it + 8 (r / 4) + 4 g + r % 4. The
       // row's exponent offset (rowterm, from the dQ kernel) folds in -LSE
       // and ALiBi's row part; the key part of ALiBi is tj.
-      const float tj = SCORE == FA_SCORE_ALIBI ? sc.slope2 * static_cast<float>(j) : 0.0f;
       float fp[16];  // score_mod' (soft-cap), else 1
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int il = 32 * it + 8 * r4 + 4 * g;  // first of 4 consecutive rows
+        const int il = 32 * it + 8 * r4;  // + 4g: first of 4 consecutive rows
         const f32x4 rt4 = *reinterpret_cast<const f32x4*>(sL + il);
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
@@ -728,13 +763,13 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
         const bool doc_mask = kbargs().f.mask.kind == FA_MASK_DOCUMENT;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const int il = 32 * it + 8 * r4 + 4 * g;
+          const int il = 32 * it + 8 * r4;  // + 4g
           int4 d4 = {dj, dj, dj, dj};
           if (doc_mask) d4 = *reinterpret_cast<const int4*>(sD + il);
           const int dqs[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
           for (int cc = 0; cc < 4; ++cc) {
-            const int irow = i0 + il + cc;
+            const int irow = i0 + il + 4 * g + cc;
             const bool ok =
                 (static_cast<unsigned>(irow - ilo) < ispan) & (dqs[cc] == dj) & (irow < q_len);
             s[4 * r4 + cc] = ok ? s[4 * r4 + cc] : 0.0f;
@@ -743,7 +778,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
       }
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 del4 = *reinterpret_cast<const f32x4*>(sE + 32 * it + 8 * r4 + 4 * g);
+        const f32x4 del4 = *reinterpret_cast<const f32x4*>(sE + 32 * it + 8 * r4);
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
           const int r = 4 * r4 + cc;
@@ -771,11 +806,11 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
         i16x8 o8[DT], q8[DT];
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const i16x4 olo = lds_read_tr(sO + v_rd[0][dt] + kk * 16 * RB);
-          const i16x4 ohi = lds_read_tr(sO + v_rd[1][dt] + kk * 16 * RB);
+          const i16x4 olo = lds_read_tr(sO + vq[0][dt] + kk * 16 * RB);
+          const i16x4 ohi = lds_read_tr(sO + vq[1][dt] + kk * 16 * RB);
           o8[dt] = i16x8{olo[0], olo[1], olo[2], olo[3], ohi[0], ohi[1], ohi[2], ohi[3]};
-          const i16x4 qlo = lds_read_tr(sQ + v_rd[0][dt] + kk * 16 * RB);
-          const i16x4 qhi = lds_read_tr(sQ + v_rd[1][dt] + kk * 16 * RB);
+          const i16x4 qlo = lds_read_tr(sQ + vq[0][dt] + kk * 16 * RB);
+          const i16x4 qhi = lds_read_tr(sQ + vq[1][dt] + kk * 16 * RB);
           q8[dt] = i16x8{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]};
         }
 #pragma unroll
@@ -815,7 +850,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
       next_stage(m_nxt, h_nxt, sub_nxt, mk_nxt);
       issue(m_nxt, h_nxt, sub_nxt, BUF1, mk_nxt);
     }
-    compute(m_cur, h_cur, sub_cur, mk_cur, smem);
+    compute(std::false_type{}, m_cur, h_cur, sub_cur, mk_cur);
     if (st + 1 >= total) break;
     m_cur = m_nxt;
     h_cur = h_nxt;
@@ -827,7 +862,7 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
       next_stage(m_nxt, h_nxt, sub_nxt, mk_nxt);
       issue(m_nxt, h_nxt, sub_nxt, 0, mk_nxt);
     }
-    compute(m_cur, h_cur, sub_cur, mk_cur, smem + BUF1);
+    compute(std::true_type{}, m_cur, h_cur, sub_cur, mk_cur);
     m_cur = m_nxt;
     h_cur = h_nxt;
     sub_cur = sub_nxt;
