@@ -38,6 +38,13 @@
 
 namespace fa {
 
+// A per-lane value the compiler cannot see through: formed where it is used
+// instead of being folded into other expressions or held across a loop.
+__device__ __forceinline__ int opaque_v(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // The soft-cap's derivative enters dT as t (1 - t) with t = 1 / (e^{2x} + 1),
 // which is (1 - tanh^2 x) / 4; the factor 4, a power of two, is applied to
 // the fp32 sums at the end (exact: scaling by 4 commutes with rounding).
@@ -690,13 +697,13 @@ __global__ __launch_bounds__(BK * 2, 1) void bwd_dkdv_kernel(const BwdLaunch bp)
     constexpr int BI = far ? 0 : BO;  // buffer offset left in the immediates
     int kq[DK], vq[2][DT];
 #pragma unroll
-    for (int dd = 0; dd < DK; ++dd) kq[dd] = far ? hw::opaque_v(k_rd[dd] + BO) : k_rd[dd];
+    for (int dd = 0; dd < DK; ++dd) kq[dd] = far ? opaque_v(k_rd[dd] + BO) : k_rd[dd];
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        vq[t2][dt] = far ? hw::opaque_v(v_rd[t2][dt] + BO) : v_rd[t2][dt];
-    const int rq = far ? hw::opaque_v(BO + 16 * g) : 16 * g;  // row terms of rows 4g..
+        vq[t2][dt] = far ? opaque_v(v_rd[t2][dt] + BO) : v_rd[t2][dt];
+    const int rq = far ? opaque_v(BO + 16 * g) : 16 * g;  // row terms of rows 4g..
     const char* sQ = smem + BI + OFF_Q;
     const char* sO = smem + BI + OFF_O;
     const float* sL = reinterpret_cast<const float*>(smem + BI + OFF_L + rq);

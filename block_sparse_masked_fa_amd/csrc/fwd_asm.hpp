@@ -83,12 +83,5 @@ __device__ __forceinline__ uint32_t opaque_u32(uint32_t x) {
   return x;
 }
 
-// The same for a per-lane value: formed where it is used instead of being
-// folded into other expressions or held across a loop.
-__device__ __forceinline__ int opaque_v(int x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
-
 }  // namespace hw
 }  // namespace fa
