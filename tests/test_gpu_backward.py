@@ -406,6 +406,27 @@ def test_workload_backward(name, workload_inputs):
         assert krel <= 1e-2
 
 
+def test_workload_backward_middle_key_block(workload_inputs):
+    # c3 at full size (sliding window W): the keys of one key block in the
+    # middle of the sequence are seen by rows [j0, j0 + 128 + W - 1) only, so
+    # the oracle over those rows gives their dK and dV exactly. Unlike the
+    # last keys, this block is reached after many stages of the dK / dV
+    # kernel's visit sequence and through both of its LDS buffers.
+    w, q, k, v, do, doc = workload_inputs("c3")
+    assert w.mask == "sliding_window" and w.block_n == 128
+    print("[bwd workload] c3 middle key block", flush=True)
+    dq, dk, dv = gpu_fwd_bwd(w, q, k, v, do, doc, splits=1)
+    j0 = 32 * w.block_n
+    keys = np.arange(j0, j0 + w.block_n)
+    rows = np.arange(j0, min(j0 + w.block_n + w.window - 1, w.q_len))
+    _, dk_ref, dv_ref = oracle_bwd(w, q, k, v, do, doc, rows=rows)
+    cols = torch.from_numpy(keys).to(DEV)
+    ek = assert_grad_close(dk.index_select(2, cols), dk_ref[:, :, keys], "dK c3 middle block")
+    ev = assert_grad_close(dv.index_select(2, cols), dv_ref[:, :, keys], "dV c3 middle block")
+    print(f"[bwd workload] c3 middle key block: max err / scale dK {ek:.3g} dV {ev:.3g}",
+          flush=True)
+
+
 @pytest.mark.parametrize("mask,score", [("causal", "none"), ("sliding_window", "alibi"),
                                         ("document", "softcap")])
 def test_backward_caller_lists(mask, score):
