@@ -17,13 +17,14 @@
 //     and the pairs of a tile realise every integer d in
 //     [i_lo - j_hi, i_hi - j_lo]. "Some pair allowed" and "all pairs allowed"
 //     are therefore interval tests on that range (one thread per tile).
-//   * document: a wavefront per tile. If the key block is one document c,
-//     allowed pairs can only sit on the query rows of document c, and some
-//     (i, j) with i >= j exists among them iff the last such row is >= the
-//     block's first key; all pairs are allowed iff the query block is also
-//     all document c and lies wholly below the diagonal. A key block that
-//     mixes documents has every pair evaluated (ids need not be sorted or
-//     contiguous).
+//   * document: a wavefront per tile. Pairs (i, j) allowed with document c
+//     (doc[i] == doc[j] == c, i >= j) exist iff the query block's last row
+//     of c is at or after the key block's first key of c; the tile is visited
+//     one distinct key id at a time (one inside a document, two at a
+//     boundary). All pairs are allowed iff both blocks are one and the same
+//     document and the tile lies wholly below the diagonal. Ids need not be
+//     sorted or contiguous. (Key blocks wider than 128 columns: a single-id
+//     block takes the same test, a mixed one has every pair evaluated.)
 // Compaction writes, per row, the listed blocks in ascending order followed by
 // the remaining block numbers in ascending order (a stable partition).
 #include <hip/hip_runtime.h>
@@ -88,13 +89,8 @@ __device__ unsigned char classify_document(const BlockMaskLaunch& p, const int* 
   const Tile t = make_tile(p, m, n);
   const int cols = t.j_hi - t.j_lo + 1;
   const int rows = t.i_hi - t.i_lo + 1;
-  // is the key block a single document c?
-  const int c = __builtin_amdgcn_readfirstlane(doc[t.j_lo]);
-  bool other = false;
-  for (int jj = lane; jj < cols; jj += 64) other |= doc[t.j_lo + jj] != c;
-  if (!__builtin_amdgcn_ballot_w64(other)) {
-    // pairs can only be allowed on rows of document c; (i, j) with i >= j
-    // exists among them iff the last such row is >= the first key j_lo
+  // the query block's last row of document c (-1 if none)
+  auto last_row_of = [&](int c) -> int {
     int last = -1;
     for (int base = 0; base < rows; base += 64) {
       const int r = base + lane;
@@ -102,7 +98,47 @@ __device__ unsigned char classify_document(const BlockMaskLaunch& p, const int* 
           __builtin_amdgcn_ballot_w64(r < rows && qdoc[min(r, rows - 1)] == c);
       if (hit) last = t.i_lo + base + 63 - __builtin_clzll(hit);
     }
-    if (last < t.j_lo) return kEmpty;
+    return last;
+  };
+  if (cols <= 128) {
+    // Allowed pairs with document c exist iff the query block's last row of
+    // c is at or after the key block's first key of c, so the key block's
+    // distinct ids are visited one at a time (one inside a document, two
+    // at a boundary; ids need not be sorted): ids in two 64-column chunks,
+    // `left*` the columns whose id is still to visit.
+    const bool in0 = lane < cols, in1 = 64 + lane < cols;
+    const int id0 = in0 ? doc[t.j_lo + lane] : 0;
+    const int id1 = in1 ? doc[t.j_lo + 64 + lane] : 0;
+    unsigned long long left0 = __builtin_amdgcn_ballot_w64(in0);
+    unsigned long long left1 = __builtin_amdgcn_ballot_w64(in1);
+    bool some = false;
+    int distinct = 0, c_one = 0;
+    while (left0 | left1) {
+      const int c = left0 ? __builtin_amdgcn_readlane(id0, __builtin_ctzll(left0))
+                          : __builtin_amdgcn_readlane(id1, __builtin_ctzll(left1));
+      const unsigned long long h0 = __builtin_amdgcn_ballot_w64(in0 && id0 == c);
+      const unsigned long long h1 = __builtin_amdgcn_ballot_w64(in1 && id1 == c);
+      const int first_key = t.j_lo + (h0 ? __builtin_ctzll(h0) : 64 + __builtin_ctzll(h1));
+      left0 &= ~h0;
+      left1 &= ~h1;
+      some |= last_row_of(c) >= first_key;
+      ++distinct;
+      c_one = c;
+      if (some && distinct > 1) return kPartial;
+    }
+    if (!some) return kEmpty;
+    // every pair allowed: one document on both sides and below the diagonal
+    if (distinct == 1 && qsingle == c_one && t.i_lo >= t.j_hi && t.complete) return kFull;
+    return kPartial;
+  }
+  // wider key blocks: is the key block a single document c?
+  const int c = __builtin_amdgcn_readfirstlane(doc[t.j_lo]);
+  bool other = false;
+  for (int jj = lane; jj < cols; jj += 64) other |= doc[t.j_lo + jj] != c;
+  if (!__builtin_amdgcn_ballot_w64(other)) {
+    // pairs can only be allowed on rows of document c; (i, j) with i >= j
+    // exists among them iff the last such row is >= the first key j_lo
+    if (last_row_of(c) < t.j_lo) return kEmpty;
     // every pair allowed: one document on both sides and below the diagonal
     if (qsingle == c && t.i_lo >= t.j_hi && t.complete) return kFull;
     return kPartial;

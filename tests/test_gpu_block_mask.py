@@ -88,13 +88,26 @@ def test_block_mask_random_small(seed):
 
 
 def test_block_mask_unsorted_document_ids():
-    # document ids need not be sorted or contiguous
+    # document ids need not be sorted or contiguous: ids drawn per key, runs
+    # of ids in shuffled order (several distinct ids per key block, ids that
+    # recur after others), and blocks wider than 128 keys, ragged tails
     rng = np.random.default_rng(7)
     doc = rng.integers(0, 3, size=500).astype(np.int32)
     got = gpu_mask("document", 1, 1, 500, 500, 32, 32, doc=doc)
     want = O.create_block_mask("document", 1, 1, 500, 500, 32, 32,
                                doc_id=doc)
     assert_same(got, want, "unsorted docs")
+    for t in range(12):
+        ql, kl = int(rng.integers(100, 1500)), int(rng.integers(100, 1500))
+        bm_ = int(rng.choice([32, 64, 128, 256]))
+        bn_ = int(rng.choice([8, 64, 128, 256]))
+        L = max(ql, kl)
+        run = int(rng.choice([1, 7, 40, 130]))
+        doc = np.repeat(rng.integers(0, 5, -(-L // run)), run)[:L].astype(np.int32)
+        label = f"unsorted docs ql={ql} kl={kl} bm={bm_} bn={bn_} run={run}"
+        got = gpu_mask("document", 1, 1, ql, kl, bm_, bn_, doc=doc)
+        want = O.create_block_mask("document", 1, 1, ql, kl, bm_, bn_, doc_id=doc)
+        assert_same(got, want, label)
 
 
 def test_block_mask_empty_lengths():
