@@ -37,8 +37,11 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 16;
-constexpr int kThreads = 64 * kWaves;
+// Workgroup sizes: 16 waves for document masks (a wavefront per tile), 4 for
+// the interval kinds (a thread per tile: a smaller group starts and passes
+// its barriers sooner).
+constexpr int kDocWaves = 16;
+constexpr int kIntervalWaves = 4;
 constexpr unsigned char kEmpty = 0, kPartial = 1, kFull = 2;
 
 struct Tile {
@@ -163,7 +166,8 @@ __device__ unsigned char classify_document(const BlockMaskLaunch& p, const int* 
 }
 
 // Exclusive prefix count of `flag` over the workgroup for one chunk of
-// kThreads consecutive key blocks; *chunk_total gets the chunk's count.
+// 64 kWaves consecutive key blocks; *chunk_total gets the chunk's count.
+template <int kWaves>
 __device__ int wg_exclusive_count(bool flag, int* wave_counts, int* chunk_total) {
   const int wave = threadIdx.x / 64;
   const unsigned long long mask = __builtin_amdgcn_ballot_w64(flag);
@@ -184,7 +188,9 @@ __device__ int wg_exclusive_count(bool flag, int* wave_counts, int* chunk_total)
   return before + lane_prefix;
 }
 
-__global__ __launch_bounds__(kThreads) void block_mask_kernel(BlockMaskLaunch p) {
+template <int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void block_mask_kernel(BlockMaskLaunch p) {
+  constexpr int kThreads = 64 * kWaves;
   extern __shared__ unsigned char states[];  // nkvb bytes
   __shared__ int wave_counts[kWaves];
   __shared__ int totals[2];
@@ -242,8 +248,8 @@ __global__ __launch_bounds__(kThreads) void block_mask_kernel(BlockMaskLaunch p)
     const bool is_p = in && (sep ? (s == kPartial) : (s != kEmpty));
     const bool is_f = in && sep && (s == kFull);
     int chunk_p, chunk_f;
-    const int pp = run_p + wg_exclusive_count(is_p, wave_counts, &chunk_p);
-    const int pf = run_f + wg_exclusive_count(is_f, wave_counts, &chunk_f);
+    const int pp = run_p + wg_exclusive_count<kWaves>(is_p, wave_counts, &chunk_p);
+    const int pf = run_f + wg_exclusive_count<kWaves>(is_f, wave_counts, &chunk_f);
     if (in) {
       idx[is_p ? pp : tot_p + (n - pp)] = n;
       if (sep) fidx[is_f ? pf : tot_f + (n - pf)] = n;
@@ -263,8 +269,12 @@ int launch_block_mask(const BlockMaskLaunch& p, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int rows = p.Bm * p.Hm * p.nqb;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(block_mask_kernel, dim3(rows), dim3(kThreads),
-                     static_cast<size_t>(p.nkvb), s, p);
+  if (p.mask.kind == FA_MASK_DOCUMENT)
+    hipLaunchKernelGGL(block_mask_kernel<kDocWaves>, dim3(rows), dim3(64 * kDocWaves),
+                       static_cast<size_t>(p.nkvb), s, p);
+  else
+    hipLaunchKernelGGL(block_mask_kernel<kIntervalWaves>, dim3(rows), dim3(64 * kIntervalWaves),
+                       static_cast<size_t>(p.nkvb), s, p);
   return hipGetLastError();
 }
 
