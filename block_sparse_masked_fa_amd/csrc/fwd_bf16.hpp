@@ -42,7 +42,9 @@
 // are multiplied by exp2(m_old - m_new)); otherwise p may exceed 1 by at most
 // 2^kRescaleSlack, which fp32 and bf16 represent with the same relative
 // precision. The row sum adds the bf16-rounded p (v_dot2c_f32_bf16 against
-// ones), i.e. exactly the weights the PV product uses.
+// ones), i.e. exactly the weights the PV product uses. Soft-capped scores are
+// bounded by the cap, so for caps up to kCapFixedRefMax the reference is a
+// constant set from the cap alone and the stages take no row max at all.
 #pragma once
 
 #include "fwd_asm.hpp"
@@ -55,6 +57,15 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kRescaleSlack = 8.0f;
+// Soft-capped scores lie in [-capL, capL] (capL = cap log2 e, log2 units).
+// Against the fixed reference m_ref = capL - kCapHeadroom every weight
+// p = exp2(s2 - m_ref) lies in [2^(kCapHeadroom - 2 capL), 2^kCapHeadroom];
+// while capL <= kCapFixedRefMax that is inside [2^-112, 2^48]: no weight
+// overflows or leaves the normal range (fp32 and bf16 alike), the row sum
+// and the accumulator stay below 2^79 |v|max for rows up to 2^31 keys, and
+// the stage loop needs neither a row maximum nor a rescale.
+constexpr float kCapHeadroom = 48.0f;
+constexpr float kCapFixedRefMax = 80.0f;
 constexpr int kStageKeys = 64;
 constexpr int kSReadAhead = 6;  // K operand reads in flight ahead of the S product
 
@@ -463,7 +474,9 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
             : 0;
     const unsigned span = static_cast<unsigned>(max(hi_abs - lo_abs, 0));
 
-    float m_run = FA_NEG_INF;  // reference max, log2 domain
+    // soft-cap with a bounded cap: fixed reference (uniform over the launch)
+    const bool cap_fixed = SCORE == FA_SCORE_SOFTCAP && sc.cap_out <= kCapFixedRefMax;
+    float m_run = cap_fixed ? sc.cap_out - kCapHeadroom : FA_NEG_INF;  // reference, log2 domain
     float l_run = 0.0f;        // this lane's share of the row sum, in two
     float l_run2 = 0.0f;       // independent accumulators
     f32x16 oacc[DT];
@@ -579,12 +592,16 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
         mx = row_pair_max(__builtin_fmaf(lane_max(), sa, sb));
       } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
         const float k2 = 2.0f * sc.cap_in * kLog2e;
+        mx = FA_NEG_INF;  // (fixed reference: no maximum)
         if (!masked) {
-          const float mraw = row_pair_max(lane_max());
-          mx = mraw == FA_NEG_INF
-                   ? FA_NEG_INF
-                   : __builtin_fmaf(-2.0f * sc.cap_out,
-                                    __builtin_amdgcn_rcpf(exp2_hw(mraw * k2) + 1.0f), sc.cap_out);
+          if (!cap_fixed) {
+            const float mraw = row_pair_max(lane_max());
+            mx = mraw == FA_NEG_INF
+                     ? FA_NEG_INF
+                     : __builtin_fmaf(-2.0f * sc.cap_out,
+                                      __builtin_amdgcn_rcpf(exp2_hw(mraw * k2) + 1.0f),
+                                      sc.cap_out);
+          }
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
@@ -601,7 +618,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
               s[jt][r] = __builtin_fmaf(-2.0f * sc.cap_out, t, sc.cap_out);
             }
           apply_mask();
-          mx = row_pair_max(lane_max());
+          if (!cap_fixed) mx = row_pair_max(lane_max());
           sa = 1.0f;
           sb = 0.0f;
         }
@@ -614,7 +631,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
 
       // ---- online softmax: lazy rescale, then p = exp2(s2 - m_ref)
       const bool raise = mx > m_run + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
+      if (!cap_fixed && __builtin_amdgcn_ballot_w64(raise)) {
         const float m_new = raise ? mx : m_run;
         const float alpha = (m_new == m_run) ? 1.0f : exp2_hw(m_run - m_new);
         l_run *= alpha;

@@ -492,3 +492,35 @@ def test_caller_lists_are_checked():
     with pytest.raises(ValueError):
         fa.flex_attention(q, k, v, bm, lse=torch.empty(1, 2, 300, device=DEV,
                                                        dtype=torch.float64))
+
+
+@pytest.mark.parametrize("cap", [3.0, 50.0, 55.0, 56.0, 300.0])
+@pytest.mark.parametrize("mask", ["causal", "document"])
+def test_softcap_reference_range(cap, mask):
+    # Caps up to 55.45 (cap log2 e <= 80) run the stages against a constant
+    # reference set from the cap; larger caps track the row maximum. Both
+    # sides of that limit, with the scores pushed to both ends of the cap:
+    # every key gets a shared component u, the second query block points
+    # along +u (scores near +cap) and the third along -u (every score of
+    # those rows near -cap, the smallest weights the constant reference
+    # produces); whole and through split-KV, every row against the oracle.
+    blk = 128
+    ql = kl = 4 * blk + 19
+    w = WL.Workload("small", "bf16", 1, 4, 2, ql, kl, 128, mask, blk, blk,
+                    seed=0, score="softcap", softcap=cap)
+    rng = np.random.default_rng(zlib.crc32(f"capref{cap}{mask}".encode()))
+    doc = (np.sort(rng.integers(0, 2, kl)).astype(np.int32)
+           if mask == "document" else None)
+    q, k, v = WL.draw_qkv(rng, w)
+    u = rng.standard_normal(128).astype(np.float32)
+    k = k + 2.0 * u
+    big = 4.0 * cap / 50.0
+    q[:, :, blk:2 * blk] = q[:, :, blk:2 * blk] * 0.25 + big * u
+    q[:, :, 2 * blk:3 * blk] = q[:, :, 2 * blk:3 * blk] * 0.25 - big * u
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+    o_ref, l_ref = oracle_case(q, k, v, w, doc)
+    for ns in (1, 3):
+        print(f"[fwd softcap reference] cap={cap} {mask} splits={ns}", flush=True)
+        o, lse = run_gpu(w, q, k, v, doc, num_splits=ns)
+        assert_close(o, lse, o_ref, l_ref, TOL["bf16"],
+                     f"softcap {cap} {mask} splits={ns}")
