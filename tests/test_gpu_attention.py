@@ -524,3 +524,38 @@ def test_softcap_reference_range(cap, mask):
         o, lse = run_gpu(w, q, k, v, doc, num_splits=ns)
         assert_close(o, lse, o_ref, l_ref, TOL["bf16"],
                      f"softcap {cap} {mask} splits={ns}")
+
+
+@pytest.mark.parametrize("jump", [12.0, 40.0, 100.0, 400.0])
+@pytest.mark.parametrize("score", ["none", "alibi"])
+def test_reference_jumps(score, jump):
+    # Without a soft-cap, a row's stages after its first are formed against
+    # the reference the row already has and only their sums are checked:
+    # here the keys of the first key block (visited last by every later
+    # query block) score about `jump` log2 units above all other keys, so
+    # that last stage's weights come out near 2^jump against the reference:
+    # kept as they are (12), rescaled after the product (40), formed again
+    # against the row max (100: sums past 2^64; 400: past the fp32 range).
+    # Causal and no mask, whole and through split-KV, every row against the
+    # oracle.
+    blk = 128
+    ql = kl = 4 * blk + 19
+    for mask in ("causal", "none"):
+        w = WL.Workload("small", "bf16", 1, 4, 2, ql, kl, 128, mask, blk, blk,
+                        seed=0, score=score)
+        rng = np.random.default_rng(zlib.crc32(f"jump{score}{jump}{mask}".encode()))
+        q, k, v = WL.draw_qkv(rng, w)
+        u = rng.standard_normal(128).astype(np.float32)
+        u /= np.linalg.norm(u)
+        a = 4.0
+        b = jump / (a * w.scale * np.log2(np.e))
+        q = q + a * u
+        k[:, :, :blk] += b * u
+        q, k, v = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+        o_ref, l_ref = oracle_case(q, k, v, w, None)
+        for ns in (1, 3):
+            print(f"[fwd reference jump] {score} jump={jump} {mask} splits={ns}",
+                  flush=True)
+            o, lse = run_gpu(w, q, k, v, None, num_splits=ns)
+            assert_close(o, lse, o_ref, l_ref, TOL["bf16"],
+                         f"{score} jump={jump} {mask} splits={ns}")
