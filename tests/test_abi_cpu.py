@@ -550,12 +550,13 @@ def test_auto_bwd_splits():
 
 
 def test_auto_decode_splits():
-    # about eight single-wavefront workgroups per compute unit, never more
+    # about sixteen single-wavefront workgroups per compute unit, never more
     # parts than 64-key stages, at most 64
-    assert api.auto_decode_splits(16, 8, 32768, 256) == 16
+    assert api.auto_decode_splits(16, 8, 32768, 256) == 32
     assert api.auto_decode_splits(1, 1, 32768, 256) == 64
     assert api.auto_decode_splits(1, 1, 128, 256) == 2
-    assert api.auto_decode_splits(256, 8, 32768, 256) == 1
+    assert api.auto_decode_splits(256, 8, 32768, 256) == 2
+    assert api.auto_decode_splits(512, 8, 32768, 256) == 1
     assert api.auto_decode_splits(0, 8, 32768, 256) == 1
 
 
