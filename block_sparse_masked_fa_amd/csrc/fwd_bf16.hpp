@@ -460,6 +460,16 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
     const int i = cur.w.m * BQ + wave * 32 + lq;
     const bool i_ok = i < kargs().q_len;
     const ScoreConsts sc = make_score_consts(kargs(), cur.w.h);
+    // ALiBi: the S product starts from the key offsets of a 32-key tile in
+    // units of q.k (register r of a tile holds key 8(r/4) + r%4 of the lane's
+    // group), so the accumulator leaves the MFMA as q.k + jl slope / scale and
+    // the bias costs no vector instruction per score
+    f32x16 s_init = f32x16{};
+    if constexpr (SCORE == FA_SCORE_ALIBI) {
+      const float u = sc.slope2 / sc.c;  // slope / scale
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_init[r] = static_cast<float>(8 * (r >> 2) + (r & 3)) * u;
+    }
     // mask_mod as an interval of key indices per row: j in [lo_abs, lo_abs + span)
     // (64-bit so that any window >= 1 is exact; keys are >= 0, so the
     // interval start is clamped there)
@@ -497,8 +507,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
       // PV product below)
       __builtin_amdgcn_s_setprio(0);
       f32x16 s[2];
-      s[0] = f32x16{};
-      s[1] = f32x16{};
+      s[0] = s_init;
+      s[1] = s_init;
       u32x4 ka[DK][2];
 #pragma unroll
       for (int dk = 0; dk < DK; ++dk)
@@ -529,9 +539,10 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
       // (sa, sb fixed for the lane over the stage), so the exponent below is
       // one FMA and one exp2 per score:
       //   NONE     x = q.k                        sa = scale log2e, sb = 0
-      //   ALIBI    x = q.k scale / slope + (jl)   sa = slope log2e,
-      //            (jl = the key's offset in the    sb = slope log2e (j0 + 4g - i)
-      //            stage: a literal per register)
+      //   ALIBI    x = q.k + jl slope / scale     sa = scale log2e,
+      //            (jl = the key's offset in its    sb = slope log2e (j0 + 4g - i)
+      //            32-key tile; added by the S      (+ 32 slope log2e for tile 1)
+      //            product through its start value)
       //   SOFTCAP  full stage: x = 1 / (e^{2 q.k scale / cap} + 1),
       //            sa = -2 cap log2e, sb = cap log2e (cap tanh = cap - 2 cap x);
       //            the row max is taken on q.k (tanh is increasing) before x is
@@ -539,6 +550,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
       // Key of (jt, r): j0 + 4g + 32jt + 8(r/4) + r%4; masked keys get x =
       // -inf before the max (p = 0).
       float sa, sb;
+      float sb1;  // (ALiBi: tile 1's offset; the other score_mods use sb for both tiles)
       float mx4[4] = {FA_NEG_INF, FA_NEG_INF, FA_NEG_INF, FA_NEG_INF};
       // max of this lane's 32 values (four independent chains); the lane
       // ^ 32 holds the row's other keys, exchanged by row_pair_max once the
@@ -549,6 +561,16 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
 #pragma unroll
           for (int r = 0; r < 8; ++r) mx4[c] = __builtin_fmaxf(mx4[c], s[c >> 1][8 * (c & 1) + r]);
         return __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
+      };
+      // the same, per 32-key tile
+      auto lane_max2 = [&](float& m0, float& m1) {
+        float t4[4] = {FA_NEG_INF, FA_NEG_INF, FA_NEG_INF, FA_NEG_INF};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int r = 0; r < 8; ++r) t4[c] = __builtin_fmaxf(t4[c], s[c >> 1][8 * (c & 1) + r]);
+        m0 = __builtin_fmaxf(t4[0], t4[1]);
+        m1 = __builtin_fmaxf(t4[2], t4[3]);
       };
       auto apply_mask = [&]() {
         const int lo = lo_abs - (j0 + 4 * g);  // interval start, lane-relative
@@ -578,18 +600,17 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
       };
       float mx;  // row max in the log2 domain
       if constexpr (SCORE == FA_SCORE_ALIBI) {
-        sa = sc.slope2;
+        // x = q.k + jl slope / scale from the product; tile jt's keys start
+        // 32 jt later, which its own offset sb1 carries
+        sa = sc.c;
         sb = sc.slope2 * static_cast<float>(j0 + 4 * g - i);
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            s[jt][r] = __builtin_fmaf(s[jt][r], sc.c_over_slope2,
-                                      static_cast<float>(32 * jt + 8 * (r >> 2) + (r & 3)));
+        sb1 = __builtin_fmaf(32.0f, sc.slope2, sb);
         if (masked) apply_mask();
         // (sb differs between the two halves of the row: exchange in the
         // log2 domain; -inf stays -inf)
-        mx = row_pair_max(__builtin_fmaf(lane_max(), sa, sb));
+        float m0, m1;
+        lane_max2(m0, m1);
+        mx = row_pair_max(__builtin_fmaxf(__builtin_fmaf(m0, sa, sb), __builtin_fmaf(m1, sa, sb1)));
       } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
         const float k2 = 2.0f * sc.cap_in * kLog2e;
         mx = FA_NEG_INF;  // (fixed reference: no maximum)
@@ -641,14 +662,15 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
         m_run = m_new;
       }
       const float m_use = (m_run == FA_NEG_INF) ? 0.0f : m_run;
-      const float ofs = sb - m_use;
+      if constexpr (SCORE != FA_SCORE_ALIBI) sb1 = sb;
+      const float ofs[2] = {sb - m_use, sb1 - m_use};
       bf16x8 pb[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         f32x8 pf;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          pf[e] = exp2_hw(__builtin_fmaf(s[kk >> 1][(kk & 1) * 8 + e], sa, ofs));
+          pf[e] = exp2_hw(__builtin_fmaf(s[kk >> 1][(kk & 1) * 8 + e], sa, ofs[kk >> 1]));
         pb[kk] = __builtin_convertvector(pf, bf16x8);
         const u32x4 pw = __builtin_bit_cast(u32x4, pb[kk]);
 #pragma unroll
