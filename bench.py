@@ -14,7 +14,8 @@ kernel over a dense causal block mask at the same shape, the other bf16
 workloads (c2, c3, c5) as sub-objects, the oracle timed on the host cores as
 a baseline, and (outside the step) the backward's time and algorithmic rate,
 and the HBM rates of the paged decode workload and of the masked-softmax
-fallback workload.
+fallback workload, and, as context only, the rate of a plain bf16 GEMM
+through torch on the same chip.
 
 Timing protocol: every workload is first run back to back for at least
 --warm-ms of GPU time (the clock settles: MI355X lowers it under sustained
@@ -335,6 +336,8 @@ def main(argv=None) -> int:
                     help="skip the timing of the paged decode workload")
     ap.add_argument("--no-softmax", action="store_true",
                     help="skip the timing of the masked softmax workload")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the timing of a plain bf16 GEMM (context only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB copy kernel (for counter "
                          "calibration under rocprofv3 --pmc)")
@@ -508,6 +511,25 @@ def main(argv=None) -> int:
         log(f"[bench] masked softmax {sm_ms * 1e3:.1f} us, {smx['achieved_GBps']} GB/s")
         del sc, sp
 
+    # context, not part of the path: a plain bf16 product of two 8192 x 8192
+    # matrices through torch (the vendor GEMM library) on the same chip and
+    # under the same power limit, the rate an MFMA-bound kernel can expect
+    gemm = None
+    if not a.no_gemm_reference:
+        ga = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+        gb = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+        gf = lambda: torch.matmul(ga, gb)  # noqa: E731
+        warm_up(torch, stream, gf, 5, a.warm_ms)
+        g_ms = time_back_to_back(torch, stream, gf, 20)
+        g_tf = 2 * 8192 ** 3 / (g_ms * 1e-3) / 1e12
+        gemm = {"what": "torch.matmul bf16 8192x8192x8192 (vendor library), context only",
+                "ms": round(g_ms, 4), "tflops": round(g_tf, 1),
+                "frac_of_peak": round(g_tf / PEAK_BF16_TFLOPS, 4),
+                "forward_over_gemm": round(achieved / g_tf, 3)}
+        log(f"[bench] bf16 GEMM reference {g_tf:.0f} TFLOP/s; forward at "
+            f"{achieved / g_tf:.2f} of it")
+        del ga, gb
+
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
@@ -558,6 +580,7 @@ def main(argv=None) -> int:
         "backward": bwd,
         "decode": dec,
         "masked_softmax": smx,
+        "gemm_reference": gemm,
     }
     print(json.dumps(line), flush=True)
     return 0
