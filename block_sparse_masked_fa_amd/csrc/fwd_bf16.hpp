@@ -66,6 +66,12 @@ constexpr float kRescaleSlack = 8.0f;
 // the stage loop needs neither a row maximum nor a rescale.
 constexpr float kCapHeadroom = 48.0f;
 constexpr float kCapFixedRefMax = 80.0f;
+// A full soft-cap stage whose every |y| = |q.k scale / cap| is at most
+// kCapSeriesY takes cap tanh y from its odd series to y^5,
+// y - y^3 / 3 + 2 y^5 / 15: the series alternates with falling terms there,
+// so the error is below the first omitted one, 17 y^7 / 315 <= 3.3e-6 (of
+// the cap), against 2^-9 for the bf16 rounding of every weight.
+constexpr float kCapSeriesY = 0.25f;
 constexpr int kStageKeys = 64;
 constexpr int kSReadAhead = 6;  // K operand reads in flight ahead of the S product
 
@@ -550,6 +556,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
       // Key of (jt, r): j0 + 4g + 32jt + 8(r/4) + r%4; masked keys get x =
       // -inf before the max (p = 0).
       float sa, sb;
+      bool series = false;  // soft-cap: this stage takes tanh's series
       float sb1;  // (ALiBi: tile 1's offset; the other score_mods use sb for both tiles)
       float mx4[4] = {FA_NEG_INF, FA_NEG_INF, FA_NEG_INF, FA_NEG_INF};
       // max of this lane's 32 values (four independent chains); the lane
@@ -614,7 +621,22 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
       } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
         const float k2 = 2.0f * sc.cap_in * kLog2e;
         mx = FA_NEG_INF;  // (fixed reference: no maximum)
-        if (!masked) {
+        if (!masked && cap_fixed) {
+          // the series when every score of the wave's stage is small enough
+          // (uniform; a NaN score takes the exact form)
+          float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+              a4[c] = __builtin_fmaxf(a4[c], __builtin_fabsf(s[c >> 1][8 * (c & 1) + r]));
+          const float amax = __builtin_fmaxf(__builtin_fmaxf(a4[0], a4[1]), __builtin_fmaxf(a4[2], a4[3]));
+          series = __builtin_amdgcn_ballot_w64(!(amax * sc.cap_in <= kCapSeriesY)) == 0;
+        }
+        if (series) {
+          sa = 0.0f;  // (the series path forms its own multiplier per score)
+          sb = 0.0f;
+        } else if (!masked) {
           if (!cap_fixed) {
             const float mraw = row_pair_max(lane_max());
             mx = mraw == FA_NEG_INF
@@ -665,23 +687,42 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
       if constexpr (SCORE != FA_SCORE_ALIBI) sb1 = sb;
       const float ofs[2] = {sb - m_use, sb1 - m_use};
       bf16x8 pb[4];
+      // p = exp2(x mul(x) + ofs): mul is sa, or on a series stage the odd
+      // series' polynomial in x^2, so that s2 = x (c0 + x^2 (c1 + x^2 c2))
+      auto weights = [&](auto mul_of) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        f32x8 pf;
+        for (int kk = 0; kk < 4; ++kk) {
+          f32x8 pf;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          pf[e] = exp2_hw(__builtin_fmaf(s[kk >> 1][(kk & 1) * 8 + e], sa, ofs[kk >> 1]));
-        pb[kk] = __builtin_convertvector(pf, bf16x8);
-        const u32x4 pw = __builtin_bit_cast(u32x4, pb[kk]);
+          for (int e = 0; e < 8; ++e) {
+            const float x = s[kk >> 1][(kk & 1) * 8 + e];
+            pf[e] = exp2_hw(__builtin_fmaf(x, mul_of(x), ofs[kk >> 1]));
+          }
+          pb[kk] = __builtin_convertvector(pf, bf16x8);
+          const u32x4 pw = __builtin_bit_cast(u32x4, pb[kk]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // copy the word out first: bit-casting a vector element in place
-          // mis-compiles (every iteration reads element 0)
-          const uint32_t word = pw[e];
-          float& acc = (e & 1) ? l_run2 : l_run;
-          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, acc,
-                                                false);
+          for (int e = 0; e < 4; ++e) {
+            // copy the word out first: bit-casting a vector element in place
+            // mis-compiles (every iteration reads element 0)
+            const uint32_t word = pw[e];
+            float& acc = (e & 1) ? l_run2 : l_run;
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, word), ones, acc,
+                                                  false);
+          }
         }
+      };
+      if (SCORE == FA_SCORE_SOFTCAP && series) {
+        // cap tanh(a x) log2 e = x (c0 + x^2 (c1 + x^2 c2)), a = scale / cap
+        const float a = sc.cap_in, a2 = a * a;
+        const float c0 = sc.cap_out * a;
+        const float c1 = -c0 * a2 * (1.0f / 3.0f);
+        const float c2 = c0 * a2 * a2 * (2.0f / 15.0f);
+        weights([&](float x) {
+          const float t = x * x;
+          return __builtin_fmaf(t, __builtin_fmaf(t, c2, c1), c0);
+        });
+      } else {
+        weights([&](float) { return sa; });
       }
 
       // ---- O^T += V^T P^T (4 k-steps of 16 keys). The wave raises its issue
