@@ -70,8 +70,12 @@ constexpr float kCapFixedRefMax = 80.0f;
 // kCapSeriesY takes cap tanh y from its odd series to y^5,
 // y - y^3 / 3 + 2 y^5 / 15: the series alternates with falling terms there,
 // so the error is below the first omitted one, 17 y^7 / 315 <= 3.3e-6 (of
-// the cap), against 2^-9 for the bf16 rounding of every weight.
+// the cap), against 2^-9 for the bf16 rounding of every weight. Up to
+// kCapSeries3Y the series stops at y^3, error below 2 y^5 / 15 <= 1.1e-5
+// (of the cap; 5.1e-4 at cap 50, a relative 5.1e-4 on a weight, a quarter
+// of its bf16 rounding), one FMA fewer per score.
 constexpr float kCapSeriesY = 0.25f;
+constexpr float kCapSeries3Y = 0.15f;
 constexpr int kStageKeys = 64;
 constexpr int kSReadAhead = 6;  // K operand reads in flight ahead of the S product
 
@@ -556,7 +560,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
       // Key of (jt, r): j0 + 4g + 32jt + 8(r/4) + r%4; masked keys get x =
       // -inf before the max (p = 0).
       float sa, sb;
-      bool series = false;  // soft-cap: this stage takes tanh's series
+      bool series = false;   // soft-cap: this stage takes tanh's series,
+      bool series3 = false;  // to y^3 only
       float sb1;  // (ALiBi: tile 1's offset; the other score_mods use sb for both tiles)
       float mx4[4] = {FA_NEG_INF, FA_NEG_INF, FA_NEG_INF, FA_NEG_INF};
       // max of this lane's 32 values (four independent chains); the lane
@@ -632,6 +637,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
               a4[c] = __builtin_fmaxf(a4[c], __builtin_fabsf(s[c >> 1][8 * (c & 1) + r]));
           const float amax = __builtin_fmaxf(__builtin_fmaxf(a4[0], a4[1]), __builtin_fmaxf(a4[2], a4[3]));
           series = __builtin_amdgcn_ballot_w64(!(amax * sc.cap_in <= kCapSeriesY)) == 0;
+          series3 = series &&
+                    __builtin_amdgcn_ballot_w64(!(amax * sc.cap_in <= kCapSeries3Y)) == 0;
         }
         if (series) {
           sa = 0.0f;  // (the series path forms its own multiplier per score)
@@ -717,10 +724,14 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
         const float c0 = sc.cap_out * a;
         const float c1 = -c0 * a2 * (1.0f / 3.0f);
         const float c2 = c0 * a2 * a2 * (2.0f / 15.0f);
-        weights([&](float x) {
-          const float t = x * x;
-          return __builtin_fmaf(t, __builtin_fmaf(t, c2, c1), c0);
-        });
+        if (series3) {
+          weights([&](float x) { return __builtin_fmaf(x * x, c1, c0); });
+        } else {
+          weights([&](float x) {
+            const float t = x * x;
+            return __builtin_fmaf(t, __builtin_fmaf(t, c2, c1), c0);
+          });
+        }
       } else {
         weights([&](float) { return sa; });
       }
