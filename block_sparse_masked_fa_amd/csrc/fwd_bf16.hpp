@@ -626,7 +626,8 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
       } else if constexpr (SCORE == FA_SCORE_SOFTCAP) {
         const float k2 = 2.0f * sc.cap_in * kLog2e;
         mx = FA_NEG_INF;  // (fixed reference: no maximum)
-        if (!masked && cap_fixed) {
+        bool small = false, small3 = false;
+        if (cap_fixed) {
           // the series when every score of the wave's stage is small enough
           // (uniform; a NaN score takes the exact form)
           float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -636,10 +637,12 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
             for (int r = 0; r < 8; ++r)
               a4[c] = __builtin_fmaxf(a4[c], __builtin_fabsf(s[c >> 1][8 * (c & 1) + r]));
           const float amax = __builtin_fmaxf(__builtin_fmaxf(a4[0], a4[1]), __builtin_fmaxf(a4[2], a4[3]));
-          series = __builtin_amdgcn_ballot_w64(!(amax * sc.cap_in <= kCapSeriesY)) == 0;
-          series3 = series &&
-                    __builtin_amdgcn_ballot_w64(!(amax * sc.cap_in <= kCapSeries3Y)) == 0;
+          small = __builtin_amdgcn_ballot_w64(!(amax * sc.cap_in <= kCapSeriesY)) == 0;
+          small3 = small &&
+                   __builtin_amdgcn_ballot_w64(!(amax * sc.cap_in <= kCapSeries3Y)) == 0;
         }
+        series = small && !masked;
+        series3 = small3 && !masked;
         if (series) {
           sa = 0.0f;  // (the series path forms its own multiplier per score)
           sb = 0.0f;
@@ -660,13 +663,38 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
           sa = -2.0f * sc.cap_out;
           sb = sc.cap_out;
         } else {
+          // masked stage: the capped score itself (log2 domain), then the mask
+          if (small) {
+            // (the series as below, on the capped score rather than in the exponent)
+            const float a = sc.cap_in, a2 = a * a;
+            const float c0 = sc.cap_out * a, c1 = -c0 * a2 * (1.0f / 3.0f),
+                        c2 = c0 * a2 * a2 * (2.0f / 15.0f);
+            if (small3) {
 #pragma unroll
-          for (int jt = 0; jt < 2; ++jt)
+              for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float t = __builtin_amdgcn_rcpf(exp2_hw(s[jt][r] * k2) + 1.0f);
-              s[jt][r] = __builtin_fmaf(-2.0f * sc.cap_out, t, sc.cap_out);
+                for (int r = 0; r < 16; ++r) {
+                  const float x = s[jt][r];
+                  s[jt][r] = x * __builtin_fmaf(x * x, c1, c0);
+                }
+            } else {
+#pragma unroll
+              for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  const float x = s[jt][r], t = x * x;
+                  s[jt][r] = x * __builtin_fmaf(t, __builtin_fmaf(t, c2, c1), c0);
+                }
             }
+          } else {
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const float t = __builtin_amdgcn_rcpf(exp2_hw(s[jt][r] * k2) + 1.0f);
+                s[jt][r] = __builtin_fmaf(-2.0f * sc.cap_out, t, sc.cap_out);
+              }
+          }
           apply_mask();
           if (!cap_fixed) mx = row_pair_max(lane_max());
           sa = 1.0f;
