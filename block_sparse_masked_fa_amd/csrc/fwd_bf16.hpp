@@ -66,7 +66,7 @@ constexpr float kRescaleSlack = 8.0f;
 // the stage loop needs neither a row maximum nor a rescale.
 constexpr float kCapHeadroom = 48.0f;
 constexpr float kCapFixedRefMax = 80.0f;
-// A full soft-cap stage whose every |y| = |q.k scale / cap| is at most
+// A soft-cap stage whose every |y| = |q.k scale / cap| is at most
 // kCapSeriesY takes cap tanh y from its odd series to y^5,
 // y - y^3 / 3 + 2 y^5 / 15: the series alternates with falling terms there,
 // so the error is below the first omitted one, 17 y^7 / 315 <= 3.3e-6 (of
