@@ -629,7 +629,7 @@ __global__ __launch_bounds__(BQ * 2, 2) void fwd_bf16_kernel(const FwdLaunch p) 
         bool small = false, small3 = false;
         if (cap_fixed) {
           // the series when every score of the wave's stage is small enough
-          // (uniform; a NaN score takes the exact form)
+          // (uniform; a NaN score gives a NaN weight on either path)
           float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
           for (int c = 0; c < 4; ++c)
