@@ -97,7 +97,11 @@ typedef enum fa_mask_kind {
  *   NONE     s
  *   SOFTCAP  softcap * tanh(s / softcap)
  *   ALIBI    s - slope_h * (q_idx - kv_idx), slope_h = 2^(-8 (h + 1) / H),
- *            h = query head, H = number of query heads. */
+ *            h = query head, H = number of query heads.
+ * Accuracy of the bf16 forward's tanh: the exact form (a few float ulps of
+ * 1); on a 64-key stage whose every |s / softcap| is at most 0.25, the odd
+ * series to y^5 (error <= 3.3e-6), at most 0.15, to y^3 (<= 1.1e-5): below
+ * the bf16 rounding of the softmax weights either way. */
 typedef enum fa_score_kind {
   FA_SCORE_NONE = 0,
   FA_SCORE_SOFTCAP = 1,
